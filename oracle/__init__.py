@@ -1,0 +1,22 @@
+"""CPU oracle for the SALR linear layer (encode, decode, forward).
+
+TEST INFRASTRUCTURE ONLY: a plain, slow, float64 NumPy definition of what the
+SALR hot path computes, used to check the HIP path.  Only tests/,
+__graft_entry__.smoke() and bench.py's cpu_baseline leg may import it; the
+product library never does, and this package imports nothing from the
+product package.
+
+Parity status of each function (what pins it, see tests/test_oracle_*.py):
+  bf16.f64_to_bits / bits_to_f64   pinned: torch conversion, hand cases
+  salr.select_keep                 pinned: brute-force pairwise ranking
+  salr.pack_masks / pack_values / block_offsets / decode_dense
+                                   pinned: bitwise round trip, per-bit loop
+  salr.truncated_svd / residual_factors
+                                   pinned: Eckart-Young, the per-entry MSE
+                                   bound (1 - r/min(N,K)), full-rank case
+  salr.forward                     pinned: per-set-bit triple loop, X = I
+  The pages print no worked example and no intermediate values, so no
+  function is pinned to a number printed on the pages.
+"""
+
+from . import bf16, salr  # noqa: F401
