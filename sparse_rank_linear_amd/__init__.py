@@ -1,1 +1,28 @@
-"""MI355X-native SALR linear layer (the HIP library and its binding follow)."""
+"""MI355X-native SALR linear layer.
+
+SALR (Sparsity-Aware Low-Rank Representation) serves a linear layer as
+Y = X W_s^T + (X A_cat) B_cat: W_s is the frozen weight after a static
+per-row magnitude prune, stored as a bitmap plus packed bf16 values, and
+A_cat / B_cat stack the truncated-SVD residual adapter with the LoRA
+adapters.  Encode and forward run in hand-written gfx950 HIP kernels behind
+the C ABI of include/salr.h (libsalr.so); this package only marshals
+arguments (binding.py) and draws synthetic inputs (synth.py).
+"""
+
+from .binding import (  # noqa: F401
+    EXPORTS,
+    LIB_PATH,
+    SalrError,
+    SalrLayer,
+    encode,
+    forward_workspace,
+    lib,
+    linear_forward,
+    query_sizes,
+    workspace,
+)
+
+__all__ = [
+    "EXPORTS", "LIB_PATH", "SalrError", "SalrLayer", "encode", "forward_workspace", "lib", "linear_forward",
+    "query_sizes", "workspace",
+]

@@ -1,0 +1,542 @@
+// SALR encode, residual truncated SVD and adapter concatenation.
+//
+// Method: gist.science summary of "Sparsity-Aware Low-Rank Representation
+// ...", Methodology 2 (rank-r truncated SVD of the pruning residual, used as
+// an extra low-rank adapter) and Methodology 3 (all adapters stacked along
+// the rank dimension).  The factor split is balanced: A' = V_r sqrt(S_r),
+// B' = sqrt(S_r) U_r^T.
+//
+// The pages fix neither the SVD algorithm nor its precision.  On the GPU the
+// leading singular subspace of R (N x K, bf16-exact) is found by randomized
+// subspace iteration (Halko, Martinsson and Tropp, "Finding structure with
+// randomness", 2011, Algorithm 4.4) with a basis of l = r + p columns:
+//     Y = R Omega;  repeat q times: Q = orth(Y), Z = orth(R^T Q), Y = R Z;
+//     Q = orth(Y);  Bt = R^T Q;  eig(Bt^T Bt) = U diag(lambda) U^T;
+//     sigma = sqrt(lambda),  A'^T = diag(sigma^-1/2) U_r^T Bt^T,
+//     B'^T = Q U_r diag(sigma^1/2).
+// orth() is Cholesky QR applied twice (the second pass repairs the first
+// pass's loss of orthogonality).  The big products run on fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32); the l x l Cholesky and the symmetric eigen
+// problem run in fp64 inside one workgroup (cyclic Jacobi, round-robin
+// pairing).  Omega is Gaussian from a counter-based generator (SplitMix64,
+// Steele, Lea and Flood 2014, fed to the Box-Muller transform).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <vector>
+
+#include "salr.h"
+#include "salr_device.hpp"
+#include "salr_encode.hpp"
+#include "salr_kernels.hpp"
+
+namespace salr {
+namespace {
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---------------------------------------------------------------------------
+// Generic strided fp32 GEMM: C(i,j) = alpha * sum_k A(i,k) B(k,j)
+//   A(i,k) = A[i*sa0 + k*sa1] (bf16 or fp32), B(k,j) = B[k*sb0 + j*sb1] (fp32)
+//   C(i,j) = C[i*sc0 + j*sc1]; with k_split > 1 the K range is split over
+//   blockIdx.z and partial sums are added atomically (C must start at 0).
+// 64x64 tile, 16-deep K tile, 4 waves of 32x32 (2x2 MFMA 16x16x4 tiles).
+// ---------------------------------------------------------------------------
+struct GemmArgs {
+  int64_t M, N, K;
+  const void* A;
+  int a_bf16;
+  int64_t sa0, sa1;
+  const float* B;
+  int64_t sb0, sb1;
+  float* C;
+  int64_t sc0, sc1;
+  float alpha;
+  int k_split;
+  int64_t k_chunk;
+};
+
+__device__ __forceinline__ float load_a(const GemmArgs& g, int64_t off) {
+  return g.a_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(g.A)[off]) : static_cast<const float*>(g.A)[off];
+}
+
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
+  __shared__ float As[16][64 + 4];
+  __shared__ float Bs[16][64 + 4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t i0 = (int64_t)blockIdx.y * 64, j0 = (int64_t)blockIdx.x * 64;
+  const int64_t kb = (int64_t)blockIdx.z * g.k_chunk;
+  const int64_t ke = std::min<int64_t>(g.K, kb + g.k_chunk);
+  const bool a_kcontig = g.sa1 == 1;
+  const bool b_jcontig = g.sb1 == 1;
+  f32x4_t acc[2][2] = {{zero4(), zero4()}, {zero4(), zero4()}};
+
+  for (int64_t k0 = kb; k0 < ke; k0 += 16) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      int ii, kk;
+      if (a_kcontig) { ii = tid >> 2; kk = (tid & 3) * 4 + u; }
+      else           { kk = tid >> 4; ii = (tid & 15) * 4 + u; }
+      const int64_t gi = i0 + ii, gk = k0 + kk;
+      As[kk][ii] = (gi < g.M && gk < ke) ? load_a(g, gi * g.sa0 + gk * g.sa1) : 0.f;
+      int jj, k2;
+      if (b_jcontig) { k2 = tid >> 4; jj = (tid & 15) * 4 + u; }
+      else           { jj = tid >> 2; k2 = (tid & 3) * 4 + u; }
+      const int64_t gj = j0 + jj, gk2 = k0 + k2;
+      Bs[k2][jj] = (gj < g.N && gk2 < ke) ? g.B[gk2 * g.sb0 + gj * g.sb1] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      float a[2], b[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        a[t] = As[4 * ks + lg][wm * 32 + 16 * t + li];
+        b[t] = Bs[4 * ks + lg][wn * 32 + 16 * t + li];
+      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[x], b[y], acc[x][y], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  // lane holds C(wm*32 + 16x + 4lg + e, wn*32 + 16y + li)
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t gi = i0 + wm * 32 + 16 * x + 4 * lg + e;
+        const int64_t gj = j0 + wn * 32 + 16 * y + li;
+        if (gi < g.M && gj < g.N) {
+          float* dst = &g.C[gi * g.sc0 + gj * g.sc1];
+          const float v = g.alpha * acc[x][y][e];
+          if (g.k_split > 1) atomicAdd(dst, v);
+          else *dst = v;
+        }
+      }
+}
+
+__global__ void fill_f32_kernel(float* p, int64_t n, float v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+// SplitMix64 finaliser: a bijective mix of a 64-bit counter.
+__device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
+  x += 0x9E3779B97F4A7C15ull;
+  x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
+  x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
+  return x ^ (x >> 31);
+}
+
+__global__ void gaussian_kernel(float* p, int64_t n, uint64_t seed) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const uint64_t h = splitmix64(seed * 0x100000001B3ull + (uint64_t)i);
+    const float u1 = ((float)(uint32_t)(h >> 40) + 1.0f) * (1.0f / 16777216.0f);  // (0, 1]
+    const float u2 = (float)(uint32_t)(h & 0xFFFFFFu) * (1.0f / 16777216.0f);     // [0, 1)
+    p[i] = sqrtf(-2.0f * logf(u1)) * cosf(6.28318530717958647692f * u2);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One-workgroup fp64 Cholesky of G (l x l, fp32, symmetric PSD) followed by
+// the upper-triangular C = L^{-T}, so that Y C has orthonormal columns when
+// G = Y^T Y.  A pivot below tol * max(diag) marks a direction Y does not
+// span (to working precision); its row and column of C are zero.
+// ---------------------------------------------------------------------------
+constexpr int kSmallThreads = 1024;
+
+__global__ __launch_bounds__(kSmallThreads) void chol_inv_kernel(const float* G, float* C, double* L, double* Li,
+                                                                 int l, double tol_rel) {
+  __shared__ double piv_sh;
+  __shared__ double maxd_sh;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < l * l; e += kSmallThreads) L[e] = (double)G[e];
+  __syncthreads();
+  if (tid == 0) {
+    double m = 0.0;
+    for (int d = 0; d < l; ++d) m = fmax(m, L[d * l + d]);
+    maxd_sh = m;
+  }
+  __syncthreads();
+  const double tol = tol_rel * maxd_sh;
+  for (int j = 0; j < l; ++j) {
+    if (tid == 0) {
+      const double p = L[j * l + j];
+      piv_sh = (p > tol && p > 0.0) ? sqrt(p) : 0.0;
+    }
+    __syncthreads();
+    const double d = piv_sh;
+    // column j below the diagonal
+    for (int i = j + 1 + tid; i < l; i += kSmallThreads) L[i * l + j] = d > 0.0 ? L[i * l + j] / d : 0.0;
+    if (tid == 0) L[j * l + j] = d;
+    __syncthreads();
+    // trailing update of the lower triangle
+    const int rem = l - j - 1;
+    for (int e = tid; e < rem * rem; e += kSmallThreads) {
+      const int i = j + 1 + e / rem, k = j + 1 + e % rem;
+      if (k <= i) L[i * l + k] -= L[i * l + j] * L[k * l + j];
+    }
+    __syncthreads();
+  }
+  // Li = L^{-1}: eliminate column k from all rows below it, k ascending
+  // (right-looking forward substitution on the identity, rows of a dropped
+  // pivot are zero).
+  for (int e = tid; e < l * l; e += kSmallThreads) Li[e] = (e / l == e % l) ? 1.0 : 0.0;
+  __syncthreads();
+  for (int k = 0; k < l; ++k) {
+    const double d = L[k * l + k];
+    for (int c = tid; c <= k; c += kSmallThreads) Li[k * l + c] = d > 0.0 ? Li[k * l + c] / d : 0.0;
+    __syncthreads();
+    const int rem = l - k - 1;
+    for (int e = tid; e < rem * (k + 1); e += kSmallThreads) {
+      const int i = k + 1 + e / (k + 1), c = e % (k + 1);
+      Li[i * l + c] -= L[i * l + k] * Li[k * l + c];
+    }
+    __syncthreads();
+  }
+  // C = Li^T
+  for (int e = tid; e < l * l; e += kSmallThreads) {
+    const int i = e / l, k = e % l;
+    C[e] = (float)Li[k * l + i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One-workgroup fp64 cyclic Jacobi eigensolver of a symmetric l x l matrix
+// (fp32 input S).  Rotations of one round act on disjoint index pairs from
+// the round-robin (circle) schedule, so a round is: compute all rotations,
+// rotate rows, rotate columns (of the matrix and of the eigenvector
+// matrix).  Output: eigenvalues in descending order (fp64) and the matching
+// eigenvectors as columns of U (fp32).
+// ---------------------------------------------------------------------------
+constexpr int kMaxPairs = 256;
+
+__global__ __launch_bounds__(kSmallThreads) void jacobi_kernel(const float* S, double* A, double* V, double* evals,
+                                                               float* U, int l, int max_sweeps) {
+  __shared__ double cs[kMaxPairs], sn[kMaxPairs];
+  __shared__ int pp[kMaxPairs], qq[kMaxPairs];
+  __shared__ double red[kSmallThreads];
+  __shared__ int order[512];
+  const int tid = threadIdx.x;
+  const int n = l + (l & 1);  // even number of players; index l (if any) is a dummy
+  const int npairs = n / 2;
+  for (int e = tid; e < l * l; e += kSmallThreads) {
+    const int i = e / l, j = e % l;
+    A[e] = 0.5 * ((double)S[i * l + j] + (double)S[j * l + i]);
+    V[e] = (i == j) ? 1.0 : 0.0;
+  }
+  __syncthreads();
+  for (int sweep = 0; sweep < max_sweeps; ++sweep) {
+    // convergence: off-diagonal mass vs diagonal mass
+    double off = 0.0, dia = 0.0;
+    for (int e = tid; e < l * l; e += kSmallThreads) {
+      const int i = e / l, j = e % l;
+      const double v = A[e] * A[e];
+      if (i == j) dia += v; else off += v;
+    }
+    red[tid] = off;
+    __syncthreads();
+    for (int s = kSmallThreads / 2; s > 0; s >>= 1) {
+      if (tid < s) red[tid] += red[tid + s];
+      __syncthreads();
+    }
+    const double off_t = red[0];
+    __syncthreads();
+    red[tid] = dia;
+    __syncthreads();
+    for (int s = kSmallThreads / 2; s > 0; s >>= 1) {
+      if (tid < s) red[tid] += red[tid + s];
+      __syncthreads();
+    }
+    const double dia_t = red[0];
+    __syncthreads();
+    if (off_t <= 1e-30 * (dia_t + 1e-300) || off_t == 0.0) break;
+
+    for (int round = 0; round < n - 1; ++round) {
+      if (tid < npairs) {
+        int p, q;
+        if (tid == 0) { p = n - 1; q = round; }
+        else { p = (round + tid) % (n - 1); q = (round - tid + (n - 1)) % (n - 1); }
+        if (p > q) { const int t = p; p = q; q = t; }
+        double c = 1.0, s = 0.0;
+        if (q < l) {
+          const double apq = A[p * l + q];
+          if (fabs(apq) > 1e-300) {
+            const double theta = (A[q * l + q] - A[p * l + p]) / (2.0 * apq);
+            const double t = (theta >= 0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
+            c = 1.0 / sqrt(t * t + 1.0);
+            s = t * c;
+          }
+        }
+        pp[tid] = p; qq[tid] = q; cs[tid] = c; sn[tid] = s;
+      }
+      __syncthreads();
+      // rows: A <- J^T A
+      for (int e = tid; e < npairs * l; e += kSmallThreads) {
+        const int k = e / l, j = e % l;
+        const int p = pp[k], q = qq[k];
+        if (q >= l) continue;
+        const double c = cs[k], s = sn[k];
+        const double ap = A[p * l + j], aq = A[q * l + j];
+        A[p * l + j] = c * ap - s * aq;
+        A[q * l + j] = s * ap + c * aq;
+      }
+      __syncthreads();
+      // columns: A <- A J, V <- V J
+      for (int e = tid; e < npairs * l; e += kSmallThreads) {
+        const int k = e / l, i = e % l;
+        const int p = pp[k], q = qq[k];
+        if (q >= l) continue;
+        const double c = cs[k], s = sn[k];
+        const double ap = A[i * l + p], aq = A[i * l + q];
+        A[i * l + p] = c * ap - s * aq;
+        A[i * l + q] = s * ap + c * aq;
+        const double vp = V[i * l + p], vq = V[i * l + q];
+        V[i * l + p] = c * vp - s * vq;
+        V[i * l + q] = s * vp + c * vq;
+      }
+      __syncthreads();
+    }
+  }
+  // sort eigenvalues descending (rank by counting)
+  for (int i = tid; i < l; i += kSmallThreads) {
+    const double di = A[i * l + i];
+    int rank = 0;
+    for (int j = 0; j < l; ++j) {
+      const double dj = A[j * l + j];
+      rank += (dj > di) || (dj == di && j < i);
+    }
+    order[rank] = i;
+  }
+  __syncthreads();
+  for (int r = tid; r < l; r += kSmallThreads) evals[r] = A[order[r] * l + order[r]];
+  for (int e = tid; e < l * l; e += kSmallThreads) {
+    const int i = e / l, r = e % l;
+    U[i * l + r] = (float)V[i * l + order[r]];
+  }
+}
+
+// a_cat rows [0, r): a_cat[i][k] = bf16(P[k][i] / sqrt(sigma_i)), P = Bt U_r.
+__global__ void write_a_kernel(const float* P, const double* evals, uint16_t* a_cat, int64_t K, int r) {
+  const int i = blockIdx.y;
+  const double lam = evals[i];
+  const double sg = lam > 0 ? sqrt(lam) : 0.0;
+  const float scale = sg > 1e-30 ? (float)(1.0 / sqrt(sg)) : 0.f;
+  for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < K; k += (int64_t)gridDim.x * blockDim.x)
+    a_cat[(int64_t)i * K + k] = f32_to_bf16(P[k * r + i] * scale);
+}
+
+// b_cat columns [0, r): b_cat[n][i] = bf16(S2[n][i] * sqrt(sigma_i)), S2 = Q U_r.
+__global__ void write_b_kernel(const float* S2, const double* evals, uint16_t* b_cat, int64_t N, int r, int r_cat) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < N * r; e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t n = e / r;
+    const int i = (int)(e % r);
+    const double lam = evals[i];
+    const double sg = lam > 0 ? sqrt(lam) : 0.0;
+    b_cat[n * r_cat + i] = f32_to_bf16(S2[e] * (float)sqrt(sg));
+  }
+}
+
+// LoRA blocks: a_cat rows [row0, row0 + q) <- lora_A [q][K]; b_cat columns
+// [row0, row0 + q) <- lora_B [N][q].  Bit copies.
+__global__ void copy_lora_kernel(const uint16_t* la, const uint16_t* lb, uint16_t* a_cat, uint16_t* b_cat,
+                                 int64_t N, int64_t K, int q, int row0, int r_cat) {
+  const int64_t na = (int64_t)q * K, nb = N * q;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < na + nb; e += (int64_t)gridDim.x * blockDim.x) {
+    if (e < na) {
+      a_cat[(int64_t)row0 * K + e] = la[e];
+    } else {
+      const int64_t f = e - na, n = f / q;
+      const int j = (int)(f % q);
+      b_cat[n * r_cat + row0 + j] = lb[f];
+    }
+  }
+}
+
+struct EncodeLayout {
+  int l;
+  size_t R, Y, Q, Z, Z2, G, C, dA, dB, dC, evals, U, flags, total;
+};
+
+EncodeLayout encode_layout(int64_t N, int64_t K, int32_t r_svd, int32_t oversample) {
+  EncodeLayout L{};
+  L.l = svd_basis(N, K, r_svd, oversample);
+  const size_t l = (size_t)std::max(L.l, 1);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes, 256); return o; };
+  L.flags = take(64);
+  L.R = take((size_t)N * K * 2);
+  L.Y = take((size_t)N * l * 4);
+  L.Q = take((size_t)N * l * 4);
+  L.Z = take((size_t)K * l * 4);
+  L.Z2 = take((size_t)K * l * 4);
+  L.G = take(l * l * 4);
+  L.C = take(l * l * 4);
+  L.dA = take(l * l * 8);
+  L.dB = take(l * l * 8);
+  L.dC = take(l * l * 8);
+  L.evals = take(l * 8);
+  L.U = take(l * l * 4);
+  L.total = off;
+  return L;
+}
+
+template <class T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+hipError_t gemm(hipStream_t s, int64_t M, int64_t N, int64_t K, const void* A, bool a_bf16, int64_t sa0, int64_t sa1,
+                const float* B, int64_t sb0, int64_t sb1, float* C, int64_t sc0, int64_t sc1, int k_split = 1) {
+  GemmArgs g{};
+  g.M = M; g.N = N; g.K = K;
+  g.A = A; g.a_bf16 = a_bf16 ? 1 : 0; g.sa0 = sa0; g.sa1 = sa1;
+  g.B = B; g.sb0 = sb0; g.sb1 = sb1;
+  g.C = C; g.sc0 = sc0; g.sc1 = sc1;
+  g.alpha = 1.0f;
+  g.k_chunk = align_up((size_t)cdiv(K, k_split), 16);
+  g.k_split = (int)cdiv(K, g.k_chunk);
+  if (g.k_split > 1) {
+    hipLaunchKernelGGL(fill_f32_kernel, dim3(256), dim3(256), 0, s, C, M * N, 0.0f);  // C is dense here
+  }
+  dim3 grid((unsigned)cdiv(N, 64), (unsigned)cdiv(M, 64), (unsigned)g.k_split);
+  hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
+// Split count so that a skinny product (few output tiles) still fills the GPU.
+int skinny_split(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = cdiv(M, 64) * cdiv(N, 64);
+  int64_t s = std::max<int64_t>(1, 512 / tiles);
+  return (int)std::min<int64_t>(s, std::max<int64_t>(1, K / 256));
+}
+
+// Y (rows x l, row-major) <- orthonormal basis of its column span; `tmp` has
+// the same shape.  Cholesky QR twice.
+hipError_t orth(hipStream_t s, float* Y, float* tmp, int64_t rows, int l, const EncodeLayout& E, void* ws) {
+  float* G = at<float>(ws, E.G);
+  float* C = at<float>(ws, E.C);
+  for (int pass = 0; pass < 2; ++pass) {
+    // G = Y^T Y
+    hipError_t e = gemm(s, l, l, rows, Y, false, 1, l, Y, l, 1, G, l, 1, skinny_split(l, l, rows));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(chol_inv_kernel, dim3(1), dim3(kSmallThreads), 0, s, G, C, at<double>(ws, E.dA),
+                       at<double>(ws, E.dB), l, 1e-10);
+    // tmp = Y C, then copy back
+    e = gemm(s, rows, l, l, Y, false, l, 1, C, l, 1, tmp, l, 1);
+    if (e != hipSuccess) return e;
+    e = hipMemcpyAsync(Y, tmp, (size_t)rows * l * 4, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int32_t svd_basis(int64_t N, int64_t K, int32_t r_svd, int32_t oversample) {
+  if (r_svd <= 0) return 0;
+  const int64_t cap = std::min<int64_t>(std::min(N, K), 320);
+  return (int32_t)std::min<int64_t>((int64_t)r_svd + std::max(oversample, 0), cap);
+}
+
+size_t encode_ws_bytes(int64_t N, int64_t K, int32_t r_svd, int32_t oversample) {
+  return encode_layout(N, K, r_svd, oversample).total;
+}
+
+#define CK(x)                              \
+  do {                                     \
+    if ((x) != hipSuccess) return SALR_ERR_HIP; \
+  } while (0)
+
+int encode_run(const EncodeParams& p) {
+  hipStream_t s = p.stream;
+  const EncodeLayout E = encode_layout(p.N, p.K, p.r_svd, p.oversample);
+  if (p.ws_bytes < E.total) return SALR_ERR_WORKSPACE;
+  void* ws = p.ws;
+  uint32_t* flags = at<uint32_t>(ws, E.flags);
+  uint16_t* R = at<uint16_t>(ws, E.R);
+  if (hipMemsetAsync(flags, 0, 64, s) != hipSuccess) return SALR_ERR_HIP;
+
+  // 1. selection, bitmap, values, lookup table, residual
+  PrunePackArgs pa{};
+  pa.W = p.W;
+  pa.masks = p.masks;
+  pa.values = p.values;
+  pa.offsets = p.offsets;
+  pa.R = p.r_svd > 0 ? R : nullptr;
+  pa.nonfinite = flags;
+  pa.N = p.N;
+  pa.K = (int32_t)p.K;
+  pa.n_keep = p.n_keep;
+  pa.kw = (int32_t)cdiv(p.K, 64);
+  pa.ng = (int32_t)cdiv(p.K, 1024);
+  if (launch_prune_pack(pa, s) != hipSuccess) return SALR_ERR_HIP;
+
+  // 2. residual truncated SVD
+  const int r = p.r_svd;
+  const int l = E.l;
+  std::vector<double> ev(std::max(l, 1), 0.0);
+  if (r > 0) {
+    const int64_t N = p.N, K = p.K;
+    float* Y = at<float>(ws, E.Y);
+    float* Q = at<float>(ws, E.Q);
+    float* Z = at<float>(ws, E.Z);
+    float* Z2 = at<float>(ws, E.Z2);
+    hipLaunchKernelGGL(gaussian_kernel, dim3(1024), dim3(256), 0, s, Z, K * l, p.seed);
+    // Y = R Z
+    CK(gemm(s, N, l, K, R, true, K, 1, Z, l, 1, Y, l, 1, skinny_split(N, l, K)));
+    for (int it = 0; it < p.iters; ++it) {
+      CK(orth(s, Y, Q, N, l, E, ws));
+      // Z = R^T Y
+      CK(gemm(s, K, l, N, R, true, 1, K, Y, l, 1, Z, l, 1, skinny_split(K, l, N)));
+      CK(orth(s, Z, Z2, K, l, E, ws));
+      // Y = R Z
+      CK(gemm(s, N, l, K, R, true, K, 1, Z, l, 1, Y, l, 1, skinny_split(N, l, K)));
+    }
+    CK(orth(s, Y, Q, N, l, E, ws));
+    // Bt = R^T Q  (K x l), in Z
+    CK(gemm(s, K, l, N, R, true, 1, K, Y, l, 1, Z, l, 1, skinny_split(K, l, N)));
+    // G = Bt^T Bt
+    float* G = at<float>(ws, E.G);
+    CK(gemm(s, l, l, K, Z, false, 1, l, Z, l, 1, G, l, 1, skinny_split(l, l, K)));
+    double* evals = at<double>(ws, E.evals);
+    float* U = at<float>(ws, E.U);
+    hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(kSmallThreads), 0, s, G, at<double>(ws, E.dA),
+                       at<double>(ws, E.dB), evals, U, l, 30);
+    // P = Bt U_r (K x r) in Z2; S2 = Q U_r (N x r) in Q
+    CK(gemm(s, K, r, l, Z, false, l, 1, U, l, 1, Z2, r, 1));
+    CK(gemm(s, N, r, l, Y, false, l, 1, U, l, 1, Q, r, 1));
+    hipLaunchKernelGGL(write_a_kernel, dim3((unsigned)std::min<int64_t>(cdiv(K, 256), 64), r), dim3(256), 0, s, Z2,
+                       evals, p.a_cat, K, r);
+    hipLaunchKernelGGL(write_b_kernel, dim3(1024), dim3(256), 0, s, Q, evals, p.b_cat, N, r, p.r_cat);
+    if (hipMemcpyAsync(ev.data(), evals, (size_t)l * 8, hipMemcpyDeviceToHost, s) != hipSuccess) return SALR_ERR_HIP;
+  }
+
+  // 3. LoRA blocks after the residual block, in call order
+  int row0 = r;
+  for (int a = 0; a < p.n_lora; ++a) {
+    hipLaunchKernelGGL(copy_lora_kernel, dim3(1024), dim3(256), 0, s, p.lora_A[a], p.lora_B[a], p.a_cat, p.b_cat,
+                       p.N, p.K, p.lora_r[a], row0, p.r_cat);
+    row0 += p.lora_r[a];
+  }
+  if (hipGetLastError() != hipSuccess) return SALR_ERR_HIP;
+
+  uint32_t hflags[4] = {0, 0, 0, 0};
+  if (hipMemcpyAsync(hflags, flags, sizeof(hflags), hipMemcpyDeviceToHost, s) != hipSuccess) return SALR_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return SALR_ERR_HIP;
+  if (hflags[0]) return SALR_ERR_NONFINITE;
+  for (int i = 0; i < r; ++i) {
+    if (!std::isfinite(ev[i])) return SALR_ERR_NUMERICAL;
+    if (p.sigma) p.sigma[i] = ev[i] > 0 ? std::sqrt(ev[i]) : 0.0;
+  }
+  return SALR_OK;
+}
+
+}  // namespace salr

@@ -1,0 +1,337 @@
+// SALR forward for many input rows (M > 16): tiled bitmap decode into LDS,
+// double-buffered against bf16 matrix-core tiles, with the concatenated
+// low-rank product folded in as extra K steps.
+//
+// Method: gist.science summary of "Sparsity-Aware Low-Rank Representation
+// ...", Methodology 4 (two-stage pipeline: stage 1 rebuilds dense sub-blocks
+// of W_s from the bitmap and the packed values, stage 2 feeds them to
+// matrix-core GEMM tiles, the stages decoupled so decode does not stall the
+// multiply) and Methodology 3 (one GEMM for all stacked adapters).
+//
+// Layout of one workgroup (template WM x WN waves): a BM = 64*WM token by
+// BN = 64*WN output tile, K walked in 64-column tiles (one bitmap word per W
+// row).  Each wave owns 64 outputs x 64 tokens (4x4 MFMA 16x16 tiles).  The
+// product is computed as Y^T = W_s X^T so that a lane's four accumulator
+// rows are four consecutive outputs of one token (8-byte stores).
+//
+// Pipeline per K tile kt (two barriers):
+//   issue global loads for tile kt+2 (X, packed values) and the bitmap of
+//   kt+3 into registers;
+//   MFMA on tile kt  ||  decode of tile kt+1 (LDS values -> LDS dense W);
+//   store the tile kt+2 registers into the buffers freed this iteration.
+// W rows are streams of packed values: a row's running kept count gives the
+// first value of each tile, so no lookup table is needed when K is walked
+// from column 0.
+#include "salr_device.hpp"
+#include "salr_kernels.hpp"
+
+namespace salr {
+namespace {
+
+constexpr int kLdsRow = 36;      // words per 64-column bf16 tile row (+16 B pad)
+constexpr int kVRow = 40;        // words per row of staged values (9 chunks + window)
+
+template <int WM, int WN>
+struct Cfg {
+  static constexpr int kThreads = 64 * WM * WN;
+  static constexpr int BM = 64 * WM;
+  static constexpr int BN = 64 * WN;
+  static constexpr int TPR = kThreads / BN;         // decode threads per W row
+  static constexpr int CPT = 64 / TPR;              // columns per decode thread
+  static constexpr int VCH = (9 + TPR - 1) / TPR;   // value chunks per thread
+  static constexpr int XCH = BM * 8 / kThreads;     // X chunks per thread
+};
+
+// Copy one 64-column X tile (rows m0.., cols k0..) into registers.
+template <class C>
+__device__ __forceinline__ void load_x_tile(u32x4_t (&r)[C::XCH], const uint16_t* X, int M, int K, int m0, int k0,
+                                            int tid) {
+#pragma unroll
+  for (int u = 0; u < C::XCH; ++u) {
+    const int c = tid + C::kThreads * u;
+    const int row = c >> 3, cc = c & 7;
+    const int m = m0 + row, k = k0 + 8 * cc;
+    r[u] = (m < M && k < K) ? load16(X + (size_t)m * K + k) : zero_u4();
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void store_x_tile(uint32_t* xl, const u32x4_t (&r)[C::XCH], int tid) {
+#pragma unroll
+  for (int u = 0; u < C::XCH; ++u) {
+    const int c = tid + C::kThreads * u;
+    *reinterpret_cast<u32x4_t*>(&xl[(c >> 3) * kLdsRow + (c & 7) * 4]) = r[u];
+  }
+}
+
+template <int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void fwd_large_kernel(LargeFwdArgs a) {
+  using C = Cfg<WM, WN>;
+  __shared__ uint32_t xl[2][C::BM * kLdsRow];
+  __shared__ uint32_t wl[2][C::BN * kLdsRow];
+  __shared__ uint32_t vl[C::BN * kVRow];
+  __shared__ u32x2_t lut[16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int wn = wave % WN, wm = wave / WN;
+  const int64_t n0 = (int64_t)blockIdx.x * C::BN;
+  const int m0 = blockIdx.y * C::BM;
+  const int nk = (a.K + 63) / 64;
+
+  if (tid < 16) lut[tid] = nibble_selectors(tid);
+
+  // this thread's decode row and column part
+  const int drow = tid / C::TPR, dpart = tid % C::TPR;
+  const int64_t grow = n0 + drow;
+  const bool row_ok = grow < a.N;
+  const int64_t row_base = row_ok ? grow * a.n_keep : 0;
+  const uint64_t* mrow = a.masks + (row_ok ? grow * a.kw : 0);
+  auto mask_at = [&](int kt) -> uint64_t { return (row_ok && kt < nk) ? mrow[kt] : 0ull; };
+
+  // Stage the packed values of one tile of this row: chunks covering
+  // [row_base + run, + popcount(mask)).
+  auto load_v = [&](u32x4_t (&r)[C::VCH], uint32_t run, uint64_t mk) {
+    const int64_t va = row_base + run;
+    const int cnt = __popcll(mk);
+    const int64_t q0 = va >> 3;
+    // chunks covering the segment, never past the last value of the layer
+    const int64_t q1 = min((va + cnt + 7) >> 3, a.vchunks);
+    const int n = cnt ? (int)(q1 - q0) : 0;
+#pragma unroll
+    for (int u = 0; u < C::VCH; ++u) {
+      const int ch = dpart + C::TPR * u;
+      r[u] = (ch < n) ? load16(a.values + (q0 + ch) * 8) : zero_u4();
+    }
+  };
+  auto store_v = [&](const u32x4_t (&r)[C::VCH]) {
+#pragma unroll
+    for (int u = 0; u < C::VCH; ++u) {
+      const int ch = dpart + C::TPR * u;
+      if (ch < 9) *reinterpret_cast<u32x4_t*>(&vl[drow * kVRow + ch * 4]) = r[u];
+    }
+  };
+  // Decode this thread's columns of one tile into dense bf16 in LDS.
+  auto decode = [&](uint32_t* wdst, uint32_t run, uint64_t mk) {
+    const uint32_t lead = (uint32_t)((row_base + run) & 7);
+    const uint32_t* rowbuf = &vl[drow * kVRow];
+    const int cbeg = dpart * C::CPT;
+    uint32_t idx = lead + (cbeg ? (uint32_t)__popcll(mk & ((1ull << cbeg) - 1ull)) : 0u);
+#pragma unroll
+    for (int b = 0; b < C::CPT / 8; ++b) {
+      const uint32_t byte = (uint32_t)(mk >> (cbeg + 8 * b)) & 0xFFu;
+      const u32x4_t d = expand_byte(rowbuf, idx, byte, lut);
+      *reinterpret_cast<u32x4_t*>(&wdst[drow * kLdsRow + (cbeg + 8 * b) / 2]) = d;
+      idx += __popc(byte);
+    }
+  };
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[x][y] = zero4();
+
+  auto mfma_tile = [&](const uint32_t* xs, const uint32_t* ws) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4_t av[4], bv[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        av[t] = *reinterpret_cast<const u32x4_t*>(&ws[(wn * 64 + t * 16 + i) * kLdsRow + ks * 16 + g * 4]);
+        bv[t] = *reinterpret_cast<const u32x4_t*>(&xs[(wm * 64 + t * 16 + i) * kLdsRow + ks * 16 + g * 4]);
+      }
+#pragma unroll
+      for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm) acc[tn][tm] = mfma_16x16x32(av[tn], bv[tm], acc[tn][tm]);
+    }
+  };
+
+  // ---- prologue: tiles 0 and 1 staged, tile 0 decoded
+  uint64_t mk0 = mask_at(0), mk1 = mask_at(1), mk2 = mask_at(2);
+  {
+    u32x4_t xr[C::XCH];
+    load_x_tile<C>(xr, a.X, a.M, a.K, m0, 0, tid);
+    store_x_tile<C>(xl[0], xr, tid);
+    load_x_tile<C>(xr, a.X, a.M, a.K, m0, 64, tid);
+    store_x_tile<C>(xl[1], xr, tid);
+    u32x4_t vr[C::VCH];
+    load_v(vr, 0u, mk0);
+    store_v(vr);
+    __syncthreads();
+    decode(wl[0], 0u, mk0);
+    __syncthreads();
+    load_v(vr, (uint32_t)__popcll(mk0), mk1);
+    store_v(vr);
+    __syncthreads();
+  }
+  uint32_t run1 = (uint32_t)__popcll(mk0);  // first value of tile kt+1
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const uint32_t run2 = run1 + (uint32_t)__popcll(mk1);
+    u32x4_t xr[C::XCH], vr[C::VCH];
+    load_x_tile<C>(xr, a.X, a.M, a.K, m0, (kt + 2) * 64, tid);
+    load_v(vr, run2, mk2);
+    const uint64_t mk3 = mask_at(kt + 3);
+
+    mfma_tile(xl[cur], wl[cur]);
+    decode(wl[cur ^ 1], run1, mk1);
+    __syncthreads();
+    store_x_tile<C>(xl[cur], xr, tid);
+    store_v(vr);
+    __syncthreads();
+    mk1 = mk2;
+    mk2 = mk3;
+    run1 = run2;
+  }
+
+  // ---- low-rank term as extra K tiles: Y^T += B_cat^T[n, :] T[m, :]^T
+  if (a.r_cat > 0) {
+    for (int r0 = 0; r0 < a.r_cat; r0 += 64) {
+      u32x4_t xr[C::XCH];
+#pragma unroll
+      for (int u = 0; u < C::XCH; ++u) {
+        const int c = tid + C::kThreads * u;
+        const int m = m0 + (c >> 3), k = r0 + 8 * (c & 7);
+        xr[u] = (m < a.M && k < a.r_pad) ? load16(a.T + (size_t)m * a.r_pad + k) : zero_u4();
+      }
+      store_x_tile<C>(xl[0], xr, tid);
+      const int cbeg = dpart * C::CPT;
+#pragma unroll
+      for (int c2 = 0; c2 < C::CPT; c2 += 2) {
+        const int ra = r0 + cbeg + c2;
+        const uint32_t lo = (row_ok && ra < a.r_cat) ? a.b_cat[grow * a.r_cat + ra] : 0u;
+        const uint32_t hi = (row_ok && ra + 1 < a.r_cat) ? a.b_cat[grow * a.r_cat + ra + 1] : 0u;
+        wl[0][drow * kLdsRow + (cbeg + c2) / 2] = lo | (hi << 16);
+      }
+      __syncthreads();
+      mfma_tile(xl[0], wl[0]);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: lane holds Y[m][n .. n+3]
+#pragma unroll
+  for (int tn = 0; tn < 4; ++tn) {
+    const int64_t n = n0 + wn * 64 + tn * 16 + 4 * g;
+#pragma unroll
+    for (int tm = 0; tm < 4; ++tm) {
+      const int m = m0 + wm * 64 + tm * 16 + i;
+      if (m >= a.M) continue;
+      uint16_t h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) h[e] = f32_to_bf16(acc[tn][tm][e]);
+      uint16_t* dst = a.Y + (size_t)m * a.N + n;
+      if ((a.N & 3) == 0 && n + 3 < a.N) {
+        *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{(uint32_t)h[0] | ((uint32_t)h[1] << 16),
+                                                   (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < a.N) dst[e] = h[e];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// T = X * A_cat (bf16 [M][r_pad], columns >= r_cat zero).  A workgroup owns 64
+// tokens (one 16-token MFMA tile per wave) and a K range; the A_cat slice of
+// each 64-column tile is shared through LDS.  K-split partials are summed by
+// the last workgroup of each token block, in split order.
+// ---------------------------------------------------------------------------
+constexpr int kTThreads = 256;
+constexpr int kMaxRTiles = 16;   // r_pad <= 256
+
+__global__ __launch_bounds__(kTThreads) void lowrank_t_kernel(LowRankTArgs a) {
+  __shared__ uint32_t al[kMaxRTiles * 16 * kLdsRow];
+  __shared__ uint32_t last_flag;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int mb = blockIdx.x, ks = blockIdx.y;
+  const int m0 = mb * 64;
+  const int token = m0 + wave * 16 + i;
+  const int rt = a.r_pad / 16;
+  const int k0 = ks * a.k_chunk, k1 = min(a.K, k0 + a.k_chunk);
+
+  f32x4_t acc[kMaxRTiles];
+#pragma unroll
+  for (int j = 0; j < kMaxRTiles; ++j) acc[j] = zero4();
+
+  for (int kt = k0; kt < k1; kt += 64) {
+    // stage A_cat[0..r_pad)[kt .. kt+64)
+    for (int c = tid; c < a.r_pad * 8; c += kTThreads) {
+      const int r = c >> 3, k = kt + 8 * (c & 7);
+      const u32x4_t v = (r < a.r_cat && k < k1) ? load16(a.a_cat + (size_t)r * a.K + k) : zero_u4();
+      *reinterpret_cast<u32x4_t*>(&al[r * kLdsRow + (c & 7) * 4]) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int k = kt + 32 * s + 8 * g;
+      const u32x4_t xv = (token < a.M && k < k1) ? load16(a.X + (size_t)token * a.K + k) : zero_u4();
+#pragma unroll
+      for (int j = 0; j < kMaxRTiles; ++j)
+        if (j < rt) {
+          const u32x4_t av = *reinterpret_cast<const u32x4_t*>(&al[(16 * j + i) * kLdsRow + s * 16 + g * 4]);
+          acc[j] = mfma_16x16x32(av, xv, acc[j]);
+        }
+    }
+    __syncthreads();
+  }
+
+  // lane holds T[token][16j + 4g + e]
+  const int tl = wave * 16 + i;  // token within block
+  if (a.splits > 1) {
+    float* part = a.tpart + ((size_t)mb * a.splits + ks) * 64 * a.r_pad;
+#pragma unroll
+    for (int j = 0; j < kMaxRTiles; ++j)
+      if (j < rt) *reinterpret_cast<f32x4_t*>(&part[(size_t)tl * a.r_pad + 16 * j + 4 * g]) = acc[j];
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) last_flag = (atomic_add_acq_rel(&a.count[mb], 1u) == (uint32_t)(a.splits - 1));
+    __syncthreads();
+    if (!last_flag) return;
+    __threadfence();
+#pragma unroll
+    for (int j = 0; j < kMaxRTiles; ++j) acc[j] = zero4();
+    for (int s = 0; s < a.splits; ++s) {
+      const float* p = a.tpart + ((size_t)mb * a.splits + s) * 64 * a.r_pad;
+#pragma unroll
+      for (int j = 0; j < kMaxRTiles; ++j)
+        if (j < rt) acc[j] += *reinterpret_cast<const f32x4_t*>(&p[(size_t)tl * a.r_pad + 16 * j + 4 * g]);
+    }
+    if (tid == 0) atomic_store_release(&a.count[mb], 0u);
+  }
+  if (token < a.M) {
+#pragma unroll
+    for (int j = 0; j < kMaxRTiles; ++j)
+      if (j < rt) {
+        const uint32_t lo = (uint32_t)f32_to_bf16(acc[j][0]) | ((uint32_t)f32_to_bf16(acc[j][1]) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16(acc[j][2]) | ((uint32_t)f32_to_bf16(acc[j][3]) << 16);
+        *reinterpret_cast<u32x2_t*>(&a.T[(size_t)token * a.r_pad + 16 * j + 4 * g]) = u32x2_t{lo, hi};
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_lowrank_t(const LowRankTArgs& a, hipStream_t s) {
+  dim3 grid((a.M + 63) / 64, a.splits);
+  hipLaunchKernelGGL(lowrank_t_kernel, grid, dim3(kTThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_large(const LargeFwdArgs& a, hipStream_t s) {
+  // 256 tokens x 128 outputs per workgroup, 8 waves.
+  using C = Cfg<4, 2>;
+  dim3 grid((unsigned)((a.N + C::BN - 1) / C::BN), (unsigned)((a.M + C::BM - 1) / C::BM));
+  hipLaunchKernelGGL((fwd_large_kernel<4, 2>), grid, dim3(C::kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace salr

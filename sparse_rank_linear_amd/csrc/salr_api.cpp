@@ -1,0 +1,281 @@
+// C ABI of the SALR library: argument validation, workspace layout and
+// kernel dispatch.  See include/salr.h for the contract of every entry point.
+#include "salr.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+
+#include "salr_encode.hpp"
+#include "salr_kernels.hpp"
+
+namespace {
+
+using salr::LargeFwdArgs;
+using salr::LowRankTArgs;
+using salr::SmallFwdArgs;
+
+constexpr int64_t kMaxK = int64_t(1) << 20;
+constexpr int64_t kMaxNK = int64_t(1) << 40;
+constexpr int32_t kMaxRank = 256;
+constexpr int64_t kSmallM = 16;      // M <= kSmallM takes the fused few-row kernel
+constexpr int kSmallTChunk = 512;    // producer K columns (few-row path)
+constexpr size_t kValuesPad = 256;   // tail bytes kernels may over-read
+constexpr int32_t kDefaultOversample = 32;
+constexpr int32_t kMaxOversample = 64;
+constexpr int32_t kDefaultIters = 24;
+constexpr int32_t kMaxIters = 1000;
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Byte layout of the forward workspace.  A fixed-size counter header comes
+// first, at the same offsets for every layer shape and every M, so one
+// workspace can serve many layers; every completed call leaves all counters
+// at zero.  Scratch regions follow and are written before they are read.
+constexpr size_t kCounterSync = 0;                       // 4 words
+constexpr size_t kCounterT = 16;                         // 16 words (few-row T tiles)
+constexpr size_t kCounterM = kCounterT + 16 * 4;         // 256 words (T token blocks)
+constexpr size_t kCounterY = kCounterM + 256 * 4;        // 65536 words (row tiles)
+constexpr int64_t kMaxRowTiles = 65536;
+constexpr size_t kHeaderBytes = 512 * 1024;
+static_assert(kCounterY + kMaxRowTiles * 4 <= kHeaderBytes, "counter header overflow");
+
+bool dims_ok(int64_t N, int64_t K, int32_t n_keep, int32_t r_cat) {
+  if (N < 1 || K < 1 || K > kMaxK || (K % 8) != 0) return false;
+  if (N > kMaxNK / K || N > kMaxRowTiles * 16) return false;
+  if (n_keep < 0 || n_keep > K) return false;
+  if (r_cat < 0 || r_cat > kMaxRank) return false;
+  return true;
+}
+
+// Large-path K-split count of the T = X A_cat kernel for M rows.
+int t_splits_large(int64_t M, int64_t K) {
+  const int64_t mblocks = cdiv(M, 64);
+  const int64_t nk = cdiv(K, 64);
+  // splits only while mblocks * splits <= 256 (bounded partial buffer and
+  // counter block)
+  int64_t s = std::max<int64_t>(1, 256 / mblocks);
+  return (int)std::min<int64_t>(s, nk);
+}
+
+struct FwdLayout {
+  // few-row path
+  int n_tiles, splits, r_tiles, t_splits, r_pad_small;
+  // many-row path
+  int64_t m_max;
+  int r_pad_large;
+  // offsets (bytes)
+  size_t tbuf, tpart, ypart, T, ltpart, total;
+};
+
+FwdLayout fwd_layout(int64_t N, int64_t K, int32_t r_cat, int64_t M_max) {
+  FwdLayout L{};
+  L.n_tiles = (int)cdiv(N, 16);
+  L.splits = (int)cdiv(K, 1024);
+  L.r_tiles = (int)cdiv(r_cat, 16);
+  L.t_splits = (int)cdiv(K, kSmallTChunk);
+  L.r_pad_small = (int)align_up((size_t)L.r_tiles * 16, 32);
+  L.m_max = std::max<int64_t>(M_max, 0);
+  L.r_pad_large = (int)align_up((size_t)r_cat, 16);
+
+  size_t off = kHeaderBytes;
+  L.tbuf = off;    off = align_up(off + (size_t)16 * L.r_pad_small * 2, 256);
+  L.tpart = off;   off = align_up(off + (size_t)L.r_tiles * L.t_splits * 256 * 4, 256);
+  L.ypart = off;   off = align_up(off + (L.splits > 1 ? (size_t)L.n_tiles * L.splits * 256 * 4 : 0), 256);
+  if (L.m_max > kSmallM && r_cat > 0) {
+    L.T = off;
+    off = align_up(off + (size_t)L.m_max * L.r_pad_large * 2, 256);
+    // K-split partials exist only while token blocks * splits <= 256
+    L.ltpart = off;
+    off = align_up(off + (size_t)256 * 64 * L.r_pad_large * 4, 256);
+  } else {
+    L.T = L.ltpart = off;
+  }
+  L.total = off;
+  return L;
+}
+
+template <class T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* salr_status_string(int status) {
+  switch (status) {
+    case SALR_OK: return "ok";
+    case SALR_ERR_INVALID_ARG: return "invalid argument";
+    case SALR_ERR_UNSUPPORTED: return "unsupported shape or option";
+    case SALR_ERR_WORKSPACE: return "workspace missing or too small";
+    case SALR_ERR_NONFINITE: return "weight matrix holds Inf or NaN";
+    case SALR_ERR_NUMERICAL: return "truncated SVD lost rank";
+    case SALR_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int salr_version(void) { return 10000; }
+
+int salr_query_sizes(int64_t N, int64_t K, int32_t n_keep, int32_t r_svd, int32_t r_cat, int64_t M_max,
+                     salr_sizes_t* out) {
+  if (!out) return SALR_ERR_INVALID_ARG;
+  if (!dims_ok(N, K, n_keep, r_cat)) return SALR_ERR_INVALID_ARG;
+  if (r_svd < 0 || r_svd > r_cat || r_svd > std::min<int64_t>(N, K)) return SALR_ERR_INVALID_ARG;
+  if (M_max < 0) return SALR_ERR_INVALID_ARG;
+  std::memset(out, 0, sizeof(*out));
+  out->masks_bytes = (size_t)N * cdiv(K, 64) * 8;
+  out->values_bytes = align_up((size_t)N * n_keep * 2, 256) + kValuesPad;
+  out->offsets_bytes = (size_t)N * cdiv(K, 1024) * 4;
+  out->a_cat_bytes = (size_t)r_cat * K * 2;
+  out->b_cat_bytes = (size_t)N * r_cat * 2;
+  out->encode_ws_bytes = salr::encode_ws_bytes(N, K, r_svd, kMaxOversample);
+  out->forward_ws_bytes = fwd_layout(N, K, r_cat, M_max).total;
+  return SALR_OK;
+}
+
+int salr_encode(const uint16_t* W, int64_t N, int64_t K, int32_t n_keep, int32_t r_svd, int32_t n_lora,
+                const uint16_t* const* lora_A, const uint16_t* const* lora_B, const int32_t* lora_r,
+                const salr_encode_opts_t* opts, salr_layer_t* out, double* sigma, void* ws, size_t ws_bytes,
+                void* stream) {
+  if (!out || !W) return SALR_ERR_INVALID_ARG;
+  if (out->N != N || out->K != K || out->n_keep != n_keep) return SALR_ERR_INVALID_ARG;
+  if (!dims_ok(N, K, n_keep, out->r_cat)) return SALR_ERR_INVALID_ARG;
+  if (r_svd < 0 || r_svd > std::min<int64_t>(N, K)) return SALR_ERR_INVALID_ARG;
+  if (n_lora < 0 || (n_lora > 0 && (!lora_A || !lora_B || !lora_r))) return SALR_ERR_INVALID_ARG;
+  int64_t r_cat = r_svd;
+  for (int i = 0; i < n_lora; ++i) {
+    if (lora_r[i] < 1 || !lora_A[i] || !lora_B[i]) return SALR_ERR_INVALID_ARG;
+    if (!aligned16(lora_A[i]) || !aligned16(lora_B[i])) return SALR_ERR_INVALID_ARG;
+    r_cat += lora_r[i];
+    if (r_cat > kMaxRank) return SALR_ERR_INVALID_ARG;
+  }
+  if (r_cat != out->r_cat) return SALR_ERR_INVALID_ARG;
+  if (!out->masks || !out->offsets || (n_keep > 0 && !out->values)) return SALR_ERR_INVALID_ARG;
+  if (r_cat > 0 && (!out->a_cat || !out->b_cat)) return SALR_ERR_INVALID_ARG;
+  const void* ptrs[] = {W, out->masks, out->values, out->offsets, out->a_cat, out->b_cat};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return SALR_ERR_INVALID_ARG;
+  salr::EncodeParams p{};
+  p.oversample = opts ? opts->oversample : kDefaultOversample;
+  p.iters = opts ? opts->iters : kDefaultIters;
+  p.seed = opts ? opts->seed : 0;
+  if (p.oversample < 0 || p.oversample > kMaxOversample || p.iters < 0 || p.iters > kMaxIters)
+    return SALR_ERR_INVALID_ARG;
+  if (!ws || !aligned16(ws)) return SALR_ERR_WORKSPACE;
+  if (ws_bytes < salr::encode_ws_bytes(N, K, r_svd, p.oversample)) return SALR_ERR_WORKSPACE;
+  p.W = W;
+  p.N = N;
+  p.K = K;
+  p.n_keep = n_keep;
+  p.r_svd = r_svd;
+  p.r_cat = (int32_t)r_cat;
+  p.n_lora = n_lora;
+  p.lora_A = lora_A;
+  p.lora_B = lora_B;
+  p.lora_r = lora_r;
+  p.masks = out->masks;
+  p.values = out->values;
+  p.offsets = out->offsets;
+  p.a_cat = out->a_cat;
+  p.b_cat = out->b_cat;
+  p.sigma = sigma;
+  p.ws = ws;
+  p.ws_bytes = ws_bytes;
+  p.stream = static_cast<hipStream_t>(stream);
+  return salr::encode_run(p);
+}
+
+int salr_linear_forward(const salr_layer_t* L, const uint16_t* X, int64_t M, uint16_t* Y, void* ws, size_t ws_bytes,
+                        void* stream) {
+  if (!L) return SALR_ERR_INVALID_ARG;
+  if (!dims_ok(L->N, L->K, L->n_keep, L->r_cat)) return SALR_ERR_INVALID_ARG;
+  if (M < 0 || M > (int64_t(1) << 31) - 1) return SALR_ERR_INVALID_ARG;
+  if (M == 0) return SALR_OK;
+  if (!X || !Y || !L->masks || !L->offsets) return SALR_ERR_INVALID_ARG;
+  if (L->n_keep > 0 && !L->values) return SALR_ERR_INVALID_ARG;
+  if (L->r_cat > 0 && (!L->a_cat || !L->b_cat)) return SALR_ERR_INVALID_ARG;
+  const void* ptrs[] = {X, Y, L->masks, L->values, L->offsets, L->a_cat, L->b_cat};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return SALR_ERR_INVALID_ARG;
+  if (static_cast<const void*>(X) == static_cast<const void*>(Y)) return SALR_ERR_INVALID_ARG;
+  if (!ws || !aligned16(ws)) return SALR_ERR_WORKSPACE;
+  const FwdLayout W = fwd_layout(L->N, L->K, L->r_cat, M);
+  if (ws_bytes < W.total) return SALR_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  hipError_t err;
+  if (M <= kSmallM) {
+    SmallFwdArgs a{};
+    a.masks = L->masks;
+    a.values = L->values;
+    a.offsets = L->offsets;
+    a.a_cat = L->a_cat;
+    a.b_cat = L->b_cat;
+    a.X = X;
+    a.Y = Y;
+    a.N = L->N;
+    a.K = (int32_t)L->K;
+    a.n_keep = L->n_keep;
+    a.r_cat = L->r_cat;
+    a.M = (int32_t)M;
+    a.kw = (int32_t)cdiv(L->K, 64);
+    a.ng = (int32_t)cdiv(L->K, 1024);
+    a.n_tiles = W.n_tiles;
+    a.splits = W.splits;
+    a.r_tiles = W.r_tiles;
+    a.t_splits = W.t_splits;
+    a.t_chunk = kSmallTChunk;
+    a.r_pad = W.r_pad_small;
+    a.sync = at<uint32_t>(ws, kCounterSync);
+    a.tcount = at<uint32_t>(ws, kCounterT);
+    a.ycount = at<uint32_t>(ws, kCounterY);
+    a.tbuf = at<uint16_t>(ws, W.tbuf);
+    a.tpart = at<float>(ws, W.tpart);
+    a.ypart = at<float>(ws, W.ypart);
+    err = salr::launch_fwd_small(a, s);
+  } else {
+    if (L->r_cat > 0) {
+      LowRankTArgs t{};
+      t.X = X;
+      t.a_cat = L->a_cat;
+      t.T = at<uint16_t>(ws, W.T);
+      t.tpart = at<float>(ws, W.ltpart);
+      t.count = at<uint32_t>(ws, kCounterM);
+      t.M = (int32_t)M;
+      t.K = (int32_t)L->K;
+      t.r_cat = L->r_cat;
+      t.r_pad = W.r_pad_large;
+      t.splits = t_splits_large(M, L->K);
+      t.k_chunk = (int32_t)(cdiv(cdiv(L->K, 64), t.splits) * 64);
+      t.splits = (int32_t)cdiv(L->K, t.k_chunk);
+      err = salr::launch_lowrank_t(t, s);
+      if (err != hipSuccess) return SALR_ERR_HIP;
+    }
+    LargeFwdArgs a{};
+    a.masks = L->masks;
+    a.values = L->values;
+    a.b_cat = L->b_cat;
+    a.X = X;
+    a.T = L->r_cat > 0 ? at<uint16_t>(ws, W.T) : nullptr;
+    a.Y = Y;
+    a.N = L->N;
+    a.K = (int32_t)L->K;
+    a.n_keep = L->n_keep;
+    a.r_cat = L->r_cat;
+    a.r_pad = W.r_pad_large;
+    a.M = (int32_t)M;
+    a.kw = (int32_t)cdiv(L->K, 64);
+    a.vchunks = cdiv(L->N * (int64_t)L->n_keep, 8);
+    err = salr::launch_fwd_large(a, s);
+  }
+  return err == hipSuccess ? SALR_OK : SALR_ERR_HIP;
+}
+
+}  // extern "C"

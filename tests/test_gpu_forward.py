@@ -1,0 +1,102 @@
+"""Forward parity: the HIP forward (through the C ABI) against the oracle's
+float64 forward on the same encoded layer, element by element.
+
+Small shapes span several tiles and ragged tails in N, K and M on both the
+few-row (M <= 16) and many-row kernels, plus the degenerate cases (no
+adapters, nothing pruned, everything pruned, one row)."""
+
+import numpy as np
+import pytest
+
+from oracle import bf16 as ob
+from oracle import salr as osl
+from sparse_rank_linear_amd import synth
+from tests.gpu_util import TOL_MAX_REL, TOL_NORMWISE, errors, say, to_dev, to_host_bits, upload_encoded
+
+pytestmark = pytest.mark.gpu
+
+# N, K, n_keep, r_svd, LoRA ranks, token counts
+CASES = [
+    (512, 512, 256, 16, (8,), (1, 5, 16, 17, 64, 300)),
+    (100, 520, 260, 4, (3, 5), (1, 16, 33, 257)),
+    (48, 2056, 1000, 0, (), (1, 16, 40)),
+    (33, 1024, 1024, 0, (16,), (2, 20)),
+    (40, 1032, 0, 0, (8,), (3, 70)),
+    (1, 64, 17, 1, (), (1, 30)),
+    (200, 3072, 1536, 8, (4, 4, 4), (7, 16, 130)),
+]
+
+
+@pytest.fixture(scope="module")
+def shared_ws():
+    import sparse_rank_linear_amd as srl
+
+    # one workspace for every call in this module: exercises the counter
+    # protocol across layer shapes and both token regimes
+    need = max(srl.query_sizes(N, K, nk, rs, rs + sum(lr), max(ms))["forward_ws_bytes"]
+               for (N, K, nk, rs, lr, ms) in CASES)
+    return srl.workspace(need)
+
+
+def _encode_case(N, K, n_keep, r_svd, loras, seed):
+    rng = np.random.default_rng(seed)
+    W = synth.make_w(N, K, seed)
+    As = [ob.f64_to_bits(rng.standard_normal((q, K)).astype(np.float32) * 0.01) for q in loras]
+    Bs = [ob.f64_to_bits(rng.standard_normal((N, q)).astype(np.float32) * 0.01) for q in loras]
+    return osl.encode(W, n_keep, r_svd, As, Bs)
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"N{c[0]}_K{c[1]}_keep{c[2]}_r{c[3]}")
+def test_forward_matches_oracle(case, shared_ws):
+    import torch
+    import sparse_rank_linear_amd as srl
+
+    N, K, n_keep, r_svd, loras, Ms = case
+    enc = _encode_case(N, K, n_keep, r_svd, loras, seed=N + K)
+    layer = upload_encoded(enc, K, r_svd)
+    for M in Ms:
+        say(f"forward N={N} K={K} n_keep={n_keep} r_cat={layer.r_cat} M={M}")
+        X = synth.make_x(K, M, seed=M + 7)
+        Y = srl.linear_forward(layer, to_dev(X), ws=shared_ws)
+        torch.cuda.synchronize()
+        Yref = osl.forward(X, enc.masks, enc.values, K, enc.A_cat, enc.B_cat)
+        mr, nw = errors(to_host_bits(Y), Yref)
+        say(f"  max_rel={mr:.3e} normwise={nw:.3e}")
+        assert mr <= TOL_MAX_REL and nw <= TOL_NORMWISE
+
+
+@pytest.mark.parametrize("M", [4, 16, 100])
+def test_forward_deterministic(M, shared_ws):
+    import torch
+    import sparse_rank_linear_amd as srl
+
+    enc = _encode_case(300, 4096, 2048, 16, (16,), seed=3)
+    layer = upload_encoded(enc, 4096, 16)
+    X = to_dev(synth.make_x(4096, M, seed=5))
+    Y1 = srl.linear_forward(layer, X, ws=shared_ws)
+    Y2 = srl.linear_forward(layer, X, ws=shared_ws)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
+
+
+def test_forward_zero_rows_is_noop(shared_ws):
+    import torch
+    import sparse_rank_linear_amd as srl
+
+    enc = _encode_case(16, 64, 32, 0, (), seed=1)
+    layer = upload_encoded(enc, 64, 0)
+    X = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    Y = srl.linear_forward(layer, X, ws=shared_ws)
+    assert Y.shape == (0, 16)
+
+
+def test_forward_rejects_small_workspace():
+    import torch
+    import sparse_rank_linear_amd as srl
+
+    enc = _encode_case(16, 64, 32, 0, (), seed=1)
+    layer = upload_encoded(enc, 64, 0)
+    X = torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros(1024, dtype=torch.uint8, device="cuda")
+    with pytest.raises(srl.SalrError, match="WORKSPACE"):
+        srl.linear_forward(layer, X, ws=ws)
