@@ -33,8 +33,9 @@ def shared_ws():
 
     # one workspace for every call in this module: exercises the counter
     # protocol across layer shapes and both token regimes
-    need = max(srl.query_sizes(N, K, nk, rs, rs + sum(lr), max(ms))["forward_ws_bytes"]
-               for (N, K, nk, rs, lr, ms) in CASES)
+    shapes = [(N, K, nk, rs, rs + sum(lr), max(ms)) for (N, K, nk, rs, lr, ms) in CASES]
+    shapes.append((300, 4096, 2048, 16, 32, 100))  # test_forward_deterministic
+    need = max(srl.query_sizes(*s)["forward_ws_bytes"] for s in shapes)
     return srl.workspace(need)
 
 
