@@ -48,7 +48,9 @@
  *           order (summary, Methodology 2 and 3).
  *   b_cat   bf16   [N][r_cat]       B_cat TRANSPOSED: row n holds output n's
  *           coefficients on the r_cat components; columns [0, r_svd) are the
- *           residual adapter U_r sqrt(S_r), then each LoRA up-projection.
+ *           residual adapter U_r sqrt(S_r), then each LoRA up-projection.  The
+ *           buffer must be sizes.b_cat_bytes long (tail padding, as for
+ *           values).
  */
 #ifndef SALR_H_
 #define SALR_H_

@@ -173,7 +173,9 @@ class SalrLayer:
             values=torch.zeros(sz["values_bytes"] // 2, dtype=torch.bfloat16, device=device),
             offsets=torch.zeros((N, ng), dtype=torch.int32, device=device),
             a_cat=torch.zeros((max(r_cat, 0), K), dtype=torch.bfloat16, device=device),
-            b_cat=torch.zeros((N, max(r_cat, 0)), dtype=torch.bfloat16, device=device),
+            # [N][r_cat] view of a buffer with the tail padding the kernels need
+            b_cat=torch.zeros(sz["b_cat_bytes"] // 2, dtype=torch.bfloat16,
+                              device=device)[: N * max(r_cat, 0)].view(N, max(r_cat, 0)),
         )
 
     @classmethod
@@ -207,8 +209,10 @@ class SalrLayer:
         return d
 
     def clone(self) -> "SalrLayer":
-        return SalrLayer(self.N, self.K, self.n_keep, self.r_svd, self.r_cat, self.masks.clone(),
-                         self.values.clone(), self.offsets.clone(), self.a_cat.clone(), self.b_cat.clone())
+        c = SalrLayer.empty(self.N, self.K, self.n_keep, self.r_svd, self.r_cat, self.masks.device)
+        for name in ("masks", "values", "offsets", "a_cat", "b_cat"):
+            getattr(c, name).copy_(getattr(self, name))
+        return c
 
     def to_numpy(self) -> dict:
         """Device tensors back as numpy arrays in the stored layout."""

@@ -45,8 +45,6 @@ def sources():
 def _compile(hipcc: str, src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     cmd = [hipcc, *COMMON, "-c", src, "-o", obj]
-    if src.endswith(".cpp"):
-        cmd = [hipcc, *[c for c in COMMON if not c.startswith("--offload-arch")], "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
     if res.returncode != 0:

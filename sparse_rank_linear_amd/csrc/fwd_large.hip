@@ -115,7 +115,7 @@ __global__ __launch_bounds__(64 * WM * WN) void fwd_large_kernel(LargeFwdArgs a)
   // Decode this thread's columns of one tile into dense bf16 in LDS.
   auto decode = [&](uint32_t* wdst, uint32_t run, uint64_t mk) {
     const uint32_t lead = (uint32_t)((row_base + run) & 7);
-    const uint32_t* rowbuf = &vl[drow * kVRow];
+    const uint16_t* rowbuf = reinterpret_cast<const uint16_t*>(&vl[drow * kVRow]);
     const int cbeg = dpart * C::CPT;
     uint32_t idx = lead + (cbeg ? (uint32_t)__popcll(mk & ((1ull << cbeg) - 1ull)) : 0u);
 #pragma unroll
@@ -188,15 +188,30 @@ __global__ __launch_bounds__(64 * WM * WN) void fwd_large_kernel(LargeFwdArgs a)
     run1 = run2;
   }
 
-  // ---- low-rank term as extra K tiles: Y^T += B_cat^T[n, :] T[m, :]^T
+  // ---- low-rank term as extra K tiles: Y^T += B_cat^T[n, :] T[m, :]^T, where
+  // T = X A_cat is the sum of the K-split partials (written by the previous
+  // launch), rounded to bf16 before it meets B_cat.
   if (a.r_cat > 0) {
+    const size_t split_stride = (size_t)a.M * a.r_pad;
     for (int r0 = 0; r0 < a.r_cat; r0 += 64) {
       u32x4_t xr[C::XCH];
 #pragma unroll
       for (int u = 0; u < C::XCH; ++u) {
         const int c = tid + C::kThreads * u;
         const int m = m0 + (c >> 3), k = r0 + 8 * (c & 7);
-        xr[u] = (m < a.M && k < a.r_pad) ? load16(a.T + (size_t)m * a.r_pad + k) : zero_u4();
+        xr[u] = zero_u4();
+        if (m < a.M && k < a.r_pad) {
+          f32x4_t lo = zero4(), hi = zero4();
+          const float* src = a.tpart + (size_t)m * a.r_pad + k;
+          for (int sp = 0; sp < a.t_splits; ++sp) {
+            lo += *reinterpret_cast<const f32x4_t*>(src + sp * split_stride);
+            hi += *reinterpret_cast<const f32x4_t*>(src + sp * split_stride + 4);
+          }
+          xr[u] = u32x4_t{(uint32_t)f32_to_bf16(lo[0]) | ((uint32_t)f32_to_bf16(lo[1]) << 16),
+                          (uint32_t)f32_to_bf16(lo[2]) | ((uint32_t)f32_to_bf16(lo[3]) << 16),
+                          (uint32_t)f32_to_bf16(hi[0]) | ((uint32_t)f32_to_bf16(hi[1]) << 16),
+                          (uint32_t)f32_to_bf16(hi[2]) | ((uint32_t)f32_to_bf16(hi[3]) << 16)};
+        }
       }
       store_x_tile<C>(xl[0], xr, tid);
       const int cbeg = dpart * C::CPT;
@@ -238,23 +253,22 @@ __global__ __launch_bounds__(64 * WM * WN) void fwd_large_kernel(LargeFwdArgs a)
 }
 
 // ---------------------------------------------------------------------------
-// T = X * A_cat (bf16 [M][r_pad], columns >= r_cat zero).  A workgroup owns 64
-// tokens (one 16-token MFMA tile per wave) and a K range; the A_cat slice of
-// each 64-column tile is shared through LDS.  K-split partials are summed by
-// the last workgroup of each token block, in split order.
+// Partial T = X * A_cat over one K range per workgroup, fp32, written to
+// tpart[split][M][r_pad] (columns >= r_cat are zero).  A workgroup owns 64
+// tokens (one 16-token MFMA tile per wave); the A_cat slice of each
+// 64-column tile is shared through LDS.  The splits are summed by the
+// consumer (the next launch), so no workgroup waits for another.
 // ---------------------------------------------------------------------------
 constexpr int kTThreads = 256;
 constexpr int kMaxRTiles = 16;   // r_pad <= 256
 
 __global__ __launch_bounds__(kTThreads) void lowrank_t_kernel(LowRankTArgs a) {
   __shared__ uint32_t al[kMaxRTiles * 16 * kLdsRow];
-  __shared__ uint32_t last_flag;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, g = lane >> 4;
   const int mb = blockIdx.x, ks = blockIdx.y;
-  const int m0 = mb * 64;
-  const int token = m0 + wave * 16 + i;
+  const int token = mb * 64 + wave * 16 + i;
   const int rt = a.r_pad / 16;
   const int k0 = ks * a.k_chunk, k1 = min(a.K, k0 + a.k_chunk);
 
@@ -285,36 +299,11 @@ __global__ __launch_bounds__(kTThreads) void lowrank_t_kernel(LowRankTArgs a) {
   }
 
   // lane holds T[token][16j + 4g + e]
-  const int tl = wave * 16 + i;  // token within block
-  if (a.splits > 1) {
-    float* part = a.tpart + ((size_t)mb * a.splits + ks) * 64 * a.r_pad;
-#pragma unroll
-    for (int j = 0; j < kMaxRTiles; ++j)
-      if (j < rt) *reinterpret_cast<f32x4_t*>(&part[(size_t)tl * a.r_pad + 16 * j + 4 * g]) = acc[j];
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) last_flag = (atomic_add_acq_rel(&a.count[mb], 1u) == (uint32_t)(a.splits - 1));
-    __syncthreads();
-    if (!last_flag) return;
-    __threadfence();
-#pragma unroll
-    for (int j = 0; j < kMaxRTiles; ++j) acc[j] = zero4();
-    for (int s = 0; s < a.splits; ++s) {
-      const float* p = a.tpart + ((size_t)mb * a.splits + s) * 64 * a.r_pad;
-#pragma unroll
-      for (int j = 0; j < kMaxRTiles; ++j)
-        if (j < rt) acc[j] += *reinterpret_cast<const f32x4_t*>(&p[(size_t)tl * a.r_pad + 16 * j + 4 * g]);
-    }
-    if (tid == 0) atomic_store_release(&a.count[mb], 0u);
-  }
   if (token < a.M) {
+    float* dst = a.tpart + ((size_t)ks * a.M + token) * a.r_pad;
 #pragma unroll
     for (int j = 0; j < kMaxRTiles; ++j)
-      if (j < rt) {
-        const uint32_t lo = (uint32_t)f32_to_bf16(acc[j][0]) | ((uint32_t)f32_to_bf16(acc[j][1]) << 16);
-        const uint32_t hi = (uint32_t)f32_to_bf16(acc[j][2]) | ((uint32_t)f32_to_bf16(acc[j][3]) << 16);
-        *reinterpret_cast<u32x2_t*>(&a.T[(size_t)token * a.r_pad + 16 * j + 4 * g]) = u32x2_t{lo, hi};
-      }
+      if (j < rt) *reinterpret_cast<f32x4_t*>(&dst[16 * j + 4 * g]) = acc[j];
   }
 }
 

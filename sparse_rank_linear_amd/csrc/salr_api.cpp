@@ -21,7 +21,8 @@ constexpr int64_t kMaxK = int64_t(1) << 20;
 constexpr int64_t kMaxNK = int64_t(1) << 40;
 constexpr int32_t kMaxRank = 256;
 constexpr int64_t kSmallM = 16;      // M <= kSmallM takes the fused few-row kernel
-constexpr int kSmallTChunk = 512;    // producer K columns (few-row path)
+constexpr size_t kSmallLdsBudget = 150 * 1024;  // one few-row workgroup per CU
+constexpr int64_t kFillWgs = 256;               // few-row consumers wanted to fill the GPU
 constexpr size_t kValuesPad = 256;   // tail bytes kernels may over-read
 constexpr int32_t kDefaultOversample = 32;
 constexpr int32_t kMaxOversample = 64;
@@ -41,8 +42,10 @@ constexpr size_t kCounterT = 16;                         // 16 words (few-row T 
 constexpr size_t kCounterM = kCounterT + 16 * 4;         // 256 words (T token blocks)
 constexpr size_t kCounterY = kCounterM + 256 * 4;        // 65536 words (row tiles)
 constexpr int64_t kMaxRowTiles = 65536;
+constexpr size_t kCounterG = kCounterY + kMaxRowTiles * 4;  // 2048 words (completion groups)
+constexpr int kMaxDoneGroups = 2048;
 constexpr size_t kHeaderBytes = 512 * 1024;
-static_assert(kCounterY + kMaxRowTiles * 4 <= kHeaderBytes, "counter header overflow");
+static_assert(kCounterG + kMaxDoneGroups * 4 <= kHeaderBytes, "counter header overflow");
 
 bool dims_ok(int64_t N, int64_t K, int32_t n_keep, int32_t r_cat) {
   if (N < 1 || K < 1 || K > kMaxK || (K % 8) != 0) return false;
@@ -64,36 +67,64 @@ int t_splits_large(int64_t M, int64_t K) {
 
 struct FwdLayout {
   // few-row path
-  int n_tiles, splits, r_tiles, t_splits, r_pad_small;
+  int n_tiles, splits, range, vcap, r_tiles, r_pad_small, t_pieces, k_range;
+  int vals_bytes, tl_bytes, bl_bytes;
   // many-row path
   int64_t m_max;
   int r_pad_large;
   // offsets (bytes)
-  size_t tbuf, tpart, ypart, T, ltpart, total;
+  size_t tsum, ypart, T, ltpart, total;
 };
 
-FwdLayout fwd_layout(int64_t N, int64_t K, int32_t r_cat, int64_t M_max) {
+FwdLayout fwd_layout(int64_t N, int64_t K, int32_t n_keep, int32_t r_cat, int64_t M_max) {
   FwdLayout L{};
   L.n_tiles = (int)cdiv(N, 16);
-  L.splits = (int)cdiv(K, 1024);
+  // Few-row T pieces: K ranges of <= 2048 columns; their partial sums are
+  // staged in LDS by the main launch, at most 32 KB of them.
   L.r_tiles = (int)cdiv(r_cat, 16);
-  L.t_splits = (int)cdiv(K, kSmallTChunk);
-  L.r_pad_small = (int)align_up((size_t)L.r_tiles * 16, 32);
+  L.r_pad_small = (int)align_up((size_t)std::max(L.r_tiles, 1) * 16, 32);
+  {
+    const int64_t max_pieces = std::max<int64_t>(1, (32 * 1024) / (16 * L.r_pad_small * 4));
+    const int64_t want = std::max<int64_t>(cdiv(K, 2048), std::min<int64_t>(4, cdiv(K, 512)));
+    L.t_pieces = (int)std::min<int64_t>(std::max<int64_t>(want, 1), std::max(max_pieces, cdiv(K, 2048)));
+    L.k_range = (int)align_up((size_t)cdiv(K, L.t_pieces), 32);
+    L.t_pieces = (int)cdiv(K, L.k_range);
+  }
+  L.tl_bytes = r_cat > 0 ? L.t_pieces * 16 * L.r_pad_small * 4 : 0;
+  L.bl_bytes = r_cat > 0 ? (int)align_up((size_t)16 * r_cat * 2, 16) : 0;
+  // Few-row column ranges: whole rows when they fit (no lookup-table round
+  // trip), else the widest range that fits; narrower ranges while there are
+  // too few workgroups to occupy the GPU.
+  const auto vcap_for = [&](int64_t range) { return salr::fwd_small_vcap(std::min<int64_t>(range, n_keep)); };
+  const auto lds_for = [&](int64_t range) { return salr::fwd_small_lds_bytes(vcap_for(range), L.tl_bytes, L.bl_bytes); };
+  L.range = 0;
+  if (K <= salr::kMaxRangeCols && lds_for(K) <= kSmallLdsBudget && (L.n_tiles >= kFillWgs || K <= 1024)) {
+    L.range = (int)K;
+  } else {
+    for (int range = salr::kMaxRangeCols; range >= 1024; range /= 2) {
+      if (lds_for(range) > kSmallLdsBudget) continue;
+      L.range = range;
+      if ((int64_t)L.n_tiles * cdiv(K, range) >= kFillWgs) break;
+    }
+    if (L.range == 0) L.range = 1024;
+    if (L.range >= K) L.range = (int)K;
+  }
+  L.splits = (int)cdiv(K, L.range);
+  L.vcap = vcap_for(L.range);
+  L.vals_bytes = (int)salr::fwd_small_vals_bytes(L.vcap);
   L.m_max = std::max<int64_t>(M_max, 0);
   L.r_pad_large = (int)align_up((size_t)r_cat, 16);
 
   size_t off = kHeaderBytes;
-  L.tbuf = off;    off = align_up(off + (size_t)16 * L.r_pad_small * 2, 256);
-  L.tpart = off;   off = align_up(off + (size_t)L.r_tiles * L.t_splits * 256 * 4, 256);
-  L.ypart = off;   off = align_up(off + (L.splits > 1 ? (size_t)L.n_tiles * L.splits * 256 * 4 : 0), 256);
+  // few-row path: T partials (fp32) and tagged range partials
+  L.tsum = off;    off = align_up(off + (size_t)L.tl_bytes, 256);
+  L.ypart = off;   off = align_up(off + (L.splits > 1 ? (size_t)L.n_tiles * L.splits * 256 * 8 : 0), 256);
+  // many-row path: fp32 split-K partials of T = X A_cat
+  L.T = L.ltpart = off;
   if (L.m_max > kSmallM && r_cat > 0) {
-    L.T = off;
-    off = align_up(off + (size_t)L.m_max * L.r_pad_large * 2, 256);
-    // K-split partials exist only while token blocks * splits <= 256
-    L.ltpart = off;
-    off = align_up(off + (size_t)256 * 64 * L.r_pad_large * 4, 256);
-  } else {
-    L.T = L.ltpart = off;
+    // splits * M <= 64 * max(256, ceil(M/64)) for every M <= m_max
+    const size_t rows = (size_t)std::max<int64_t>(64 * 256, cdiv(L.m_max, 64) * 64);
+    off = align_up(off + rows * L.r_pad_large * 4, 256);
   }
   L.total = off;
   return L;
@@ -134,9 +165,9 @@ int salr_query_sizes(int64_t N, int64_t K, int32_t n_keep, int32_t r_svd, int32_
   out->values_bytes = align_up((size_t)N * n_keep * 2, 256) + kValuesPad;
   out->offsets_bytes = (size_t)N * cdiv(K, 1024) * 4;
   out->a_cat_bytes = (size_t)r_cat * K * 2;
-  out->b_cat_bytes = (size_t)N * r_cat * 2;
+  out->b_cat_bytes = align_up((size_t)N * r_cat * 2, 256) + kValuesPad;
   out->encode_ws_bytes = salr::encode_ws_bytes(N, K, r_svd, kMaxOversample);
-  out->forward_ws_bytes = fwd_layout(N, K, r_cat, M_max).total;
+  out->forward_ws_bytes = fwd_layout(N, K, n_keep, r_cat, M_max).total;
   return SALR_OK;
 }
 
@@ -206,20 +237,34 @@ int salr_linear_forward(const salr_layer_t* L, const uint16_t* X, int64_t M, uin
     if (p && !aligned16(p)) return SALR_ERR_INVALID_ARG;
   if (static_cast<const void*>(X) == static_cast<const void*>(Y)) return SALR_ERR_INVALID_ARG;
   if (!ws || !aligned16(ws)) return SALR_ERR_WORKSPACE;
-  const FwdLayout W = fwd_layout(L->N, L->K, L->r_cat, M);
+  const FwdLayout W = fwd_layout(L->N, L->K, L->n_keep, L->r_cat, M);
   if (ws_bytes < W.total) return SALR_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   hipError_t err;
   if (M <= kSmallM) {
+    if (L->r_cat > 0) {
+      salr::SmallTArgs t{};
+      t.X = X;
+      t.a_cat = L->a_cat;
+      t.tsum = at<float>(ws, W.tsum);
+      t.M = (int32_t)M;
+      t.K = (int32_t)L->K;
+      t.r_cat = L->r_cat;
+      t.r_pad = W.r_pad_small;
+      t.r_tiles = W.r_tiles;
+      t.t_pieces = W.t_pieces;
+      t.k_range = W.k_range;
+      if (salr::launch_lowrank_t_small(t, s) != hipSuccess) return SALR_ERR_HIP;
+    }
     SmallFwdArgs a{};
     a.masks = L->masks;
     a.values = L->values;
     a.offsets = L->offsets;
-    a.a_cat = L->a_cat;
     a.b_cat = L->b_cat;
     a.X = X;
     a.Y = Y;
+    a.tsum = at<float>(ws, W.tsum);
     a.N = L->N;
     a.K = (int32_t)L->K;
     a.n_keep = L->n_keep;
@@ -229,25 +274,32 @@ int salr_linear_forward(const salr_layer_t* L, const uint16_t* X, int64_t M, uin
     a.ng = (int32_t)cdiv(L->K, 1024);
     a.n_tiles = W.n_tiles;
     a.splits = W.splits;
+    a.range = W.range;
+    a.vcap = W.vcap;
     a.r_tiles = W.r_tiles;
-    a.t_splits = W.t_splits;
-    a.t_chunk = kSmallTChunk;
     a.r_pad = W.r_pad_small;
+    a.t_pieces = W.t_pieces;
+    a.vals_bytes = W.vals_bytes;
+    a.tl_bytes = W.tl_bytes;
+    a.bl_bytes = W.bl_bytes;
     a.sync = at<uint32_t>(ws, kCounterSync);
-    a.tcount = at<uint32_t>(ws, kCounterT);
     a.ycount = at<uint32_t>(ws, kCounterY);
-    a.tbuf = at<uint16_t>(ws, W.tbuf);
-    a.tpart = at<float>(ws, W.tpart);
-    a.ypart = at<float>(ws, W.ypart);
+    a.gdone = at<uint32_t>(ws, kCounterG);
+    {
+      const int64_t n_wgs = (int64_t)W.n_tiles * W.splits;
+      int64_t groups = 1;
+      while (groups * groups < n_wgs) ++groups;
+      a.done_groups = (int32_t)std::min<int64_t>(groups, kMaxDoneGroups);
+    }
+    a.ypart = at<uint64_t>(ws, W.ypart);
     err = salr::launch_fwd_small(a, s);
   } else {
+    int t_splits = 0;
     if (L->r_cat > 0) {
       LowRankTArgs t{};
       t.X = X;
       t.a_cat = L->a_cat;
-      t.T = at<uint16_t>(ws, W.T);
       t.tpart = at<float>(ws, W.ltpart);
-      t.count = at<uint32_t>(ws, kCounterM);
       t.M = (int32_t)M;
       t.K = (int32_t)L->K;
       t.r_cat = L->r_cat;
@@ -255,6 +307,7 @@ int salr_linear_forward(const salr_layer_t* L, const uint16_t* X, int64_t M, uin
       t.splits = t_splits_large(M, L->K);
       t.k_chunk = (int32_t)(cdiv(cdiv(L->K, 64), t.splits) * 64);
       t.splits = (int32_t)cdiv(L->K, t.k_chunk);
+      t_splits = t.splits;
       err = salr::launch_lowrank_t(t, s);
       if (err != hipSuccess) return SALR_ERR_HIP;
     }
@@ -263,7 +316,8 @@ int salr_linear_forward(const salr_layer_t* L, const uint16_t* X, int64_t M, uin
     a.values = L->values;
     a.b_cat = L->b_cat;
     a.X = X;
-    a.T = L->r_cat > 0 ? at<uint16_t>(ws, W.T) : nullptr;
+    a.tpart = L->r_cat > 0 ? at<float>(ws, W.ltpart) : nullptr;
+    a.t_splits = t_splits;
     a.Y = Y;
     a.N = L->N;
     a.K = (int32_t)L->K;

@@ -41,11 +41,12 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
 //
 // Four consecutive columns whose keep-bits form the nibble q take their
 // values, in order, from a packed stream u[0], u[1], ... (bf16).  Given the
-// stream window e0 = u0 | u1<<16, e1 = u2 | u3<<16, the dense 4-column group
-// is two v_perm_b32 byte selections of {e1, e0}: column c reads u[popcount
-// of q's bits below c] when its bit is set, and 0x00 bytes (selector 12)
-// otherwise.  nibble_selectors(q) gives the two selector words; kernels keep
-// the 16 entries in LDS.
+// stream window e0 = u0 | u1<<16, e1 = u2 | u3<<16 (the 4 values from the
+// group's first kept value on), the dense 4-column group is two v_perm_b32
+// byte selections of {e1, e0}: column c reads u[popcount of q's bits below
+// c] when its bit is set, and 0x00 bytes (selector 12) otherwise.
+// nibble_selectors(q) gives the two selector words; kernels keep the 16
+// entries in LDS.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ u32x2_t nibble_selectors(uint32_t q) {
   uint32_t sel[4];
@@ -62,41 +63,111 @@ __device__ __forceinline__ u32x2_t nibble_selectors(uint32_t q) {
   return u32x2_t{sel[0] | (sel[1] << 16), sel[2] | (sel[3] << 16)};
 }
 
-// Dense 4-column group from packed values starting at value index `idx` of a
-// row buffer in LDS (`buf32` = the buffer as 32-bit words, 4-byte aligned).
-// Reads three words at the word holding value idx; a funnel shift drops the
-// odd leading value.  Words past the live values may be read; they are never
-// selected because their keep-bits are clear.
-__device__ __forceinline__ u32x2_t expand_nibble(const uint32_t* buf32, uint32_t idx, u32x2_t sel) {
-  const uint32_t w = idx >> 1;
+// Window of the 4 stream values starting at value index idx of a bf16
+// stream in LDS, as two 32-bit words: three aligned words are read (one
+// 8-byte read of an even word pair plus one word; unaligned 8-byte LDS reads
+// are correct on CDNA but slower) and a funnel shift drops an odd leading
+// value.  Words past the live values may be read; they are never selected.
+struct Window3 {
+  uint32_t d0, d1, d2;
+};
+__device__ __forceinline__ Window3 lds_window_words(const uint16_t* vals, uint32_t idx) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(vals) + (idx >> 1);
+  return Window3{w[0], w[1], w[2]};
+}
+__device__ __forceinline__ u32x2_t window_values(Window3 w, uint32_t idx) {
   const uint32_t sh = (idx & 1u) << 4;
-  const uint32_t d0 = buf32[w], d1 = buf32[w + 1], d2 = buf32[w + 2];
-  const uint32_t e0 = __builtin_amdgcn_alignbit(d1, d0, sh);
-  const uint32_t e1 = __builtin_amdgcn_alignbit(d2, d1, sh);
-  return u32x2_t{__builtin_amdgcn_perm(e1, e0, sel.x), __builtin_amdgcn_perm(e1, e0, sel.y)};
+  return u32x2_t{__builtin_amdgcn_alignbit(w.d1, w.d0, sh), __builtin_amdgcn_alignbit(w.d2, w.d1, sh)};
 }
 
-// Dense 8-column group (one MFMA operand slice) for byte pattern `byte` whose
-// first kept value is stream index `idx`.
-__device__ __forceinline__ u32x4_t expand_byte(const uint32_t* buf32, uint32_t idx, uint32_t byte,
-                                               const u32x2_t* lut) {
+// Dense 4-column group from the window of the 4 stream values starting at the
+// group's first kept value.
+__device__ __forceinline__ u32x2_t expand_nibble(u32x2_t win, u32x2_t sel) {
+  return u32x2_t{__builtin_amdgcn_perm(win.y, win.x, sel.x), __builtin_amdgcn_perm(win.y, win.x, sel.y)};
+}
+
+// Dense 8-column group (one MFMA operand slice) for keep-bits `byte` whose
+// first kept value is stream index `idx` (two windows: one per nibble).
+__device__ __forceinline__ u32x4_t expand_byte(const uint16_t* vals, uint32_t idx, uint32_t byte, const u32x2_t* lut) {
   const uint32_t lo = byte & 15u, hi = byte >> 4;
-  const u32x2_t a = expand_nibble(buf32, idx, lut[lo]);
-  const u32x2_t b = expand_nibble(buf32, idx + __builtin_popcount(lo), lut[hi]);
+  const uint32_t idx2 = idx + __builtin_popcount(lo);
+  const u32x2_t a = expand_nibble(window_values(lds_window_words(vals, idx), idx), lut[lo]);
+  const u32x2_t b = expand_nibble(window_values(lds_window_words(vals, idx2), idx2), lut[hi]);
   return u32x4_t{a.x, a.y, b.x, b.y};
 }
 
 // ---------------------------------------------------------------------------
-// Agent-scope synchronisation between workgroups of one launch.
+// Passing data between workgroups of one launch.
+//
+// On a multi-die GPU an agent-scope fence writes back or invalidates the
+// whole L2 of the die, which is far too slow to do per workgroup.  So no
+// such fence is used.  Instead every word one workgroup hands to another is
+// a 64-bit "tagged" word: 32 data bits and, in the high half, the launch's
+// tag, written with one device-coherent 64-bit store.  Readers poll each
+// word with device-coherent loads until its tag equals the current launch's
+// tag, so they can never consume a stale or torn value, whatever order the
+// stores become visible in.  Counters (device-coherent atomics) only elect
+// which workgroup performs a reduction; they order nothing.
+//
+// The launch tag is epoch+1, where epoch lives in the workspace and is
+// advanced by the last workgroup of each launch (a "done" counter elects
+// it), after every workgroup of that launch has read it.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t atomic_add_acq_rel(uint32_t* p, uint32_t v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+__device__ __forceinline__ uint32_t atomic_add_relaxed(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint32_t atomic_load_acquire(uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint32_t load_coherent(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void atomic_store_release(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void store_coherent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_tagged(uint64_t* p, uint32_t data, uint32_t tag) {
+  __hip_atomic_store(p, ((uint64_t)tag << 32) | data, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t load_tagged_raw(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until all n (<= 4) consecutive tagged words at p carry `tag`; return
+// their data halves.  Bounded: after kSpinLimit polls the error word is set
+// and the (stale) data returned, so a kernel can never hang here.
+template <int n>
+__device__ __forceinline__ void poll_tagged(const uint64_t* p, uint32_t tag, uint32_t (&out)[n], uint32_t* err) {
+  uint32_t spins = 0;
+  while (true) {
+    bool ok = true;
+#pragma unroll
+    for (int k = 0; k < n; ++k) {
+      const uint64_t v = load_tagged_raw(p + k);
+      out[k] = (uint32_t)v;
+      ok &= (uint32_t)(v >> 32) == tag;
+    }
+    if (ok) return;
+    if (++spins >= kSpinLimit) {
+      store_coherent(err, 1u);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// Called once per workgroup, by one lane, as the workgroup's last action:
+// the workgroup that completes the launch advances the epoch.  Device-scope
+// atomics on one address serialise (about 11 ns each on MI355X), so the
+// workgroups count in ngroups interleaved groups first and only each
+// group's last finisher touches the launch-wide counter.
+__device__ __forceinline__ void finish_launch(uint32_t* epoch, uint32_t* done, uint32_t* gdone, uint32_t wg,
+                                              uint32_t n_wgs, uint32_t ngroups) {
+  const uint32_t g = wg % ngroups;
+  const uint32_t gsize = n_wgs / ngroups + (g < n_wgs % ngroups ? 1u : 0u);
+  if (atomic_add_relaxed(&gdone[g], 1u) != gsize - 1) return;
+  store_coherent(&gdone[g], 0u);
+  if (atomic_add_relaxed(done, 1u) != ngroups - 1) return;
+  store_coherent(done, 0u);
+  store_coherent(epoch, load_coherent(epoch) + 1u);
 }
 
 __device__ __forceinline__ u32x4_t load16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }

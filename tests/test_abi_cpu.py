@@ -44,7 +44,7 @@ def test_query_sizes_layout():
     assert sz["values_bytes"] >= N * n_keep * 2 + 256
     assert sz["offsets_bytes"] == N * (K // 1024) * 4
     assert sz["a_cat_bytes"] == r_cat * K * 2
-    assert sz["b_cat_bytes"] == N * r_cat * 2
+    assert sz["b_cat_bytes"] >= N * r_cat * 2 + 256  # tail padding, like values
     assert sz["forward_ws_bytes"] >= 512 * 1024
     assert sz["encode_ws_bytes"] >= N * K * 2
     # ragged shapes round up
