@@ -168,7 +168,11 @@ int salr_encode(const uint16_t* W, int64_t N, int64_t K, int32_t n_keep,
  * ws  device workspace of at least forward_ws_bytes for some M_max >= M.
  *     It must be zero-filled before its first use; every completed call
  *     leaves it ready for the next one.  Two calls that share a workspace
- *     must be ordered (same stream or synchronised).
+ *     must be ordered (same stream or synchronised).  Workgroups of one
+ *     call hand partial results to each other through the workspace and
+ *     every such wait is bounded: should one time out, the uint32 at byte
+ *     offset 8 of ws becomes nonzero (and Y is unreliable); the library
+ *     never clears it.
  * Products accumulate in fp32; X*A_cat is rounded to bf16 before it meets
  * B_cat; Y is rounded to bf16 (nearest-even).
  * Asynchronous on `stream`: returns after queueing.  Errors: INVALID_ARG,

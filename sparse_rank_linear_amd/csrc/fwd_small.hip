@@ -26,14 +26,17 @@
 //     their latencies overlap;
 //   * range partials of one row tile are combined by the last workgroup to
 //     finish, in range order (results do not depend on scheduling);
-//   * T = X A_cat comes from a small preceding launch (lowrank_t_small
-//     below, a few K-pieces of fp32 partial sums); the main launch copies
-//     those partials and the tile's B_cat rows into LDS together with the
-//     weights, so the low-rank term T B_cat is a few LDS reads and extra
-//     matrix-core steps at the end;
-//   * range partials handed between workgroups travel as tagged words (see
-//     salr_device.hpp), so no cache-wide fence is ever executed; with whole
-//     rows there is no cross-workgroup traffic at all.
+//   * T = X A_cat is cut into pieces of 16 ranks x (a multiple of 1024)
+//     columns.  The first workgroups each compute one piece as soon as their
+//     own data has landed (its operands are fetched with the weights) and
+//     publish it; after its decode every workgroup gathers the pieces of its
+//     share of the ranks, summing them in a fixed order into LDS, and adds
+//     T B_cat for those ranks (B_cat rows fetched with the weights) as extra
+//     matrix-core steps.  With whole rows a workgroup takes all ranks; with
+//     ranges, range r takes the 32-rank chunks r, r + ranges, ..., so the
+//     low-rank work and its gather traffic are spread over the ranges;
+//   * pieces and range partials handed between workgroups travel as tagged
+//     words (see salr_device.hpp), so no cache-wide fence is ever executed.
 #include "salr_device.hpp"
 #include "salr_kernels.hpp"
 
@@ -57,7 +60,13 @@ struct Lds {
   uint32_t seg[kRows][2];  // per-row range of kept-value indices (within the row)
   int64_t vorg[kRows];     // global value index = LDS value slot + vorg (per row)
   uint64_t masks[kRows * kMaskRowWords];
+  f32x4_t pred[3 * 64];  // wave sums of a T piece (waves 1-3)
+  uint32_t tag;
 };
+constexpr int kPieceWaves = 4;                         // waves computing a T piece
+constexpr int kPieceSteps = 1024 / 32 / kPieceWaves;  // their steps per 1024-column chunk
+constexpr int kFinBatch = 4;                           // pieces requested together when finishing T
+constexpr int kMaxLoadRows = kRows / (kWaves - kPieceWaves);  // rows per load-issuing wave
 static_assert(sizeof(Lds) % 16 == 0, "values area must stay 16-byte aligned");
 
 __device__ __forceinline__ u32x4_t load_x_frag(const uint16_t* X, int M, int K, int m, int col) {
@@ -142,21 +151,29 @@ void fwd_small_kernel(SmallFwdArgs a) {
   Lds& L = *reinterpret_cast<Lds*>(smem);
   uint32_t* const vals = reinterpret_cast<uint32_t*>(smem + sizeof(Lds));
   f32x4_t* const red = reinterpret_cast<f32x4_t*>(vals);
-  // after the values area: the T partials [t_pieces][16][r_pad] fp32, then
-  // the tile's B_cat rows [16][r_cat] bf16
-  float* const tl = reinterpret_cast<float*>(smem + sizeof(Lds) + a.vals_bytes);
+  // after the values area: this workgroup's T chunks as MFMA operands
+  // [chunk][64 lanes] (bf16 pairs), then the tile's B_cat rows [16][r_cat]
+  u32x4_t* const tl = reinterpret_cast<u32x4_t*>(smem + sizeof(Lds) + a.vals_bytes);
   uint16_t* const bl = reinterpret_cast<uint16_t*>(smem + sizeof(Lds) + a.vals_bytes + a.tl_bytes);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, g = lane >> 4;
   const uint32_t n_wgs = gridDim.x;
-  const bool talk = a.splits > 1;  // any cross-workgroup data?
-  uint32_t* const epoch = &a.sync[0];
-  uint32_t* const done = &a.sync[1];
-  uint32_t* const err = &a.sync[2];
-  const uint32_t ngroups = (uint32_t)a.done_groups;
-  const uint32_t tag = load_coherent(epoch) + 1u;
+  const bool talk = a.splits > 1 || a.r_cat > 0;  // any cross-workgroup data?
+  uint32_t* const err = a.err;
+  // This launch's tag: the ticket is drawn now and resolved by wave 0 where
+  // first needed (its latency hides behind the loads issued meanwhile).
+  uint64_t drawn = 0;
+  if (talk && tid == 0) drawn = draw_ticket(a.tickets, blockIdx.x, n_wgs);
+  uint32_t tag = 0;
+  bool resolved = false;
+  const auto resolve_tag = [&]() {
+    uint32_t t = 0;
+    if (lane == 0) t = tag_from_ticket(a.tickets, drawn, blockIdx.x, n_wgs);
+    tag = __shfl(t, 0);
+    resolved = true;
+  };
   f32x4_t acc = zero4();
 
   // ---------------- this workgroup's weights: 16 rows x one column range
@@ -171,76 +188,193 @@ void fwd_small_kernel(SmallFwdArgs a) {
   const int s0 = wave * spw;
   const int nwords = (ncols + 63) / 64;            // bitmap words in the range
   const int rows_here = (int)min<int64_t>(kRows, a.N - row0);
+  const int n_pieces = a.r_tiles * a.t_pieces;
+  const bool producer = c < n_pieces;
+  // In a workgroup that computes T pieces, waves 0-3 do that while waves 4-7
+  // issue every weight load; elsewhere all waves issue them.
+  const int lw0 = producer ? kPieceWaves : 0;
 
-  // X operand slices of this wave's steps (independent of the weights).
   u32x4_t xf[kMaxSteps];
+  const auto load_x_frags = [&]() {
 #pragma unroll
-  for (int q = 0; q < kMaxSteps; ++q)
-    xf[q] = (q < spw) ? load_x_frag(a.X, a.M, a.K, i, col0 + 32 * (s0 + q) + 8 * g) : zero_u4();
+    for (int q = 0; q < kMaxSteps; ++q)
+      xf[q] = (q < spw) ? load_x_frag(a.X, a.M, a.K, i, col0 + 32 * (s0 + q) + 8 * g) : zero_u4();
+  };
 
+  if (wave >= lw0) load_x_frags();
   if (tid < 16) L.lut[tid] = nibble_selectors(tid);
-  // Bitmap words of the range, per row 2*nwords dwords direct to LDS; rows
-  // past N read as zero.
-  for (int r = wave; r < kRows; r += kWaves) {
-    uint32_t* dst = reinterpret_cast<uint32_t*>(&L.masks[r * kMaskRowWords]);
-    if (r < rows_here) {
-      const uint32_t* src = reinterpret_cast<const uint32_t*>(a.masks + (row0 + r) * a.kw + (col0 >> 6));
-      for (int b = 0; b * 64 < 2 * nwords; ++b)
-        if (b * 64 + lane < 2 * nwords) __builtin_amdgcn_global_load_lds(src + b * 64 + lane, dst + b * 64, 4, 0, 0);
-    } else {
-      for (int w = lane; w < 2 * kMaskRowWords; w += 64) dst[w] = 0u;
+  if (wave >= lw0) {
+    const int lw = wave - lw0, lws = kWaves - lw0;
+    // Bitmap words of the range, per row 2*nwords dwords direct to LDS; rows
+    // past N read as zero.
+    for (int r = lw; r < kRows; r += lws) {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(&L.masks[r * kMaskRowWords]);
+      if (r < rows_here) {
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(a.masks + (row0 + r) * a.kw + (col0 >> 6));
+        for (int b = 0; b * 64 < 2 * nwords; ++b)
+          if (b * 64 + lane < 2 * nwords) __builtin_amdgcn_global_load_lds(src + b * 64 + lane, dst + b * 64, 4, 0, 0);
+      } else {
+        for (int w = lane; w < 2 * kMaskRowWords; w += 64) dst[w] = 0u;
+      }
     }
-  }
-  if (a.splits == 1) {
-    // Whole rows: row r's values start at (row0 + r) * n_keep, known without
-    // reading anything.  Each row gets its own LDS area (vcap chunks, the
-    // stride chosen so that row areas start in different LDS banks).
-    if (tid < kRows) L.seg[tid][0] = 0;
-    for (int r = wave; r < kRows; r += kWaves) {
-      const int64_t va = (row0 + r) * a.n_keep, vb = va + a.n_keep;
-      const int64_t q0 = va >> 3, nch = (r < rows_here && vb > va) ? ((vb + 7) >> 3) - q0 : 0;
-      copy_chunks_to_lds(reinterpret_cast<const uint32_t*>(a.values) + q0 * 4, vals + (size_t)r * a.vcap * 4, nch,
-                         0, 1, lane);
-      if (lane == 0) L.vorg[r] = q0 * 8 - (int64_t)r * a.vcap * 8;
-    }
-  } else {
-    // A range of a longer row: locate each row's values with the lookup
-    // table (one round trip), then copy each row's chunks.
-    if (tid < kRows) {
-      const int64_t row = row0 + tid;
-      uint32_t lo = 0, hi = 0;
-      if (tid < rows_here) {
-        const int g0 = col0 >> 10, g1 = (col0 + ncols + 1023) >> 10;  // lookup-table entries
-        hi = (g1 < a.ng) ? a.offsets[row * a.ng + g1] : (uint32_t)a.n_keep;
-        hi = min(hi, (uint32_t)a.n_keep);
-        lo = min(a.offsets[row * a.ng + g0], hi);
+    // Values: row r's kept values [lo, hi) (indices within the row) go to
+    // the row's own LDS area (vcap chunks, a stride that starts row areas in
+    // different banks).  Whole rows need nothing read first; a range reads
+    // its bounds from the per-row lookup table (entries every 1024 columns).
+    uint32_t seg_lo[kMaxLoadRows], seg_hi[kMaxLoadRows];
+#pragma unroll
+    for (int k = 0; k < kMaxLoadRows; ++k) {
+      const int r = lw + k * lws;
+      uint32_t lo = 0, hi = (uint32_t)a.n_keep;
+      if (a.splits > 1 && r < rows_here) {
+        const uint32_t* orow = a.offsets + (row0 + r) * a.ng;
+        const int g0 = col0 >> 10, g1 = (col0 + ncols + 1023) >> 10;
+        hi = min(g1 < a.ng ? orow[g1] : (uint32_t)a.n_keep, (uint32_t)a.n_keep);
+        lo = min(orow[g0], hi);
         lo = max(lo, hi > (uint32_t)a.range ? hi - (uint32_t)a.range : 0u);  // inside the row's LDS area
       }
-      L.seg[tid][0] = lo;
-      L.seg[tid][1] = hi;
+      seg_lo[k] = lo;
+      seg_hi[k] = hi;
     }
-    __syncthreads();
-    for (int r = wave; r < kRows; r += kWaves) {
-      const int64_t va = (row0 + r) * a.n_keep + L.seg[r][0];
-      const int64_t vb = (row0 + r) * a.n_keep + L.seg[r][1];
-      const int64_t q0 = va >> 3, nch = (r < rows_here && vb > va) ? ((vb + 7) >> 3) - q0 : 0;
-      copy_chunks_to_lds(reinterpret_cast<const uint32_t*>(a.values) + q0 * 4, vals + (size_t)r * a.vcap * 4, nch,
-                         0, 1, lane);
-      if (lane == 0) L.vorg[r] = q0 * 8 - (int64_t)r * a.vcap * 8;
+#pragma unroll
+    for (int k = 0; k < kMaxLoadRows; ++k) {
+      const int r = lw + k * lws;
+      if (r < kRows) {
+        const int64_t va = (row0 + r) * a.n_keep + seg_lo[k], vb = (row0 + r) * a.n_keep + seg_hi[k];
+        const int64_t q0 = va >> 3, nch = (r < rows_here && vb > va) ? ((vb + 7) >> 3) - q0 : 0;
+        copy_chunks_to_lds(reinterpret_cast<const uint32_t*>(a.values) + q0 * 4, vals + (size_t)r * a.vcap * 4, nch,
+                           0, 1, lane);
+        if (lane == 0) {
+          L.vorg[r] = q0 * 8 - (int64_t)r * a.vcap * 8;
+          L.seg[r][0] = seg_lo[k];
+        }
+      }
+    }
+    // This tile's B_cat rows.
+    if (a.r_cat > 0) {
+      const int64_t bbytes = (int64_t)rows_here * a.r_cat * 2;
+      copy_chunks_to_lds(reinterpret_cast<const uint32_t*>(a.b_cat + row0 * a.r_cat), reinterpret_cast<uint32_t*>(bl),
+                         (bbytes + 15) / 16, lw, lws, lane);
     }
   }
 
-  // Low-rank operands for the epilogue, fetched with the weights: the T
-  // partials of the preceding launch and this tile's B_cat rows.
-  if (a.r_cat > 0) {
-    copy_chunks_to_lds(reinterpret_cast<const uint32_t*>(a.tsum), reinterpret_cast<uint32_t*>(tl),
-                       (int64_t)a.tl_bytes / 16, wave, kWaves, lane);
-    const int64_t bbytes = (int64_t)rows_here * a.r_cat * 2;
-    copy_chunks_to_lds(reinterpret_cast<const uint32_t*>(a.b_cat + row0 * a.r_cat), reinterpret_cast<uint32_t*>(bl),
-                       (bbytes + 15) / 16, (wave + 3) % kWaves, kWaves, lane);
+  // ---------------- T pieces (producer workgroups, waves 0-3)
+  // Piece p = (rank tile j, K range kp) is T^T[16 ranks][16 tokens] summed
+  // over t_chunks * 1024 columns; workgroup c takes pieces c, c + n_wgs, ...
+  // Wave 0 publishes each piece as tagged words (lane (i, g) holds ranks
+  // 16j + 4g + e of token i) and counts it; the workgroup that completes a
+  // rank tile's count sums the tile's pieces in K order and publishes T for
+  // the tile as bf16 pairs.  Every workgroup waits on nothing before its
+  // pieces are published, so no wait here can depend on a later one.
+  if (producer) {
+    uint32_t elected = 0;  // rank tiles this workgroup completes (bit j)
+    for (int piece = c; piece < n_pieces; piece += (int)n_wgs) {
+      const int j = piece / a.t_pieces, kp = piece % a.t_pieces;
+      f32x4_t t = zero4();
+      if (wave < kPieceWaves) {
+        const int rank = 16 * j + i;
+        for (int ch = 0; ch < a.t_chunks; ++ch) {
+          u32x4_t pav[kPieceSteps], pxv[kPieceSteps];
+#pragma unroll
+          for (int q = 0; q < kPieceSteps; ++q) {
+            const int col = (kp * a.t_chunks + ch) * 1024 + 32 * (wave * kPieceSteps + q) + 8 * g;
+            pav[q] = (rank < a.r_cat && col < a.K) ? load16(a.a_cat + (size_t)rank * a.K + col) : zero_u4();
+            pxv[q] = load_x_frag(a.X, a.M, a.K, i, col);
+          }
+#pragma unroll
+          for (int q = 0; q < kPieceSteps; ++q) t = mfma_16x16x32(pav[q], pxv[q], t);
+        }
+        if (wave > 0) L.pred[(wave - 1) * 64 + lane] = t;
+      }
+      __syncthreads();
+      if (wave == 0) {
+        if (!resolved) resolve_tag();
+#pragma unroll
+        for (int w = 0; w < kPieceWaves - 1; ++w) t += L.pred[w * 64 + lane];
+        uint64_t* dst = a.tpiece + ((size_t)piece * 64 + lane) * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = t[e];  // (scalar copy first: see reduce_parts)
+          store_tagged(dst + e, __float_as_uint(v), tag);
+        }
+      }
+      __syncthreads();
+    }
+    if (wave == 0) {
+      for (int piece = c; piece < n_pieces; piece += (int)n_wgs) {
+        const int j = piece / a.t_pieces;
+        uint32_t old = 0;
+        if (lane == 0) old = atomic_add_relaxed(&a.tcount[j], 1u);
+        old = __shfl(old, 0);
+        if (old == (uint32_t)(a.t_pieces - 1)) elected |= 1u << j;
+      }
+      while (elected) {
+        const int j = __builtin_ctz(elected);
+        elected &= elected - 1;
+        if (lane == 0) store_coherent(&a.tcount[j], 0u);
+        float sum[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int kp0 = 0; kp0 < a.t_pieces; kp0 += kFinBatch) {
+          uint64_t v[kFinBatch][4];
+#pragma unroll
+          for (int b = 0; b < kFinBatch; ++b)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              v[b][e] = (kp0 + b < a.t_pieces)
+                            ? load_tagged_raw(a.tpiece + ((size_t)(j * a.t_pieces + kp0 + b) * 64 + lane) * 4 + e)
+                            : 0ull;
+#pragma unroll
+          for (int b = 0; b < kFinBatch; ++b) {
+            if (kp0 + b < a.t_pieces) {
+              bool ok = true;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) ok &= (uint32_t)(v[b][e] >> 32) == tag;
+              uint32_t w[4];
+              if (ok) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[e] = (uint32_t)v[b][e];
+              } else {
+                poll_tagged<4>(a.tpiece + ((size_t)(j * a.t_pieces + kp0 + b) * 64 + lane) * 4, tag, w, err);
+              }
+#pragma unroll
+              for (int e = 0; e < 4; ++e) sum[e] += __uint_as_float(w[e]);
+            }
+          }
+        }
+        uint64_t* dst = a.tfinal + ((size_t)j * 64 + lane) * 2;
+        store_tagged(dst, (uint32_t)f32_to_bf16(sum[0]) | ((uint32_t)f32_to_bf16(sum[1]) << 16), tag);
+        store_tagged(dst + 1, (uint32_t)f32_to_bf16(sum[2]) | ((uint32_t)f32_to_bf16(sum[3]) << 16), tag);
+      }
+    }
   }
+
+  // X operand slices of this wave's steps (piece waves: after the piece).
+  if (wave < lw0) load_x_frags();
+
   __builtin_amdgcn_s_waitcnt(0);
+  if (talk && wave == 0) {
+    if (!resolved) resolve_tag();
+    if (lane == 0) L.tag = tag;
+  }
   __syncthreads();
+  if (talk) tag = L.tag;
+
+  // This workgroup's share of the low-rank term: the 32-rank chunks rng,
+  // rng + splits, ...; wave k requests chunk k's T operand now and checks it
+  // after the decode.  Lane (i, g) needs T[token i][32q + 8g .. +7]: tile
+  // 2q + g/2, i.e. the words of lanes i + 16 g' (g' = 2(g % 2), +1) there.
+  const int n_chunks = a.r_pad / 32;
+  const int n_own = a.r_cat > 0 && rng < n_chunks ? (n_chunks - rng + a.splits - 1) / a.splits : 0;
+  const int my_chunk = rng + wave * a.splits;
+  const int tj = 2 * my_chunk + (g >> 1);
+  const bool t_live = wave < n_own && tj < a.r_tiles;
+  const uint64_t* tsrc = a.tfinal + ((size_t)tj * 64 + i + 32 * (g & 1)) * 2;
+  uint64_t tw[4] = {0ull, 0ull, 0ull, 0ull};
+  if (t_live) {
+    tw[0] = load_tagged_raw(tsrc);
+    tw[1] = load_tagged_raw(tsrc + 1);
+    tw[2] = load_tagged_raw(tsrc + 32);
+    tw[3] = load_tagged_raw(tsrc + 33);
+  }
 
   // Decode + multiply this wave's steps.  The wave's bitmap words come to
   // registers first; then each batch of kBatch steps issues all its LDS
@@ -295,46 +429,46 @@ void fwd_small_kernel(SmallFwdArgs a) {
       }
     }
   }
-  if (!reduce_waves(acc, red, wave, lane)) return;
-  if (a.splits > 1) {
-    if (!reduce_parts(acc, a.ypart + (size_t)tile * a.splits * 256, a.splits, rng, &a.ycount[tile], tag, err,
-                      lane)) {
-      if (lane == 0) finish_launch(epoch, done, a.gdone, blockIdx.x, n_wgs, ngroups);
-      return;
-    }
-  }
 
-  // Low-rank term: acc += B_cat^T[rows, :] T^T, as extra K steps.  T is the
-  // sum of the partials, rounded to bf16 before it meets B_cat.
-  if (a.r_cat > 0) {
-    const int tcols = a.r_tiles * 16;
-    for (int r0 = 0; r0 < a.r_pad; r0 += 32) {
-      const int rb = r0 + 8 * g;
-      uint32_t w[4];
+  // The T operand of this wave's chunk, into LDS for the epilogue.
+  if (wave < n_own) {
+    uint32_t d[4] = {0u, 0u, 0u, 0u};
+    if (t_live) {
+      bool ok = true;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int ra = rb + 2 * e;
-        const uint32_t lo = (i < rows_here && ra < a.r_cat) ? bl[i * a.r_cat + ra] : 0u;
-        const uint32_t hi = (i < rows_here && ra + 1 < a.r_cat) ? bl[i * a.r_cat + ra + 1] : 0u;
-        w[e] = lo | (hi << 16);
+        d[e] = (uint32_t)tw[e];
+        ok &= (uint32_t)(tw[e] >> 32) == tag;
       }
-      u32x4_t tv = zero_u4();
-      if (rb < tcols) {
-        f32x4_t s0v = zero4(), s1v = zero4();
-        for (int p = 0; p < a.t_pieces; ++p) {
-          const float* src = tl + ((size_t)p * 16 + i) * a.r_pad + rb;
-          s0v += *reinterpret_cast<const f32x4_t*>(src);
-          s1v += *reinterpret_cast<const f32x4_t*>(src + 4);
-        }
-        const float t0 = s0v[0], t1 = s0v[1], t2 = s0v[2], t3 = s0v[3];
-        const float t4 = s1v[0], t5 = s1v[1], t6 = s1v[2], t7 = s1v[3];
-        tv = u32x4_t{(uint32_t)f32_to_bf16(t0) | ((uint32_t)f32_to_bf16(t1) << 16),
-                     (uint32_t)f32_to_bf16(t2) | ((uint32_t)f32_to_bf16(t3) << 16),
-                     (uint32_t)f32_to_bf16(t4) | ((uint32_t)f32_to_bf16(t5) << 16),
-                     (uint32_t)f32_to_bf16(t6) | ((uint32_t)f32_to_bf16(t7) << 16)};
+      if (!ok) {
+        uint32_t d0[2], d1[2];
+        poll_tagged<2>(tsrc, tag, d0, err);
+        poll_tagged<2>(tsrc + 32, tag, d1, err);
+        d[0] = d0[0], d[1] = d0[1], d[2] = d1[0], d[3] = d1[1];
       }
-      acc = mfma_16x16x32(u32x4_t{w[0], w[1], w[2], w[3]}, tv, acc);
     }
+    tl[wave * 64 + lane] = u32x4_t{d[0], d[1], d[2], d[3]};
+  }
+  if (!reduce_waves(acc, red, wave, lane)) return;
+
+  // Low-rank term for this workgroup's chunks: acc += B_cat^T[rows, chunk]
+  // T^T[chunk, :], as extra K steps (T already rounded to bf16).
+  for (int k = 0; k < n_own; ++k) {
+    const int rb = 32 * (rng + k * a.splits) + 8 * g;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ra = rb + 2 * e;
+      const uint32_t lo = (i < rows_here && ra < a.r_cat) ? bl[i * a.r_cat + ra] : 0u;
+      const uint32_t hi = (i < rows_here && ra + 1 < a.r_cat) ? bl[i * a.r_cat + ra + 1] : 0u;
+      w[e] = lo | (hi << 16);
+    }
+    acc = mfma_16x16x32(u32x4_t{w[0], w[1], w[2], w[3]}, tl[k * 64 + lane], acc);
+  }
+  if (a.splits > 1) {
+    if (!reduce_parts(acc, a.ypart + (size_t)tile * a.splits * 256, a.splits, rng, &a.ycount[tile], tag, err,
+                      lane))
+      return;
   }
 
   // lane holds Y^T[row0 + 4g + e][token i]
@@ -345,48 +479,6 @@ void fwd_small_kernel(SmallFwdArgs a) {
       if (n < a.N) a.Y[(size_t)i * a.N + n] = f32_to_bf16(acc[e]);
     }
   }
-  if (talk && lane == 0) finish_launch(epoch, done, a.gdone, blockIdx.x, n_wgs, ngroups);
-}
-
-// ---------------------------------------------------------------------------
-// T pieces for the few-row path: tsum[p][token][rank] = sum over the p-th
-// K range of X[token][k] A_cat[rank][k], fp32, for 16 tokens (rows past M
-// are zero) and all r_pad ranks (ranks past r_cat are zero).  One workgroup
-// per (16-rank tile, K range); its 8 waves split the range and add up in
-// LDS.
-// ---------------------------------------------------------------------------
-constexpr int kTWaves = 8;
-constexpr int kTMaxSteps = 8;  // 32-column steps per wave (K range <= 2048)
-
-__global__ __launch_bounds__(kTWaves * 64) void lowrank_t_small_kernel(SmallTArgs a) {
-  __shared__ f32x4_t red[(kTWaves - 1) * 64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int i = lane & 15, g = lane >> 4;
-  const int j = blockIdx.x, p = blockIdx.y;
-  const int k0 = p * a.k_range, k1 = min(a.K, k0 + a.k_range);
-  const int nsteps = (k1 - k0 + 31) / 32;
-  const int spw = (nsteps + kTWaves - 1) / kTWaves;
-  const int rank = 16 * j + i;
-  u32x4_t av[kTMaxSteps], xv[kTMaxSteps];
-#pragma unroll
-  for (int q = 0; q < kTMaxSteps; ++q) {
-    const int st = wave * spw + q;
-    const int col = k0 + 32 * st + 8 * g;
-    const bool ok = q < spw && st < nsteps && col < k1;
-    av[q] = (ok && rank < a.r_cat) ? load16(a.a_cat + (size_t)rank * a.K + col) : zero_u4();
-    xv[q] = (ok && i < a.M) ? load16(a.X + (size_t)i * a.K + col) : zero_u4();
-  }
-  f32x4_t acc = zero4();
-#pragma unroll
-  for (int q = 0; q < kTMaxSteps; ++q) acc = mfma_16x16x32(av[q], xv[q], acc);
-  if (wave > 0) red[(wave - 1) * 64 + lane] = acc;
-  __syncthreads();
-  if (wave > 0) return;
-#pragma unroll
-  for (int w = 0; w < kTWaves - 1; ++w) acc += red[w * 64 + lane];
-  // lane holds T^T[rank 16j + 4g + e][token i]
-  float* dst = a.tsum + ((size_t)p * 16 + i) * a.r_pad + 16 * j + 4 * g;
-  *reinterpret_cast<f32x4_t*>(dst) = acc;
 }
 
 }  // namespace
@@ -405,11 +497,6 @@ hipError_t launch_fwd_small(const SmallFwdArgs& a, hipStream_t s) {
   const int grid = a.n_tiles * a.splits;
   hipLaunchKernelGGL(fwd_small_kernel, dim3(grid), dim3(kThreads), fwd_small_lds_bytes(a.vcap, a.tl_bytes, a.bl_bytes),
                      s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_lowrank_t_small(const SmallTArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(lowrank_t_small_kernel, dim3(a.r_tiles, a.t_pieces), dim3(kTWaves * 64), 0, s, a);
   return hipGetLastError();
 }
 

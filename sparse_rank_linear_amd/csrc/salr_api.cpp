@@ -37,15 +37,15 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 // first, at the same offsets for every layer shape and every M, so one
 // workspace can serve many layers; every completed call leaves all counters
 // at zero.  Scratch regions follow and are written before they are read.
-constexpr size_t kCounterSync = 0;                       // 4 words
-constexpr size_t kCounterT = 16;                         // 16 words (few-row T tiles)
+constexpr size_t kCounterSync = 0;                       // [8, 12): the error word
+constexpr size_t kCounterT = 16;                         // 16 words (few-row T rank tiles)
 constexpr size_t kCounterM = kCounterT + 16 * 4;         // 256 words (T token blocks)
 constexpr size_t kCounterY = kCounterM + 256 * 4;        // 65536 words (row tiles)
 constexpr int64_t kMaxRowTiles = 65536;
-constexpr size_t kCounterG = kCounterY + kMaxRowTiles * 4;  // 2048 words (completion groups)
-constexpr int kMaxDoneGroups = 2048;
+constexpr size_t kCounterTickets = 384 * 1024;             // launch-tag ticket words
 constexpr size_t kHeaderBytes = 512 * 1024;
-static_assert(kCounterG + kMaxDoneGroups * 4 <= kHeaderBytes, "counter header overflow");
+static_assert(kCounterY + kMaxRowTiles * 4 <= kCounterTickets, "counter header overflow");
+static_assert(kCounterTickets + salr::kTicketGroups * salr::kTicketStride * 8 <= kHeaderBytes, "counter header overflow");
 
 bool dims_ok(int64_t N, int64_t K, int32_t n_keep, int32_t r_cat) {
   if (N < 1 || K < 1 || K > kMaxK || (K % 8) != 0) return false;
@@ -67,30 +67,21 @@ int t_splits_large(int64_t M, int64_t K) {
 
 struct FwdLayout {
   // few-row path
-  int n_tiles, splits, range, vcap, r_tiles, r_pad_small, t_pieces, k_range;
+  int n_tiles, splits, range, vcap, r_tiles, r_pad_small, t_pieces, t_chunks;
   int vals_bytes, tl_bytes, bl_bytes;
   // many-row path
   int64_t m_max;
   int r_pad_large;
   // offsets (bytes)
-  size_t tsum, ypart, T, ltpart, total;
+  size_t tsum, tfinal, ypart, T, ltpart, total;
 };
 
 FwdLayout fwd_layout(int64_t N, int64_t K, int32_t n_keep, int32_t r_cat, int64_t M_max) {
   FwdLayout L{};
   L.n_tiles = (int)cdiv(N, 16);
-  // Few-row T pieces: K ranges of <= 2048 columns; their partial sums are
-  // staged in LDS by the main launch, at most 32 KB of them.
   L.r_tiles = (int)cdiv(r_cat, 16);
   L.r_pad_small = (int)align_up((size_t)std::max(L.r_tiles, 1) * 16, 32);
-  {
-    const int64_t max_pieces = std::max<int64_t>(1, (32 * 1024) / (16 * L.r_pad_small * 4));
-    const int64_t want = std::max<int64_t>(cdiv(K, 2048), std::min<int64_t>(4, cdiv(K, 512)));
-    L.t_pieces = (int)std::min<int64_t>(std::max<int64_t>(want, 1), std::max(max_pieces, cdiv(K, 2048)));
-    L.k_range = (int)align_up((size_t)cdiv(K, L.t_pieces), 32);
-    L.t_pieces = (int)cdiv(K, L.k_range);
-  }
-  L.tl_bytes = r_cat > 0 ? L.t_pieces * 16 * L.r_pad_small * 4 : 0;
+  L.tl_bytes = r_cat > 0 ? (L.r_pad_small / 32) * 1024 : 0;
   L.bl_bytes = r_cat > 0 ? (int)align_up((size_t)16 * r_cat * 2, 16) : 0;
   // Few-row column ranges: whole rows when they fit (no lookup-table round
   // trip), else the widest range that fits; narrower ranges while there are
@@ -112,12 +103,22 @@ FwdLayout fwd_layout(int64_t N, int64_t K, int32_t n_keep, int32_t r_cat, int64_
   L.splits = (int)cdiv(K, L.range);
   L.vcap = vcap_for(L.range);
   L.vals_bytes = (int)salr::fwd_small_vals_bytes(L.vcap);
+  // Few-row T pieces: 16 ranks x t_chunks 1024-column chunks, at most 8
+  // pieces per rank tile (bounds the work of the workgroup that sums them);
+  // workgroups take more than one piece only when there are fewer
+  // workgroups than pieces.
+  {
+    const int64_t chunks = cdiv(K, 1024);
+    L.t_chunks = (int)cdiv(chunks, 8);
+    L.t_pieces = (int)cdiv(chunks, L.t_chunks);
+  }
   L.m_max = std::max<int64_t>(M_max, 0);
   L.r_pad_large = (int)align_up((size_t)r_cat, 16);
 
   size_t off = kHeaderBytes;
-  // few-row path: T partials (fp32) and tagged range partials
-  L.tsum = off;    off = align_up(off + (size_t)L.tl_bytes, 256);
+  // few-row path: tagged T pieces and tagged range partials
+  L.tsum = off;    off = align_up(off + (size_t)L.r_tiles * L.t_pieces * 256 * 8, 256);
+  L.tfinal = off;  off = align_up(off + (size_t)L.r_tiles * 128 * 8, 256);
   L.ypart = off;   off = align_up(off + (L.splits > 1 ? (size_t)L.n_tiles * L.splits * 256 * 8 : 0), 256);
   // many-row path: fp32 split-K partials of T = X A_cat
   L.T = L.ltpart = off;
@@ -243,20 +244,6 @@ int salr_linear_forward(const salr_layer_t* L, const uint16_t* X, int64_t M, uin
 
   hipError_t err;
   if (M <= kSmallM) {
-    if (L->r_cat > 0) {
-      salr::SmallTArgs t{};
-      t.X = X;
-      t.a_cat = L->a_cat;
-      t.tsum = at<float>(ws, W.tsum);
-      t.M = (int32_t)M;
-      t.K = (int32_t)L->K;
-      t.r_cat = L->r_cat;
-      t.r_pad = W.r_pad_small;
-      t.r_tiles = W.r_tiles;
-      t.t_pieces = W.t_pieces;
-      t.k_range = W.k_range;
-      if (salr::launch_lowrank_t_small(t, s) != hipSuccess) return SALR_ERR_HIP;
-    }
     SmallFwdArgs a{};
     a.masks = L->masks;
     a.values = L->values;
@@ -264,7 +251,10 @@ int salr_linear_forward(const salr_layer_t* L, const uint16_t* X, int64_t M, uin
     a.b_cat = L->b_cat;
     a.X = X;
     a.Y = Y;
-    a.tsum = at<float>(ws, W.tsum);
+    a.a_cat = L->a_cat;
+    a.tpiece = at<uint64_t>(ws, W.tsum);
+    a.tfinal = at<uint64_t>(ws, W.tfinal);
+    a.tcount = at<uint32_t>(ws, kCounterT);
     a.N = L->N;
     a.K = (int32_t)L->K;
     a.n_keep = L->n_keep;
@@ -279,18 +269,13 @@ int salr_linear_forward(const salr_layer_t* L, const uint16_t* X, int64_t M, uin
     a.r_tiles = W.r_tiles;
     a.r_pad = W.r_pad_small;
     a.t_pieces = W.t_pieces;
+    a.t_chunks = W.t_chunks;
     a.vals_bytes = W.vals_bytes;
     a.tl_bytes = W.tl_bytes;
     a.bl_bytes = W.bl_bytes;
-    a.sync = at<uint32_t>(ws, kCounterSync);
+    a.tickets = at<uint64_t>(ws, kCounterTickets);
+    a.err = at<uint32_t>(ws, kCounterSync + 8);
     a.ycount = at<uint32_t>(ws, kCounterY);
-    a.gdone = at<uint32_t>(ws, kCounterG);
-    {
-      const int64_t n_wgs = (int64_t)W.n_tiles * W.splits;
-      int64_t groups = 1;
-      while (groups * groups < n_wgs) ++groups;
-      a.done_groups = (int32_t)std::min<int64_t>(groups, kMaxDoneGroups);
-    }
     a.ypart = at<uint64_t>(ws, W.ypart);
     err = salr::launch_fwd_small(a, s);
   } else {

@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "salr_kernels.hpp"
+
 namespace salr {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -109,13 +111,25 @@ __device__ __forceinline__ u32x4_t expand_byte(const uint16_t* vals, uint32_t id
 // stores become visible in.  Counters (device-coherent atomics) only elect
 // which workgroup performs a reduction; they order nothing.
 //
-// The launch tag is epoch+1, where epoch lives in the workspace and is
-// advanced by the last workgroup of each launch (a "done" counter elects
-// it), after every workgroup of that launch has read it.
+// The tag comes from kTicketGroups 64-bit ticket words {count (low half),
+// epoch (high half)} in the workspace, one per group of workgroups (wg mod
+// kTicketGroups), each in its own 256-byte slot so that draws on different
+// words do not queue behind each other.  Every workgroup adds 1 to its
+// group's word as it starts; its tag is the returned epoch + 1.  The
+// workgroup that draws its group's last ticket folds the count into an epoch
+// increment, and workgroup 0 advances the words of groups that have no
+// members in this launch, so every word's epoch advances exactly once per
+// launch and all groups agree on the tag; the next launch (stream-ordered
+// after this one) runs with the next tag.  All of this happens while the
+// loads of the launch's start are in flight; nothing is left to do when
+// workgroups finish.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kSpinLimit = 1u << 22;
 
 __device__ __forceinline__ uint32_t atomic_add_relaxed(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t atomic_add_relaxed64(uint64_t* p, uint64_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t load_coherent(const uint32_t* p) {
@@ -154,20 +168,20 @@ __device__ __forceinline__ void poll_tagged(const uint64_t* p, uint32_t tag, uin
   }
 }
 
-// Called once per workgroup, by one lane, as the workgroup's last action:
-// the workgroup that completes the launch advances the epoch.  Device-scope
-// atomics on one address serialise (about 11 ns each on MI355X), so the
-// workgroups count in ngroups interleaved groups first and only each
-// group's last finisher touches the launch-wide counter.
-__device__ __forceinline__ void finish_launch(uint32_t* epoch, uint32_t* done, uint32_t* gdone, uint32_t wg,
-                                              uint32_t n_wgs, uint32_t ngroups) {
-  const uint32_t g = wg % ngroups;
-  const uint32_t gsize = n_wgs / ngroups + (g < n_wgs % ngroups ? 1u : 0u);
-  if (atomic_add_relaxed(&gdone[g], 1u) != gsize - 1) return;
-  store_coherent(&gdone[g], 0u);
-  if (atomic_add_relaxed(done, 1u) != ngroups - 1) return;
-  store_coherent(done, 0u);
-  store_coherent(epoch, load_coherent(epoch) + 1u);
+// Draw workgroup wg's ticket (one lane; see above).
+__device__ __forceinline__ uint64_t draw_ticket(uint64_t* tickets, uint32_t wg, uint32_t n_wgs) {
+  if (wg == 0)
+    for (uint32_t g = n_wgs; g < kTicketGroups; ++g)
+      atomic_add_relaxed64(tickets + g * kTicketStride, uint64_t(1) << 32);
+  return atomic_add_relaxed64(tickets + (wg % kTicketGroups) * kTicketStride, 1);
+}
+// The launch tag from a drawn ticket; the drawer of its group's last ticket
+// also advances the group's epoch.  The lane that drew calls this.
+__device__ __forceinline__ uint32_t tag_from_ticket(uint64_t* tickets, uint64_t drawn, uint32_t wg, uint32_t n_wgs) {
+  const uint32_t g = wg % kTicketGroups;
+  const uint32_t gsize = n_wgs / kTicketGroups + (g < n_wgs % kTicketGroups ? 1u : 0u);
+  if ((uint32_t)drawn == gsize - 1u) atomic_add_relaxed64(tickets + g * kTicketStride, (uint64_t(1) << 32) - gsize);
+  return (uint32_t)(drawn >> 32) + 1u;
 }
 
 __device__ __forceinline__ u32x4_t load16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }

@@ -7,6 +7,9 @@
 namespace salr {
 
 constexpr int kMaxRangeCols = 4096;  // columns per few-row workgroup
+// Launch-tag ticket words in the forward workspace (see salr_device.hpp).
+constexpr uint32_t kTicketGroups = 16;
+constexpr uint32_t kTicketStride = 32;  // uint64 words between ticket words
 
 // ----------------------------------------------------------------------------
 // Forward, M <= 16: one fused launch.  Each workgroup decodes 16 rows x one
@@ -21,7 +24,10 @@ struct SmallFwdArgs {
   const uint16_t* b_cat;   // [N][r_cat] (+ tail padding)
   const uint16_t* X;       // [M][K]
   uint16_t* Y;             // [M][N]
-  const float* tsum;       // [t_pieces][16][r_pad] partial T (when r_cat > 0)
+  const uint16_t* a_cat;   // [r_cat][K]
+  uint64_t* tpiece;        // [r_tiles * t_pieces][256] tagged fp32 pieces of T
+  uint64_t* tfinal;        // [r_tiles][128] tagged bf16 pairs: T per rank tile
+  uint32_t* tcount;        // [r_tiles] pieces published per rank tile
   int64_t N;
   int32_t K, n_keep, r_cat, M;
   int32_t kw, ng;          // words / lookup entries per row
@@ -30,14 +36,14 @@ struct SmallFwdArgs {
   int32_t range;           // columns per range (K when splits == 1, else 1024/2048/4096)
   int32_t vcap;            // 16-byte chunks of LDS per row
   int32_t r_tiles;         // ceil(r_cat/16)
-  int32_t r_pad;           // rank stride of tsum (multiple of 32)
-  int32_t t_pieces;        // K ranges of tsum
+  int32_t r_pad;           // ranks of T rounded up to a multiple of 32
+  int32_t t_pieces;        // K ranges of T pieces, t_chunks * 1024 columns each
+  int32_t t_chunks;
   int32_t vals_bytes;      // LDS bytes of the values area
-  int32_t tl_bytes;        // LDS bytes of the T partials (t_pieces * 16 * r_pad * 4)
+  int32_t tl_bytes;        // LDS bytes of the T operands (r_pad / 32 chunks x 1 KB)
   int32_t bl_bytes;        // LDS bytes of the B_cat rows (16 * r_cat * 2, rounded up to 16)
-  int32_t done_groups;     // groups of the two-level completion count
-  uint32_t* sync;          // [0] epoch, [1] finished groups, [2] error
-  uint32_t* gdone;         // [done_groups] finished workgroups per group
+  uint64_t* tickets;       // {count, epoch} ticket words of the launch tags
+  uint32_t* err;           // set nonzero when a wait times out
   uint32_t* ycount;        // [n_tiles]
   uint64_t* ypart;         // [n_tiles][splits][256] tagged fp32
 };
@@ -52,16 +58,6 @@ inline int fwd_small_vcap(int64_t cap) {
   const int v = (int)((cap + 16) / 8 + 2);
   return v + ((1 - v % 8) + 8) % 8;
 }
-
-// T = X * A_cat for M <= 16, as t_pieces partial sums over K ranges.
-struct SmallTArgs {
-  const uint16_t* X;       // [M][K]
-  const uint16_t* a_cat;   // [r_cat][K]
-  float* tsum;             // [t_pieces][16][r_pad]
-  int32_t M, K, r_cat, r_pad, r_tiles;
-  int32_t t_pieces, k_range;  // K ranges (k_range columns each, <= 2048)
-};
-hipError_t launch_lowrank_t_small(const SmallTArgs& a, hipStream_t s);
 
 // ----------------------------------------------------------------------------
 // Forward, M > 16: T = X * A_cat (bf16, [M][r_pad]) then the tiled

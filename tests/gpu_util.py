@@ -47,3 +47,10 @@ def errors(Y_gpu_bits, Y_ref):
     nrm = float(np.linalg.norm(Y_ref))
     nw = float(np.linalg.norm(Yg - Y_ref) / nrm) if nrm > 0 else float(np.linalg.norm(Yg))
     return mr, nw
+
+
+def wait_error(ws) -> int:
+    """The forward workspace's wait-timeout word (uint32 at byte offset 8)."""
+    import torch
+
+    return int(ws[8:12].cpu().view(torch.int32).item())

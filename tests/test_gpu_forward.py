@@ -11,7 +11,7 @@ import pytest
 from oracle import bf16 as ob
 from oracle import salr as osl
 from sparse_rank_linear_amd import synth
-from tests.gpu_util import TOL_MAX_REL, TOL_NORMWISE, errors, say, to_dev, to_host_bits, upload_encoded
+from tests.gpu_util import TOL_MAX_REL, TOL_NORMWISE, errors, say, to_dev, to_host_bits, upload_encoded, wait_error
 
 pytestmark = pytest.mark.gpu
 
@@ -24,6 +24,9 @@ CASES = [
     (40, 1032, 0, 0, (8,), (3, 70)),
     (1, 64, 17, 1, (), (1, 30)),
     (200, 3072, 1536, 8, (4, 4, 4), (7, 16, 130)),
+    (64, 9216, 4608, 8, (32,), (1, 16, 20)),      # T pieces of 2048 columns, ranges
+    (16, 1024, 512, 0, (200,), (4, 16)),          # one workgroup computes 13 T pieces
+    (30, 64, 32, 0, (256,), (16,)),               # the largest r_cat, tiny K
 ]
 
 
@@ -63,6 +66,7 @@ def test_forward_matches_oracle(case, shared_ws):
         Yref = osl.forward(X, enc.masks, enc.values, K, enc.A_cat, enc.B_cat)
         mr, nw = errors(to_host_bits(Y), Yref)
         say(f"  max_rel={mr:.3e} normwise={nw:.3e}")
+        assert wait_error(shared_ws) == 0
         assert mr <= TOL_MAX_REL and nw <= TOL_NORMWISE
 
 
