@@ -44,6 +44,34 @@ METRIC = "SALR linear fwd TFLOP/s (dense-equiv) + compressed-weight GB/s, % of M
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2516.6
 COPIES = 32
+# Sources that decide what the few-row forward kernel does and how it is
+# launched; a stored counter measurement counts only while they are unchanged.
+FWD_SMALL_SOURCES = ("fwd_small.hip", "salr_device.hpp", "salr_kernels.hpp", "salr_api.cpp")
+PROFILE_JSON = os.path.join(ROOT, "profiles", "fwd_small_llama7b_attn_4096x4096_decode.json")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in FWD_SMALL_SOURCES:
+        with open(os.path.join(ROOT, "sparse_rank_linear_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter runs (FETCH_SIZE and
+    WRITE_SIZE, scaled by a plain copy's readings), or None when the kernel
+    sources changed since they were taken."""
+    try:
+        with open(PROFILE_JSON) as f:
+            prof = json.load(f)
+    except OSError:
+        return None
+    if prof.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return int(prof["traffic_bytes_per_launch"])
 
 
 def _dev_bits(a, dev):
@@ -203,7 +231,7 @@ def main():
         "tflops_effective": round(2 * M * (wl.N * wl.n_keep + wl.r_cat * (wl.K + wl.N)) / t / 1e12, 4),
         "roofline": {"bound": "hbm", "kernel": "fwd_small_kernel", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic()},
         "encode": {"seconds": round(encode_s, 4), "iters": 24, "oversample": 32},
     }
     if not args.no_extra:
