@@ -27,12 +27,12 @@
 //   * range partials of one row tile are combined by the last workgroup to
 //     finish, in range order (results do not depend on scheduling);
 //   * T = X A_cat is cut into pieces of 16 ranks x (a multiple of 1024)
-//     columns.  The first workgroups each compute one piece as soon as their
-//     own data has landed (its operands are fetched with the weights) and
-//     publish it; after its decode every workgroup gathers the pieces of its
-//     share of the ranks, summing them in a fixed order into LDS, and adds
-//     T B_cat for those ranks (B_cat rows fetched with the weights) as extra
-//     matrix-core steps.  With whole rows a workgroup takes all ranks; with
+//     columns.  Extra workgroups at the front of the grid each compute one
+//     piece and nothing else, so T is complete long before any weight tile
+//     needs it; the last producer of a rank tile sums its pieces in a fixed
+//     order.  After its decode every weight workgroup reads T for its share
+//     of the ranks and adds T B_cat for those ranks (B_cat rows fetched with
+//     the weights) as extra matrix-core steps.  With whole rows a workgroup takes all ranks; with
 //     ranges, range r takes the 32-rank chunks r, r + ranges, ..., so the
 //     low-rank work and its gather traffic are spread over the ranges;
 //   * pieces and range partials handed between workgroups travel as tagged
@@ -55,23 +55,30 @@ constexpr int kPollBatch = 8;
 constexpr int kBatch = 4;  // decode steps whose LDS reads are issued together
 
 // LDS carve-up (dynamic shared memory): a fixed part, then the values area.
-struct Lds {
+struct alignas(16) Lds {
   u32x2_t lut[16];
   uint32_t seg[kRows][2];  // per-row range of kept-value indices (within the row)
   int64_t vorg[kRows];     // global value index = LDS value slot + vorg (per row)
   uint64_t masks[kRows * kMaskRowWords];
-  f32x4_t pred[3 * 64];  // wave sums of a T piece (waves 1-3)
   uint32_t tag;
 };
-constexpr int kPieceWaves = 4;                         // waves computing a T piece
-constexpr int kPieceSteps = 1024 / 32 / kPieceWaves;  // their steps per 1024-column chunk
-constexpr int kFinBatch = 4;                           // pieces requested together when finishing T
-constexpr int kMaxLoadRows = kRows / (kWaves - kPieceWaves);  // rows per load-issuing wave
+constexpr int kPieceSteps = 1024 / 32 / kWaves;  // steps per wave of a T piece's 1024-column chunk
+constexpr int kFinBatch = 4;                      // pieces requested together when finishing T
+constexpr int kMaxLoadRows = kRows / kWaves;      // rows per load-issuing wave
 static_assert(sizeof(Lds) % 16 == 0, "values area must stay 16-byte aligned");
 
 __device__ __forceinline__ u32x4_t load_x_frag(const uint16_t* X, int M, int K, int m, int col) {
   if (m < M && col < K) return load16(X + (size_t)m * K + col);
   return zero_u4();
+}
+
+// Workgroup barrier that waits for the wave's LDS operations but not for its
+// outstanding global ones (__syncthreads waits for both).
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // Sum the waves' accumulators into wave 0 (fixed order).  Other waves return
@@ -145,7 +152,7 @@ __device__ __forceinline__ void copy_chunks_to_lds(const uint32_t* src, uint32_t
   }
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void fwd_small_kernel(SmallFwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   Lds& L = *reinterpret_cast<Lds*>(smem);
@@ -176,8 +183,12 @@ void fwd_small_kernel(SmallFwdArgs a) {
   };
   f32x4_t acc = zero4();
 
-  // ---------------- this workgroup's weights: 16 rows x one column range
-  const int c = blockIdx.x;
+  // ---------------- this workgroup's role: the first n_pieces workgroups
+  // compute T pieces and nothing else; the rest own 16 W rows x one column
+  // range
+  const int n_pieces = a.r_tiles * a.t_pieces;
+  const bool producer = (int)blockIdx.x < n_pieces;
+  const int c = producer ? (int)blockIdx.x : (int)blockIdx.x - n_pieces;
   const int tile = c / a.splits, rng = c % a.splits;
   const int64_t row0 = (int64_t)tile * kRows;
   const int col0 = rng * a.range;
@@ -188,11 +199,6 @@ void fwd_small_kernel(SmallFwdArgs a) {
   const int s0 = wave * spw;
   const int nwords = (ncols + 63) / 64;            // bitmap words in the range
   const int rows_here = (int)min<int64_t>(kRows, a.N - row0);
-  const int n_pieces = a.r_tiles * a.t_pieces;
-  const bool producer = c < n_pieces;
-  // In a workgroup that computes T pieces, waves 0-3 do that while waves 4-7
-  // issue every weight load; elsewhere all waves issue them.
-  const int lw0 = producer ? kPieceWaves : 0;
 
   u32x4_t xf[kMaxSteps];
   const auto load_x_frags = [&]() {
@@ -201,10 +207,10 @@ void fwd_small_kernel(SmallFwdArgs a) {
       xf[q] = (q < spw) ? load_x_frag(a.X, a.M, a.K, i, col0 + 32 * (s0 + q) + 8 * g) : zero_u4();
   };
 
-  if (wave >= lw0) load_x_frags();
-  if (tid < 16) L.lut[tid] = nibble_selectors(tid);
-  if (wave >= lw0) {
-    const int lw = wave - lw0, lws = kWaves - lw0;
+  if (!producer) {
+    load_x_frags();
+    if (tid < 16) L.lut[tid] = nibble_selectors(tid);
+    const int lw = wave, lws = kWaves;
     // Bitmap words of the range, per row 2*nwords dwords direct to LDS; rows
     // past N read as zero.
     for (int r = lw; r < kRows; r += lws) {
@@ -258,109 +264,89 @@ void fwd_small_kernel(SmallFwdArgs a) {
     }
   }
 
-  // ---------------- T pieces (producer workgroups, waves 0-3)
+  // ---------------- T pieces (producer workgroups)
   // Piece p = (rank tile j, K range kp) is T^T[16 ranks][16 tokens] summed
-  // over t_chunks * 1024 columns; workgroup c takes pieces c, c + n_wgs, ...
-  // Wave 0 publishes each piece as tagged words (lane (i, g) holds ranks
-  // 16j + 4g + e of token i) and counts it; the workgroup that completes a
-  // rank tile's count sums the tile's pieces in K order and publishes T for
-  // the tile as bf16 pairs.  Every workgroup waits on nothing before its
-  // pieces are published, so no wait here can depend on a later one.
+  // over t_chunks * 1024 columns; producer workgroup p computes piece p with
+  // all its waves (partials summed in LDS in wave order).  Wave 0 publishes
+  // it as tagged words (lane (i, g) holds ranks 16j + 4g + e of token i) and
+  // counts it; the producer that completes a rank tile's count sums the
+  // tile's pieces in K order and publishes T for the tile as bf16 pairs.
+  // Producers wait on nothing but each other's pieces, which are published
+  // before any wait, and carry no weights, so T is ready early and no weight
+  // tile is held up by it.
   if (producer) {
-    uint32_t elected = 0;  // rank tiles this workgroup completes (bit j)
-    for (int piece = c; piece < n_pieces; piece += (int)n_wgs) {
-      const int j = piece / a.t_pieces, kp = piece % a.t_pieces;
-      f32x4_t t = zero4();
-      if (wave < kPieceWaves) {
-        const int rank = 16 * j + i;
-        for (int ch = 0; ch < a.t_chunks; ++ch) {
-          u32x4_t pav[kPieceSteps], pxv[kPieceSteps];
+    const int piece = c;
+    const int j = piece / a.t_pieces, kp = piece % a.t_pieces;
+    const int rank = 16 * j + i;
+    f32x4_t t = zero4();
+    for (int ch = 0; ch < a.t_chunks; ++ch) {
+      u32x4_t pav[kPieceSteps], pxv[kPieceSteps];
 #pragma unroll
-          for (int q = 0; q < kPieceSteps; ++q) {
-            const int col = (kp * a.t_chunks + ch) * 1024 + 32 * (wave * kPieceSteps + q) + 8 * g;
-            pav[q] = (rank < a.r_cat && col < a.K) ? load16(a.a_cat + (size_t)rank * a.K + col) : zero_u4();
-            pxv[q] = load_x_frag(a.X, a.M, a.K, i, col);
+      for (int q = 0; q < kPieceSteps; ++q) {
+        const int col = (kp * a.t_chunks + ch) * 1024 + 32 * (wave * kPieceSteps + q) + 8 * g;
+        pav[q] = (rank < a.r_cat && col < a.K) ? load16(a.a_cat + (size_t)rank * a.K + col) : zero_u4();
+        pxv[q] = load_x_frag(a.X, a.M, a.K, i, col);
+      }
+#pragma unroll
+      for (int q = 0; q < kPieceSteps; ++q) t = mfma_16x16x32(pav[q], pxv[q], t);
+    }
+    if (!reduce_waves(t, red, wave, lane)) return;
+    resolve_tag();
+    uint64_t* dst = a.tpiece + ((size_t)piece * 64 + lane) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v = t[e];  // (scalar copy first: see reduce_parts)
+      store_tagged(dst + e, __float_as_uint(v), tag);
+    }
+    uint32_t old = 0;
+    if (lane == 0) old = atomic_add_relaxed(&a.tcount[j], 1u);
+    old = __shfl(old, 0);
+    if (old != (uint32_t)(a.t_pieces - 1)) return;
+    if (lane == 0) store_coherent(&a.tcount[j], 0u);
+    float sum[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int kp0 = 0; kp0 < a.t_pieces; kp0 += kFinBatch) {
+      uint64_t v[kFinBatch][4];
+#pragma unroll
+      for (int b = 0; b < kFinBatch; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[b][e] = (kp0 + b < a.t_pieces)
+                        ? load_tagged_raw(a.tpiece + ((size_t)(j * a.t_pieces + kp0 + b) * 64 + lane) * 4 + e)
+                        : 0ull;
+#pragma unroll
+      for (int b = 0; b < kFinBatch; ++b) {
+        if (kp0 + b < a.t_pieces) {
+          bool ok = true;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ok &= (uint32_t)(v[b][e] >> 32) == tag;
+          uint32_t w[4];
+          if (ok) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = (uint32_t)v[b][e];
+          } else {
+            poll_tagged<4>(a.tpiece + ((size_t)(j * a.t_pieces + kp0 + b) * 64 + lane) * 4, tag, w, err);
           }
 #pragma unroll
-          for (int q = 0; q < kPieceSteps; ++q) t = mfma_16x16x32(pav[q], pxv[q], t);
+          for (int e = 0; e < 4; ++e) sum[e] += __uint_as_float(w[e]);
         }
-        if (wave > 0) L.pred[(wave - 1) * 64 + lane] = t;
-      }
-      __syncthreads();
-      if (wave == 0) {
-        if (!resolved) resolve_tag();
-#pragma unroll
-        for (int w = 0; w < kPieceWaves - 1; ++w) t += L.pred[w * 64 + lane];
-        uint64_t* dst = a.tpiece + ((size_t)piece * 64 + lane) * 4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float v = t[e];  // (scalar copy first: see reduce_parts)
-          store_tagged(dst + e, __float_as_uint(v), tag);
-        }
-      }
-      __syncthreads();
-    }
-    if (wave == 0) {
-      for (int piece = c; piece < n_pieces; piece += (int)n_wgs) {
-        const int j = piece / a.t_pieces;
-        uint32_t old = 0;
-        if (lane == 0) old = atomic_add_relaxed(&a.tcount[j], 1u);
-        old = __shfl(old, 0);
-        if (old == (uint32_t)(a.t_pieces - 1)) elected |= 1u << j;
-      }
-      while (elected) {
-        const int j = __builtin_ctz(elected);
-        elected &= elected - 1;
-        if (lane == 0) store_coherent(&a.tcount[j], 0u);
-        float sum[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int kp0 = 0; kp0 < a.t_pieces; kp0 += kFinBatch) {
-          uint64_t v[kFinBatch][4];
-#pragma unroll
-          for (int b = 0; b < kFinBatch; ++b)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              v[b][e] = (kp0 + b < a.t_pieces)
-                            ? load_tagged_raw(a.tpiece + ((size_t)(j * a.t_pieces + kp0 + b) * 64 + lane) * 4 + e)
-                            : 0ull;
-#pragma unroll
-          for (int b = 0; b < kFinBatch; ++b) {
-            if (kp0 + b < a.t_pieces) {
-              bool ok = true;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) ok &= (uint32_t)(v[b][e] >> 32) == tag;
-              uint32_t w[4];
-              if (ok) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) w[e] = (uint32_t)v[b][e];
-              } else {
-                poll_tagged<4>(a.tpiece + ((size_t)(j * a.t_pieces + kp0 + b) * 64 + lane) * 4, tag, w, err);
-              }
-#pragma unroll
-              for (int e = 0; e < 4; ++e) sum[e] += __uint_as_float(w[e]);
-            }
-          }
-        }
-        uint64_t* dst = a.tfinal + ((size_t)j * 64 + lane) * 2;
-        store_tagged(dst, (uint32_t)f32_to_bf16(sum[0]) | ((uint32_t)f32_to_bf16(sum[1]) << 16), tag);
-        store_tagged(dst + 1, (uint32_t)f32_to_bf16(sum[2]) | ((uint32_t)f32_to_bf16(sum[3]) << 16), tag);
       }
     }
+    uint64_t* fin = a.tfinal + ((size_t)j * 64 + lane) * 2;
+    store_tagged(fin, (uint32_t)f32_to_bf16(sum[0]) | ((uint32_t)f32_to_bf16(sum[1]) << 16), tag);
+    store_tagged(fin + 1, (uint32_t)f32_to_bf16(sum[2]) | ((uint32_t)f32_to_bf16(sum[3]) << 16), tag);
+    return;
   }
-
-  // X operand slices of this wave's steps (piece waves: after the piece).
-  if (wave < lw0) load_x_frags();
 
   __builtin_amdgcn_s_waitcnt(0);
   if (talk && wave == 0) {
     if (!resolved) resolve_tag();
     if (lane == 0) L.tag = tag;
   }
-  __syncthreads();
+  lds_barrier();  // (the tag's epoch update, if any, need not complete)
   if (talk) tag = L.tag;
 
   // This workgroup's share of the low-rank term: the 32-rank chunks rng,
-  // rng + splits, ...; wave k requests chunk k's T operand now and checks it
-  // after the decode.  Lane (i, g) needs T[token i][32q + 8g .. +7]: tile
+  // rng + splits, ...; wave k reads chunk k's T operand after the decode.  Lane (i, g) needs T[token i][32q + 8g .. +7]: tile
   // 2q + g/2, i.e. the words of lanes i + 16 g' (g' = 2(g % 2), +1) there.
   const int n_chunks = a.r_pad / 32;
   const int n_own = a.r_cat > 0 && rng < n_chunks ? (n_chunks - rng + a.splits - 1) / a.splits : 0;
@@ -368,13 +354,6 @@ void fwd_small_kernel(SmallFwdArgs a) {
   const int tj = 2 * my_chunk + (g >> 1);
   const bool t_live = wave < n_own && tj < a.r_tiles;
   const uint64_t* tsrc = a.tfinal + ((size_t)tj * 64 + i + 32 * (g & 1)) * 2;
-  uint64_t tw[4] = {0ull, 0ull, 0ull, 0ull};
-  if (t_live) {
-    tw[0] = load_tagged_raw(tsrc);
-    tw[1] = load_tagged_raw(tsrc + 1);
-    tw[2] = load_tagged_raw(tsrc + 32);
-    tw[3] = load_tagged_raw(tsrc + 33);
-  }
 
   // Decode + multiply this wave's steps.  The wave's bitmap words come to
   // registers first; then each batch of kBatch steps issues all its LDS
@@ -389,7 +368,13 @@ void fwd_small_kernel(SmallFwdArgs a) {
     const uint32_t base = live ? (uint32_t)((row0 + i) * a.n_keep + L.seg[i][0] - L.vorg[i]) : 0u;
     const int w0 = s0 >> 1;
     uint32_t part = 0;
-    for (int w = g; w < w0; w += 4) part += __popcll(mrow[w]);
+    // (all reads issued together: clamped in-row indices, masked counts)
+#pragma unroll
+    for (int k = 0; k < (kMaskRowWords - 1) / 4; ++k) {
+      const int w = g + 4 * k;
+      const uint64_t m = mrow[min(w, kMaskRowWords - 1)];
+      part += w < w0 ? (uint32_t)__popcll(m) : 0u;
+    }
     part += __shfl_xor(part, 16);
     part += __shfl_xor(part, 32);
     uint64_t mw[kMaxWaveWords];
@@ -430,7 +415,16 @@ void fwd_small_kernel(SmallFwdArgs a) {
     }
   }
 
-  // The T operand of this wave's chunk, into LDS for the epilogue.
+  // The T operand of this wave's chunk, into LDS for the epilogue (read
+  // only now: held across the decode its registers would not fit two
+  // workgroups per CU).
+  uint64_t tw[4] = {0ull, 0ull, 0ull, 0ull};
+  if (t_live) {
+    tw[0] = load_tagged_raw(tsrc);
+    tw[1] = load_tagged_raw(tsrc + 1);
+    tw[2] = load_tagged_raw(tsrc + 32);
+    tw[3] = load_tagged_raw(tsrc + 33);
+  }
   if (wave < n_own) {
     uint32_t d[4] = {0u, 0u, 0u, 0u};
     if (t_live) {
@@ -455,15 +449,22 @@ void fwd_small_kernel(SmallFwdArgs a) {
   // T^T[chunk, :], as extra K steps (T already rounded to bf16).
   for (int k = 0; k < n_own; ++k) {
     const int rb = 32 * (rng + k * a.splits) + 8 * g;
-    uint32_t w[4];
+    u32x4_t wv;
+    if (a.r_cat % 8 == 0) {
+      // eight ranks in one aligned 16-byte read (ranks past r_cat: zero)
+      wv = (i < rows_here && rb < a.r_cat) ? *reinterpret_cast<const u32x4_t*>(bl + i * a.r_cat + rb) : zero_u4();
+    } else {
+      uint32_t w[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int ra = rb + 2 * e;
-      const uint32_t lo = (i < rows_here && ra < a.r_cat) ? bl[i * a.r_cat + ra] : 0u;
-      const uint32_t hi = (i < rows_here && ra + 1 < a.r_cat) ? bl[i * a.r_cat + ra + 1] : 0u;
-      w[e] = lo | (hi << 16);
+      for (int e = 0; e < 4; ++e) {
+        const int ra = rb + 2 * e;
+        const uint32_t lo = (i < rows_here && ra < a.r_cat) ? bl[i * a.r_cat + ra] : 0u;
+        const uint32_t hi = (i < rows_here && ra + 1 < a.r_cat) ? bl[i * a.r_cat + ra + 1] : 0u;
+        w[e] = lo | (hi << 16);
+      }
+      wv = u32x4_t{w[0], w[1], w[2], w[3]};
     }
-    acc = mfma_16x16x32(u32x4_t{w[0], w[1], w[2], w[3]}, tl[k * 64 + lane], acc);
+    acc = mfma_16x16x32(wv, tl[k * 64 + lane], acc);
   }
   if (a.splits > 1) {
     if (!reduce_parts(acc, a.ypart + (size_t)tile * a.splits * 256, a.splits, rng, &a.ycount[tile], tag, err,
@@ -494,7 +495,7 @@ size_t fwd_small_lds_bytes(int vcap, int tl_bytes, int bl_bytes) {
 }
 
 hipError_t launch_fwd_small(const SmallFwdArgs& a, hipStream_t s) {
-  const int grid = a.n_tiles * a.splits;
+  const int grid = a.n_tiles * a.splits + a.r_tiles * a.t_pieces;
   hipLaunchKernelGGL(fwd_small_kernel, dim3(grid), dim3(kThreads), fwd_small_lds_bytes(a.vcap, a.tl_bytes, a.bl_bytes),
                      s, a);
   return hipGetLastError();

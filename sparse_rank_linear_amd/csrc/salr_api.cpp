@@ -86,7 +86,10 @@ FwdLayout fwd_layout(int64_t N, int64_t K, int32_t n_keep, int32_t r_cat, int64_
   // Few-row column ranges: whole rows when they fit (no lookup-table round
   // trip), else the widest range that fits; narrower ranges while there are
   // too few workgroups to occupy the GPU.
-  const auto vcap_for = [&](int64_t range) { return salr::fwd_small_vcap(std::min<int64_t>(range, n_keep)); };
+  // (whole rows start on a chunk when n_keep is a multiple of 8)
+  const auto vcap_for = [&](int64_t range) {
+    return salr::fwd_small_vcap(std::min<int64_t>(range, n_keep), range >= K && n_keep % 8 == 0);
+  };
   const auto lds_for = [&](int64_t range) { return salr::fwd_small_lds_bytes(vcap_for(range), L.tl_bytes, L.bl_bytes); };
   L.range = 0;
   if (K <= salr::kMaxRangeCols && lds_for(K) <= kSmallLdsBudget && (L.n_tiles >= kFillWgs || K <= 1024)) {

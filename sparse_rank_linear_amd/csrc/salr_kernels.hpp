@@ -12,10 +12,10 @@ constexpr uint32_t kTicketGroups = 16;
 constexpr uint32_t kTicketStride = 32;  // uint64 words between ticket words
 
 // ----------------------------------------------------------------------------
-// Forward, M <= 16: one fused launch.  Each workgroup decodes 16 rows x one
-// column range of W_s and multiplies; the first workgroups also compute the
-// pieces of T = X * A_cat; range partials and T meet in each row tile's
-// finishing workgroup, which adds the low-rank term.
+// Forward, M <= 16: one fused launch.  Extra workgroups at the front of the
+// grid compute the pieces of T = X * A_cat; every other workgroup decodes 16
+// rows x one column range of W_s, multiplies, and adds its share of the
+// low-rank term; range partials meet in each row tile's finishing workgroup.
 // ----------------------------------------------------------------------------
 struct SmallFwdArgs {
   const uint64_t* masks;
@@ -51,11 +51,14 @@ hipError_t launch_fwd_small(const SmallFwdArgs& a, hipStream_t s);
 size_t fwd_small_vals_bytes(int vcap);
 // Dynamic LDS bytes of one few-row workgroup.
 size_t fwd_small_lds_bytes(int vcap, int tl_bytes, int bl_bytes);
-// LDS chunks per row for rows whose staged values never exceed `cap`: room
-// for the misaligned start and the decode window's overrun, rounded to a
-// stride of 1 mod 8 chunks so consecutive rows start 4 banks apart.
-inline int fwd_small_vcap(int64_t cap) {
-  const int v = (int)((cap + 16) / 8 + 2);
+// LDS chunks per row for rows whose staged values never exceed `cap`.  The
+// first value sits at slot 0..7 of the first chunk (always 0 when
+// `aligned_start`), and a decode window reads at most 5 slots past one past
+// the last value; rounded to a stride of 1 mod 8 chunks so consecutive rows
+// start 4 banks apart.  (Two whole-row workgroups of 4096 columns with a
+// low-rank term fit on one CU only with this tight count.)
+inline int fwd_small_vcap(int64_t cap, bool aligned_start) {
+  const int v = (int)(((aligned_start ? 0 : 7) + cap + 5) / 8 + 1);
   return v + ((1 - v % 8) + 8) % 8;
 }
 

@@ -38,6 +38,7 @@ def shared_ws():
     # protocol across layer shapes and both token regimes
     shapes = [(N, K, nk, rs, rs + sum(lr), max(ms)) for (N, K, nk, rs, lr, ms) in CASES]
     shapes.append((300, 4096, 2048, 16, 32, 100))  # test_forward_deterministic
+    shapes.append((96, 4096, 2048, 8, 32, 16))  # test_forward_clustered_rows
     need = max(srl.query_sizes(*s)["forward_ws_bytes"] for s in shapes)
     return srl.workspace(need)
 
@@ -105,3 +106,32 @@ def test_forward_rejects_small_workspace():
     ws = torch.zeros(1024, dtype=torch.uint8, device="cuda")
     with pytest.raises(srl.SalrError, match="WORKSPACE"):
         srl.linear_forward(layer, X, ws=ws)
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_forward_clustered_rows(M, shared_ws):
+    """Rows whose kept values crowd into one or two 1024-column blocks (very
+    uneven counts per block), mixed with ordinary rows in the same tiles."""
+    import torch
+    import sparse_rank_linear_amd as srl
+
+    N, K, n_keep = 96, 4096, 2048
+    W = ob.bits_to_f64(synth.make_w(N, K, seed=21))
+    W[1::2, :1024] *= 50.0  # odd rows: every value of block 0 outranks the rest
+    W[3::8, 2048:3072] *= 50.0  # some rows: two crowded blocks
+    rng = np.random.default_rng(22)
+    A = ob.f64_to_bits(rng.standard_normal((24, K)).astype(np.float32) * 0.01)
+    B = ob.f64_to_bits(rng.standard_normal((N, 24)).astype(np.float32) * 0.01)
+    enc = osl.encode(ob.f64_to_bits(W), n_keep, 8, [A], [B])
+    per_block = np.array([[bin(int(w)).count("1") for w in row[:16]] for row in enc.masks[:4]]).sum(axis=1)
+    assert per_block[1] >= 900  # block 0 of an odd row is nearly all kept
+    layer = upload_encoded(enc, K, 8)
+    say(f"forward clustered N={N} K={K} M={M}")
+    X = synth.make_x(K, M, seed=23)
+    Y = srl.linear_forward(layer, to_dev(X), ws=shared_ws)
+    torch.cuda.synchronize()
+    Yref = osl.forward(X, enc.masks, enc.values, K, enc.A_cat, enc.B_cat)
+    mr, nw = errors(to_host_bits(Y), Yref)
+    say(f"  max_rel={mr:.3e} normwise={nw:.3e}")
+    assert wait_error(shared_ws) == 0
+    assert mr <= TOL_MAX_REL and nw <= TOL_NORMWISE
