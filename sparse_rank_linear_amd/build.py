@@ -26,6 +26,10 @@ COMMON = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     # no packed-fp32 VALU instructions are generated
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # every atomic here is issued by one lane on purpose; the wave-wide
+    # rewrite of the atomic optimizer would make the wave wait for the result
+    # right after issuing it
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -169,17 +169,15 @@ void fwd_small_kernel(SmallFwdArgs a) {
   const uint32_t n_wgs = gridDim.x;
   const bool talk = a.splits > 1 || a.r_cat > 0;  // any cross-workgroup data?
   uint32_t* const err = a.err;
-  // This launch's tag: the ticket is drawn now and resolved by wave 0 where
-  // first needed (its latency hides behind the loads issued meanwhile).
+  // This launch's tag: a ticket drawn by thread 0 and resolved by wave 0
+  // where first needed (producers: first thing; weight workgroups: after
+  // their decode).
   uint64_t drawn = 0;
-  if (talk && tid == 0) drawn = draw_ticket(a.tickets, blockIdx.x, n_wgs);
   uint32_t tag = 0;
-  bool resolved = false;
   const auto resolve_tag = [&]() {
     uint32_t t = 0;
     if (lane == 0) t = tag_from_ticket(a.tickets, drawn, blockIdx.x, n_wgs);
     tag = __shfl(t, 0);
-    resolved = true;
   };
   f32x4_t acc = zero4();
 
@@ -275,6 +273,7 @@ void fwd_small_kernel(SmallFwdArgs a) {
   // before any wait, and carry no weights, so T is ready early and no weight
   // tile is held up by it.
   if (producer) {
+    if (tid == 0) drawn = draw_ticket(a.tickets, blockIdx.x, n_wgs);
     const int piece = c;
     const int j = piece / a.t_pieces, kp = piece % a.t_pieces;
     const int rank = 16 * j + i;
@@ -337,17 +336,13 @@ void fwd_small_kernel(SmallFwdArgs a) {
     return;
   }
 
-  __builtin_amdgcn_s_waitcnt(0);
-  if (talk && wave == 0) {
-    if (!resolved) resolve_tag();
-    if (lane == 0) L.tag = tag;
-  }
-  lds_barrier();  // (the tag's epoch update, if any, need not complete)
-  if (talk) tag = L.tag;
+  __builtin_amdgcn_s_waitcnt(0);  // every load of this wave has landed
+  lds_barrier();
 
   // This workgroup's share of the low-rank term: the 32-rank chunks rng,
-  // rng + splits, ...; wave k reads chunk k's T operand after the decode.  Lane (i, g) needs T[token i][32q + 8g .. +7]: tile
-  // 2q + g/2, i.e. the words of lanes i + 16 g' (g' = 2(g % 2), +1) there.
+  // rng + splits, ...; wave k reads chunk k's T operand after the decode.
+  // Lane (i, g) needs T[token i][32q + 8g .. +7]: tile 2q + g/2, i.e. the
+  // words of lanes i + 16 g' (g' = 2(g % 2), +1) there.
   const int n_chunks = a.r_pad / 32;
   const int n_own = a.r_cat > 0 && rng < n_chunks ? (n_chunks - rng + a.splits - 1) / a.splits : 0;
   const int my_chunk = rng + wave * a.splits;
@@ -415,9 +410,13 @@ void fwd_small_kernel(SmallFwdArgs a) {
     }
   }
 
-  // The T operand of this wave's chunk, into LDS for the epilogue (read
-  // only now: held across the decode its registers would not fit two
-  // workgroups per CU).
+  // The launch tag, then the T operand of this wave's chunk into LDS for
+  // the epilogue.  Both are requested only now: a load in flight holds up
+  // every later wait of its wave (the weights must not wait for the ticket),
+  // and T held across the decode would not fit two workgroups per CU.  The
+  // first barrier also ends every wave's reads of the values area, which
+  // the wave sums then reuse.
+  if (talk && tid == 0) drawn = draw_ticket(a.tickets, blockIdx.x, n_wgs);
   uint64_t tw[4] = {0ull, 0ull, 0ull, 0ull};
   if (t_live) {
     tw[0] = load_tagged_raw(tsrc);
@@ -425,6 +424,12 @@ void fwd_small_kernel(SmallFwdArgs a) {
     tw[2] = load_tagged_raw(tsrc + 32);
     tw[3] = load_tagged_raw(tsrc + 33);
   }
+  if (talk && wave == 0) {
+    resolve_tag();
+    if (lane == 0) L.tag = tag;
+  }
+  lds_barrier();
+  if (talk) tag = L.tag;
   if (wave < n_own) {
     uint32_t d[4] = {0u, 0u, 0u, 0u};
     if (t_live) {
@@ -443,7 +448,12 @@ void fwd_small_kernel(SmallFwdArgs a) {
     }
     tl[wave * 64 + lane] = u32x4_t{d[0], d[1], d[2], d[3]};
   }
-  if (!reduce_waves(acc, red, wave, lane)) return;
+  // sum the waves' accumulators into wave 0 (fixed order)
+  if (wave > 0) red[(wave - 1) * 64 + lane] = acc;
+  lds_barrier();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 0; w < kWaves - 1; ++w) acc += red[w * 64 + lane];
 
   // Low-rank term for this workgroup's chunks: acc += B_cat^T[rows, chunk]
   // T^T[chunk, :], as extra K steps (T already rounded to bf16).
