@@ -54,8 +54,10 @@ def kernel_source_hash() -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for name in FWD_SMALL_SOURCES:
-        with open(os.path.join(ROOT, "sparse_rank_linear_amd", "csrc", name), "rb") as f:
+    paths = [os.path.join(ROOT, "sparse_rank_linear_amd", "csrc", n) for n in FWD_SMALL_SOURCES]
+    paths.append(os.path.join(ROOT, "sparse_rank_linear_amd", "build.py"))  # compile flags
+    for path in paths:
+        with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
