@@ -137,6 +137,13 @@ def truncated_svd(R: np.ndarray, r: int):
     return U * sign, S, V * sign
 
 
+def singular_values(R: np.ndarray) -> np.ndarray:
+    """Every singular value of the residual, descending ([summary]
+    Methodology 2: the residual's spectrum, whose discarded tail is the
+    error of the rank-r factorization).  LAPACK in float64, values only."""
+    return np.linalg.svd(R, compute_uv=False)
+
+
 def residual_factors(U_r, S_r, V_r):
     """Balanced split of the truncated SVD into an adapter pair, float64:
     A' = V_r diag(sqrt(S_r)) [K x r], B' = diag(sqrt(S_r)) U_r^T [r x N],

@@ -28,6 +28,7 @@
 namespace salr {
 namespace {
 
+constexpr int kDies = 8;         // XCDs of the GPU, each with its own L2
 constexpr int kLdsRow = 36;      // words per 64-column bf16 tile row (+16 B pad)
 constexpr int kVRow = 40;        // words per row of staged values (9 chunks + window)
 
@@ -76,8 +77,19 @@ __global__ __launch_bounds__(64 * WM * WN) void fwd_large_kernel(LargeFwdArgs a)
   const int lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, g = lane >> 4;
   const int wn = wave % WN, wm = wave / WN;
-  const int64_t n0 = (int64_t)blockIdx.x * C::BN;
-  const int m0 = blockIdx.y * C::BM;
+  // Tile of this workgroup.  Workgroups are dealt to the 8 dies (XCDs) in
+  // turn (id % 8); tiles are numbered token-block-major and each die gets a
+  // contiguous run of them, so the workgroups on one die share the same X
+  // slab (read into that die's L2 once) instead of every die streaming every
+  // slab.
+  const int nb = (int)((a.N + C::BN - 1) / C::BN);
+  const int total = nb * ((a.M + C::BM - 1) / C::BM);
+  const int per_die = (total + kDies - 1) / kDies;
+  const int id = (int)blockIdx.x;  // grid: per_die * kDies workgroups
+  const int tile = (id % kDies) * per_die + id / kDies;
+  if (tile >= total) return;
+  const int64_t n0 = (int64_t)(tile % nb) * C::BN;
+  const int m0 = (tile / nb) * C::BM;
   const int nk = (a.K + 63) / 64;
 
   if (tid < 16) lut[tid] = nibble_selectors(tid);
@@ -318,7 +330,9 @@ hipError_t launch_lowrank_t(const LowRankTArgs& a, hipStream_t s) {
 hipError_t launch_fwd_large(const LargeFwdArgs& a, hipStream_t s) {
   // 256 tokens x 128 outputs per workgroup, 8 waves.
   using C = Cfg<4, 2>;
-  dim3 grid((unsigned)((a.N + C::BN - 1) / C::BN), (unsigned)((a.M + C::BM - 1) / C::BM));
+  // (ceil(tiles / 8) workgroups per die: see the tile mapping)
+  const int64_t tiles = ((a.N + C::BN - 1) / C::BN) * (int64_t)((a.M + C::BM - 1) / C::BM);
+  const dim3 grid((unsigned)((tiles + kDies - 1) / kDies * kDies));
   hipLaunchKernelGGL((fwd_large_kernel<4, 2>), grid, dim3(C::kThreads), 0, s, a);
   return hipGetLastError();
 }

@@ -1,0 +1,231 @@
+"""Full-size parity: every workload at its real shape, through the same C-ABI
+calls and launch configurations the benchmark times, checked where the
+oracle can follow.
+
+Encode (salr_encode on the whole weight):
+  * the whole bitmap by its defining properties, on the device: n_keep kept
+    per row, no pruned magnitude above a kept one, kept ties are the lowest
+    columns (the canonical set, unique); values and lookup table as the
+    kept entries and their running counts;
+  * sampled rows bit for bit against the oracle (bitmap, values, table) and
+    the LoRA blocks of A_cat / B_cat bit for bit;
+  * the truncated SVD against LAPACK's spectrum of the same residual
+    (fixtures written by tests/golden/make_svd_golden.py from the oracle):
+    top singular values within 1e-2, at least 99% of the optimal error
+    reduction, and the per-entry MSE bound of the pages.
+Forward (salr_linear_forward on the encoded bitmap and values with seeded
+adapters of the workload's total rank): sampled output columns, for every
+token up to 256 tokens and 256 sampled tokens beyond, against the oracle's
+float64 forward of the same rows from its own encoding."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import salr as osl
+from sparse_rank_linear_amd import synth
+from tests.gpu_util import TOL_MAX_REL, TOL_NORMWISE, errors, say, to_dev, to_host_bits, wait_error
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+# workload -> token counts of its forward checks
+FULL = {
+    "tiny_512": (16,),
+    "llama7b_attn_4096": (1, 4, 16),
+    "llama7b_mlp_up_11008": (2048,),
+    "llama7b_mlp_down_11008": (2048,),
+    "llama3_8b_qo": (1, 16, 256, 4096),
+    "llama3_8b_kv": (1, 16, 256, 4096),
+    "llama3_8b_gate_up": (1, 16, 256, 4096),
+    "llama3_8b_down": (1, 16, 256, 4096),
+    "l70b_up_s50": (8192,),
+    "l70b_up_s60": (8192,),
+    "l70b_up_s70": (8192,),
+    "l70b_down_s50": (8192,),
+    "l70b_down_s60": (8192,),
+    "l70b_down_s70": (8192,),
+}
+ROW_SAMPLES = 30
+TOKEN_SAMPLES = 256
+
+_inputs = {}
+_encoded = {}
+
+
+def _inputs_for(name):
+    """W and the LoRA pairs of a workload (shared by its sparsity variants)."""
+    wl = synth.WORKLOADS[name]
+    key = (wl.N, wl.K, wl.w_dist, wl.w_scale, wl.seed, wl.lora_ranks)
+    if key not in _inputs:
+        _inputs.clear()  # one weight on the host at a time
+        _inputs[key] = synth.make_inputs(wl, with_x=False)
+    return _inputs[key]
+
+
+def _rows(N):
+    rng = np.random.default_rng(1234)
+    pick = rng.choice(N, size=min(N, ROW_SAMPLES), replace=False)
+    return np.unique(np.concatenate([pick, [0, N - 1]]))
+
+
+def _encode(name):
+    """GPU encode of the whole workload (cached for the forward checks)."""
+    import torch
+    import sparse_rank_linear_amd as srl
+
+    if name not in _encoded:
+        _encoded.clear()
+        torch.cuda.empty_cache()
+        wl = synth.WORKLOADS[name]
+        inp = _inputs_for(name)
+        say(f"encode {name}: N={wl.N} K={wl.K} n_keep={wl.n_keep} r_svd={wl.r_svd} loras={wl.lora_ranks}")
+        Wd = to_dev(inp.W)
+        layer, sigma = srl.encode(Wd, wl.n_keep, wl.r_svd, [to_dev(a) for a in inp.lora_A],
+                                  [to_dev(b) for b in inp.lora_B])
+        torch.cuda.synchronize()
+        _encoded[name] = (Wd, layer, np.array(sigma))
+    return _encoded[name]
+
+
+def _unpack_rows(masks_rows, K):
+    """Bool [n, K] from int64 bitmap words [n, ceil(K/64)] (device)."""
+    import torch
+
+    shifts = torch.arange(64, device=masks_rows.device, dtype=torch.int64)
+    bits = (masks_rows.unsqueeze(-1) >> shifts) & 1
+    return bits.reshape(masks_rows.shape[0], -1)[:, :K].bool()
+
+
+def _check_bitmap_properties(Wd, layer, n_keep):
+    """Whole-layer checks of the kept set, values and table, on the device."""
+    import torch
+
+    N, K = Wd.shape
+    ng = layer.offsets.shape[1]
+    vals = layer.values.view(torch.int16)[: N * n_keep].view(N, n_keep)
+    step = max(1, (1 << 26) // max(K, 1))
+    for r0 in range(0, N, step):
+        r1 = min(N, r0 + step)
+        keep = _unpack_rows(layer.masks[r0:r1], K)
+        wb = Wd[r0:r1].view(torch.int16)
+        mag = wb.to(torch.int32) & 0x7FFF
+        cnt = keep.sum(dim=1)
+        assert bool((cnt == n_keep).all()), f"rows {r0}..{r1}: kept count != n_keep"
+        if 0 < n_keep < K:
+            big = torch.iinfo(torch.int32).max
+            t_min = torch.where(keep, mag, torch.full_like(mag, big)).min(dim=1).values
+            p_max = torch.where(keep, torch.full_like(mag, -1), mag).max(dim=1).values
+            assert bool((p_max <= t_min).all()), f"rows {r0}..{r1}: a pruned magnitude exceeds a kept one"
+            col = torch.arange(K, device=Wd.device, dtype=torch.int32).expand_as(mag)
+            tie = mag == t_min.unsqueeze(1)
+            last_kept_tie = torch.where(keep & tie, col, torch.full_like(col, -1)).max(dim=1).values
+            first_pruned_tie = torch.where(~keep & tie, col, torch.full_like(col, K)).min(dim=1).values
+            assert bool((last_kept_tie < first_pruned_tie).all()), f"rows {r0}..{r1}: ties not kept lowest-first"
+        # values: the kept entries, ascending columns, bit for bit
+        assert torch.equal(wb[keep].view(r1 - r0, n_keep), vals[r0:r1]), f"rows {r0}..{r1}: values"
+        # table: kept columns before every 1024th column
+        cs = torch.nn.functional.pad(keep.to(torch.int32).cumsum(dim=1), (1, 0))
+        want = cs[:, torch.arange(ng, device=Wd.device) * 1024]
+        assert torch.equal(want, layer.offsets[r0:r1]), f"rows {r0}..{r1}: lookup table"
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_fullsize_encode(name):
+    import torch
+
+    wl = synth.WORKLOADS[name]
+    inp = _inputs_for(name)
+    Wd, layer, sigma = _encode(name)
+    N, K, n_keep, r_svd = wl.N, wl.K, wl.n_keep, wl.r_svd
+
+    _check_bitmap_properties(Wd, layer, n_keep)
+    say("  bitmap properties ok")
+
+    # sampled rows against the oracle, bit for bit
+    rows = _rows(N)
+    keep = osl.select_keep(inp.W[rows], n_keep)
+    host = {k: v.cpu() for k, v in (("masks", layer.masks[rows]), ("offsets", layer.offsets[rows]))}
+    vals = layer.values.view(torch.int16)[: N * n_keep].view(N, n_keep)[rows].cpu().numpy().view(np.uint16)
+    assert np.array_equal(host["masks"].numpy().view(np.uint64), osl.pack_masks(keep))
+    assert np.array_equal(vals, osl.pack_values(inp.W[rows], keep, n_keep))
+    assert np.array_equal(host["offsets"].numpy().view(np.uint32), osl.block_offsets(keep))
+    a_cat = layer.a_cat.view(torch.int16)
+    b_cat = layer.b_cat.view(torch.int16)
+    r0 = r_svd
+    for A, B in zip(inp.lora_A, inp.lora_B):
+        q = A.shape[0]
+        assert np.array_equal(a_cat[r0:r0 + q].cpu().numpy().view(np.uint16), A)
+        assert np.array_equal(b_cat[:, r0:r0 + q][rows].cpu().numpy().view(np.uint16), B[rows])
+        r0 += q
+    say(f"  sampled rows {len(rows)} bit-exact")
+
+    # truncated SVD against the LAPACK spectrum of the same residual
+    gold = json.load(open(os.path.join(GOLDEN, f"svd_{name}.json")))
+    assert (gold["N"], gold["K"], gold["n_keep"], gold["r_svd"]) == (N, K, n_keep, r_svd)
+    ref = np.array(gold["sigma_top"])
+    rel = np.abs(sigma[:r_svd] - ref) / ref
+    say(f"  max sigma rel err={rel.max():.2e}")
+    assert rel.max() <= 1e-2
+    A = a_cat[:r_svd].view(torch.bfloat16).double()          # A'^T [r][K]
+    B = b_cat[:, :r_svd].view(torch.bfloat16).double()       # B'^T [N][r]
+    e_r = e_err = 0.0
+    step = max(1, (1 << 25) // K)
+    for s0 in range(0, N, step):
+        s1 = min(N, s0 + step)
+        kept = _unpack_rows(layer.masks[s0:s1], K)
+        R = torch.where(kept, torch.zeros((), dtype=torch.float64, device=Wd.device), Wd[s0:s1].double())
+        e_r += float((R * R).sum())
+        D = R - B[s0:s1] @ A
+        e_err += float((D * D).sum())
+    opt = gold["R_energy"] - gold["tail_energy"]       # best possible reduction
+    got = e_r - e_err
+    say(f"  ||R||^2 {e_r:.6e} (oracle {gold['R_energy']:.6e}); reduction {got:.6e} of optimal {opt:.6e}")
+    assert abs(e_r - gold["R_energy"]) <= 1e-9 * gold["R_energy"] + 1e-30
+    assert got >= 0.99 * opt
+    assert e_err / (N * K) <= (1 - r_svd / min(N, K)) * e_r / (N * K) + 1e-30
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_fullsize_forward(name):
+    import torch
+    import sparse_rank_linear_amd as srl
+
+    wl = synth.WORKLOADS[name]
+    inp = _inputs_for(name)
+    Wd, enc, _ = _encode(name)
+    N, K, n_keep = wl.N, wl.K, wl.n_keep
+    # adapters: a seeded block of rank r_svd in place of the residual factors
+    # (so that both sides take the same inputs), then the LoRA pairs
+    A_res = synth.make_w(wl.r_svd, K, seed=wl.seed + 101, scale=0.01)
+    B_res = synth.make_w(N, wl.r_svd, seed=wl.seed + 102, scale=0.01)
+    a_cat = np.concatenate([A_res] + list(inp.lora_A), axis=0)       # [r_cat][K]
+    b_cat = np.concatenate([B_res] + list(inp.lora_B), axis=1)       # [N][r_cat]
+    layer = srl.SalrLayer.empty(N, K, n_keep, wl.r_svd, wl.r_cat)
+    layer.masks.copy_(enc.masks)
+    layer.values.copy_(enc.values)
+    layer.offsets.copy_(enc.offsets)
+    layer.a_cat.view(torch.int16).copy_(torch.from_numpy(a_cat.view(np.int16)))
+    layer.b_cat.view(torch.int16).copy_(torch.from_numpy(np.ascontiguousarray(b_cat).view(np.int16)))
+
+    rows = _rows(N)
+    keep = osl.select_keep(inp.W[rows], n_keep)
+    m_o, v_o = osl.pack_masks(keep), osl.pack_values(inp.W[rows], keep, n_keep)
+    for M in FULL[name]:
+        X = synth.make_x(K, M, seed=wl.seed + 7 + M)
+        say(f"forward {name}: M={M} N={N} K={K} r_cat={wl.r_cat}")
+        ws = srl.forward_workspace(layer, M)
+        Y = srl.linear_forward(layer, to_dev(X), ws=ws)
+        torch.cuda.synchronize()
+        assert wait_error(ws) == 0
+        tok = np.arange(M) if M <= TOKEN_SAMPLES else np.sort(
+            np.random.default_rng(M).choice(M, TOKEN_SAMPLES, replace=False))
+        Yg = to_host_bits(Y[torch.from_numpy(tok).cuda()][:, torch.from_numpy(rows).cuda()])
+        Yref = osl.forward(X[tok], m_o, v_o, K, a_cat.T, b_cat[rows].T)
+        mr, nw = errors(Yg, Yref)
+        say(f"  {len(tok)} tokens x {len(rows)} rows: max_rel={mr:.3e} normwise={nw:.3e}")
+        assert mr <= TOL_MAX_REL and nw <= TOL_NORMWISE
+        del Y, ws

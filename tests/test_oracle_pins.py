@@ -208,6 +208,20 @@ def test_svd_on_known_spectrum():
     assert np.allclose(A1 @ B1, ((U[:, :3] * s[:3]) @ V[:, :3].T).T, atol=1e-11)
 
 
+def test_singular_values_on_known_spectrum():
+    """The values-only spectrum used for the full-size fixtures: a matrix of
+    known singular values (rank 7 in 40 x 30: the rest are zero), and the
+    tail energy identity sum(sigma^2) = ||R||_F^2."""
+    rng = np.random.default_rng(13)
+    s = np.array([9.0, 7.0, 5.0, 3.0, 2.0, 1.0, 0.5])
+    _, _, R = _known_svd_matrix(rng, 40, 30, s)
+    S = osl.singular_values(R)
+    assert S.shape == (30,)
+    assert np.allclose(S[:7], s, rtol=1e-12)
+    assert np.all(np.abs(S[7:]) < 1e-12)
+    assert np.isclose(np.sum(S ** 2), np.sum(R * R), rtol=1e-12)
+
+
 def test_svd_full_rank_reconstructs():
     rng = np.random.default_rng(12)
     R = rng.standard_normal((20, 13))
