@@ -14,11 +14,11 @@
 // product is computed as Y^T = W_s X^T so that a lane's four accumulator
 // rows are four consecutive outputs of one token (8-byte stores).
 //
-// Pipeline per K tile kt (two barriers):
-//   issue global loads for tile kt+2 (X, packed values) and the bitmap of
-//   kt+3 into registers;
+// Pipeline per K tile kt (one barrier):
+//   X of tile kt+1 straight to LDS (global_load_lds), the packed values of
+//   tile kt+2 and the bitmap word of kt+3 into registers;
 //   MFMA on tile kt  ||  decode of tile kt+1 (LDS values -> LDS dense W);
-//   store the tile kt+2 registers into the buffers freed this iteration.
+//   the values of kt+2 into the buffer freed by tile kt; barrier.
 // W rows are streams of packed values: a row's running kept count gives the
 // first value of each tile, so no lookup table is needed when K is walked
 // from column 0.
@@ -40,37 +40,42 @@ struct Cfg {
   static constexpr int TPR = kThreads / BN;         // decode threads per W row
   static constexpr int CPT = 64 / TPR;              // columns per decode thread
   static constexpr int VCH = (9 + TPR - 1) / TPR;   // value chunks per thread
-  static constexpr int XCH = BM * 8 / kThreads;     // X chunks per thread
+  static constexpr int XDMA = BM * 8 / kThreads;    // X chunks (direct-to-LDS loads) per thread
 };
 
-// Copy one 64-column X tile (rows m0.., cols k0..) into registers.
-template <class C>
-__device__ __forceinline__ void load_x_tile(u32x4_t (&r)[C::XCH], const uint16_t* X, int M, int K, int m0, int k0,
-                                            int tid) {
-#pragma unroll
-  for (int u = 0; u < C::XCH; ++u) {
-    const int c = tid + C::kThreads * u;
-    const int row = c >> 3, cc = c & 7;
-    const int m = m0 + row, k = k0 + 8 * cc;
-    r[u] = (m < M && k < K) ? load16(X + (size_t)m * K + k) : zero_u4();
-  }
-}
+// A 64-column bf16 tile row is 8 chunks of 16 bytes, stored without padding
+// at chunk slot (c ^ (row & 7)): a 16-row MFMA operand read (one chunk per
+// row) then hits every bank once per pass, and a whole-wave direct-to-LDS
+// load (64 lanes x 16 bytes, contiguous) fills 8 rows by choosing which
+// chunk each lane fetches.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
 
+// X tile (rows m0.., columns k0..) straight to LDS: load j of this wave
+// covers tile rows 8 (XDMA * wave + j) .. +7.  Rows past M and columns past
+// K read clamped (in-bounds) addresses: such rows only reach outputs that
+// are never stored, such columns meet zero weights.
 template <class C>
-__device__ __forceinline__ void store_x_tile(uint32_t* xl, const u32x4_t (&r)[C::XCH], int tid) {
+__device__ __forceinline__ void dma_x_tile(u32x4_t* xt, const uint16_t* X, int M, int K, int m0, int k0, int wave,
+                                           int lane) {
 #pragma unroll
-  for (int u = 0; u < C::XCH; ++u) {
-    const int c = tid + C::kThreads * u;
-    *reinterpret_cast<u32x4_t*>(&xl[(c >> 3) * kLdsRow + (c & 7) * 4]) = r[u];
+  for (int j = 0; j < C::XDMA; ++j) {
+    const int blk = C::XDMA * wave + j;  // 8-row block
+    const int row = 8 * blk + (lane >> 3);
+    const int chunk = (lane & 7) ^ (row & 7);
+    const int m = min(m0 + row, M - 1), k = min(k0 + 8 * chunk, K - 8);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(X + (size_t)m * K + k),
+                                     reinterpret_cast<uint32_t*>(xt + blk * 64), 16, 0, 0);
   }
 }
 
 template <int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN) void fwd_large_kernel(LargeFwdArgs a) {
   using C = Cfg<WM, WN>;
-  __shared__ uint32_t xl[2][C::BM * kLdsRow];
-  __shared__ uint32_t wl[2][C::BN * kLdsRow];
-  __shared__ uint32_t vl[C::BN * kVRow];
+  // (each buffer its own array, so the compiler can tell a load in flight
+  // into one from reads of the other)
+  __shared__ u32x4_t xl0[C::BM * 8], xl1[C::BM * 8];
+  __shared__ u32x4_t wl0[C::BN * 8], wl1[C::BN * 8];
+  __shared__ uint32_t vl0[C::BN * kVRow], vl1[C::BN * kVRow];
   __shared__ u32x2_t lut[16];
 
   const int tid = threadIdx.x;
@@ -100,41 +105,48 @@ __global__ __launch_bounds__(64 * WM * WN) void fwd_large_kernel(LargeFwdArgs a)
   const bool row_ok = grow < a.N;
   const int64_t row_base = row_ok ? grow * a.n_keep : 0;
   const uint64_t* mrow = a.masks + (row_ok ? grow * a.kw : 0);
-  auto mask_at = [&](int kt) -> uint64_t { return (row_ok && kt < nk) ? mrow[kt] : 0ull; };
+  // (the raw word of a clamped, unconditional load; mask_ok() applies the
+  // bounds where the word is used, so that it is not waited for at once)
+  auto mask_raw = [&](int kt) -> uint64_t { return mrow[min(kt, nk - 1)]; };
+  auto mask_ok = [&](uint64_t w, int kt) -> uint64_t { return (row_ok && kt < nk) ? w : 0ull; };
 
   // Stage the packed values of one tile of this row: chunks covering
-  // [row_base + run, + popcount(mask)).
-  auto load_v = [&](u32x4_t (&r)[C::VCH], uint32_t run, uint64_t mk) {
+  // [row_base + run, + popcount(mask)); returns how many.  The loads are
+  // unconditional (from clamped addresses; chunk 0 exists even for an empty
+  // layer thanks to the values buffer's tail padding) and their registers
+  // are not touched until stored, so the compiler counts them exactly and
+  // waits only at the store.
+  auto load_v = [&](u32x4_t (&r)[C::VCH], uint32_t run, uint64_t mk) -> int {
     const int64_t va = row_base + run;
     const int cnt = __popcll(mk);
     const int64_t q0 = va >> 3;
-    // chunks covering the segment, never past the last value of the layer
     const int64_t q1 = min((va + cnt + 7) >> 3, a.vchunks);
-    const int n = cnt ? (int)(q1 - q0) : 0;
 #pragma unroll
     for (int u = 0; u < C::VCH; ++u) {
       const int ch = dpart + C::TPR * u;
-      r[u] = (ch < n) ? load16(a.values + (q0 + ch) * 8) : zero_u4();
+      int64_t q = q0 + ch < a.vchunks ? q0 + ch : a.vchunks - 1;
+      q = q > 0 ? q : 0;
+      r[u] = load16(a.values + q * 8);
     }
+    return cnt ? (int)(q1 - q0) : 0;
   };
-  auto store_v = [&](const u32x4_t (&r)[C::VCH]) {
+  auto store_v = [&](uint32_t* vb, const u32x4_t (&r)[C::VCH], int n) {
 #pragma unroll
     for (int u = 0; u < C::VCH; ++u) {
       const int ch = dpart + C::TPR * u;
-      if (ch < 9) *reinterpret_cast<u32x4_t*>(&vl[drow * kVRow + ch * 4]) = r[u];
+      if (ch < 9) *reinterpret_cast<u32x4_t*>(&vb[drow * kVRow + ch * 4]) = ch < n ? r[u] : zero_u4();
     }
   };
   // Decode this thread's columns of one tile into dense bf16 in LDS.
-  auto decode = [&](uint32_t* wdst, uint32_t run, uint64_t mk) {
+  auto decode = [&](u32x4_t* wt, const uint32_t* vb, uint32_t run, uint64_t mk) {
     const uint32_t lead = (uint32_t)((row_base + run) & 7);
-    const uint16_t* rowbuf = reinterpret_cast<const uint16_t*>(&vl[drow * kVRow]);
+    const uint16_t* rowbuf = reinterpret_cast<const uint16_t*>(&vb[drow * kVRow]);
     const int cbeg = dpart * C::CPT;
     uint32_t idx = lead + (cbeg ? (uint32_t)__popcll(mk & ((1ull << cbeg) - 1ull)) : 0u);
 #pragma unroll
     for (int b = 0; b < C::CPT / 8; ++b) {
       const uint32_t byte = (uint32_t)(mk >> (cbeg + 8 * b)) & 0xFFu;
-      const u32x4_t d = expand_byte(rowbuf, idx, byte, lut);
-      *reinterpret_cast<u32x4_t*>(&wdst[drow * kLdsRow + (cbeg + 8 * b) / 2]) = d;
+      wt[swz(drow, cbeg / 8 + b)] = expand_byte(rowbuf, idx, byte, lut);
       idx += __popc(byte);
     }
   };
@@ -145,14 +157,14 @@ __global__ __launch_bounds__(64 * WM * WN) void fwd_large_kernel(LargeFwdArgs a)
 #pragma unroll
     for (int y = 0; y < 4; ++y) acc[x][y] = zero4();
 
-  auto mfma_tile = [&](const uint32_t* xs, const uint32_t* ws) {
+  auto mfma_tile = [&](const u32x4_t* xt, const u32x4_t* wt) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       u32x4_t av[4], bv[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        av[t] = *reinterpret_cast<const u32x4_t*>(&ws[(wn * 64 + t * 16 + i) * kLdsRow + ks * 16 + g * 4]);
-        bv[t] = *reinterpret_cast<const u32x4_t*>(&xs[(wm * 64 + t * 16 + i) * kLdsRow + ks * 16 + g * 4]);
+        av[t] = wt[swz(wn * 64 + t * 16 + i, ks * 4 + g)];
+        bv[t] = xt[swz(wm * 64 + t * 16 + i, ks * 4 + g)];
       }
 #pragma unroll
       for (int tn = 0; tn < 4; ++tn)
@@ -161,43 +173,49 @@ __global__ __launch_bounds__(64 * WM * WN) void fwd_large_kernel(LargeFwdArgs a)
     }
   };
 
-  // ---- prologue: tiles 0 and 1 staged, tile 0 decoded
-  uint64_t mk0 = mask_at(0), mk1 = mask_at(1), mk2 = mask_at(2);
+  // ---- prologue: X tile 0 and the values of tiles 0 and 1 in LDS, tile 0
+  // decoded
+  const uint64_t mk0 = mask_ok(mask_raw(0), 0);
+  uint64_t mk1 = mask_ok(mask_raw(1), 1);
+  uint64_t mk2raw = mask_raw(2);
   {
-    u32x4_t xr[C::XCH];
-    load_x_tile<C>(xr, a.X, a.M, a.K, m0, 0, tid);
-    store_x_tile<C>(xl[0], xr, tid);
-    load_x_tile<C>(xr, a.X, a.M, a.K, m0, 64, tid);
-    store_x_tile<C>(xl[1], xr, tid);
+    dma_x_tile<C>(xl0, a.X, a.M, a.K, m0, 0, wave, lane);
     u32x4_t vr[C::VCH];
-    load_v(vr, 0u, mk0);
-    store_v(vr);
+    int n = load_v(vr, 0u, mk0);
+    store_v(vl0, vr, n);
+    n = load_v(vr, (uint32_t)__popcll(mk0), mk1);
+    store_v(vl1, vr, n);
     __syncthreads();
-    decode(wl[0], 0u, mk0);
-    __syncthreads();
-    load_v(vr, (uint32_t)__popcll(mk0), mk1);
-    store_v(vr);
+    decode(wl0, vl0, 0u, mk0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
   uint32_t run1 = (uint32_t)__popcll(mk0);  // first value of tile kt+1
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
+  // One K tile, one barrier: X of tile kt+1 goes straight to LDS and the
+  // values of tile kt+2 to registers while the matrix cores work on tile kt
+  // and the decode builds tile kt+1; the values land in the buffer tile kt's
+  // values just left.  (Unrolled by two so that every buffer is named.)
+  auto step = [&](int kt, u32x4_t* xc, u32x4_t* xn, u32x4_t* wc, u32x4_t* wn_, uint32_t* vc, uint32_t* vn) {
+    if (kt + 1 < nk) dma_x_tile<C>(xn, a.X, a.M, a.K, m0, (kt + 1) * 64, wave, lane);
+    const uint64_t mk2 = mask_ok(mk2raw, kt + 2);
     const uint32_t run2 = run1 + (uint32_t)__popcll(mk1);
-    u32x4_t xr[C::XCH], vr[C::VCH];
-    load_x_tile<C>(xr, a.X, a.M, a.K, m0, (kt + 2) * 64, tid);
-    load_v(vr, run2, mk2);
-    const uint64_t mk3 = mask_at(kt + 3);
+    u32x4_t vr[C::VCH];
+    const int n2 = load_v(vr, run2, mk2);
+    const uint64_t mk3raw = mask_raw(kt + 3);
 
-    mfma_tile(xl[cur], wl[cur]);
-    decode(wl[cur ^ 1], run1, mk1);
-    __syncthreads();
-    store_x_tile<C>(xl[cur], xr, tid);
-    store_v(vr);
+    mfma_tile(xc, wc);
+    if (kt + 1 < nk) decode(wn_, vn, run1, mk1);
+    store_v(vc, vr, n2);
+    __builtin_amdgcn_s_waitcnt(0);  // (this wave's X loads into LDS)
     __syncthreads();
     mk1 = mk2;
-    mk2 = mk3;
+    mk2raw = mk3raw;
     run1 = run2;
+  };
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, xl0, xl1, wl0, wl1, vl0, vl1);
+    if (kt + 1 < nk) step(kt + 1, xl1, xl0, wl1, wl0, vl1, vl0);
   }
 
   // ---- low-rank term as extra K tiles: Y^T += B_cat^T[n, :] T[m, :]^T, where
@@ -206,36 +224,42 @@ __global__ __launch_bounds__(64 * WM * WN) void fwd_large_kernel(LargeFwdArgs a)
   if (a.r_cat > 0) {
     const size_t split_stride = (size_t)a.M * a.r_pad;
     for (int r0 = 0; r0 < a.r_cat; r0 += 64) {
-      u32x4_t xr[C::XCH];
 #pragma unroll
-      for (int u = 0; u < C::XCH; ++u) {
+      for (int u = 0; u < C::XDMA; ++u) {
         const int c = tid + C::kThreads * u;
-        const int m = m0 + (c >> 3), k = r0 + 8 * (c & 7);
-        xr[u] = zero_u4();
+        const int row = c >> 3, ch = c & 7;
+        const int m = m0 + row, k = r0 + 8 * ch;
+        u32x4_t v = zero_u4();
         if (m < a.M && k < a.r_pad) {
           f32x4_t lo = zero4(), hi = zero4();
           const float* src = a.tpart + (size_t)m * a.r_pad + k;
+#pragma unroll 4
           for (int sp = 0; sp < a.t_splits; ++sp) {
             lo += *reinterpret_cast<const f32x4_t*>(src + sp * split_stride);
             hi += *reinterpret_cast<const f32x4_t*>(src + sp * split_stride + 4);
           }
-          xr[u] = u32x4_t{(uint32_t)f32_to_bf16(lo[0]) | ((uint32_t)f32_to_bf16(lo[1]) << 16),
-                          (uint32_t)f32_to_bf16(lo[2]) | ((uint32_t)f32_to_bf16(lo[3]) << 16),
-                          (uint32_t)f32_to_bf16(hi[0]) | ((uint32_t)f32_to_bf16(hi[1]) << 16),
-                          (uint32_t)f32_to_bf16(hi[2]) | ((uint32_t)f32_to_bf16(hi[3]) << 16)};
+          v = u32x4_t{(uint32_t)f32_to_bf16(lo[0]) | ((uint32_t)f32_to_bf16(lo[1]) << 16),
+                      (uint32_t)f32_to_bf16(lo[2]) | ((uint32_t)f32_to_bf16(lo[3]) << 16),
+                      (uint32_t)f32_to_bf16(hi[0]) | ((uint32_t)f32_to_bf16(hi[1]) << 16),
+                      (uint32_t)f32_to_bf16(hi[2]) | ((uint32_t)f32_to_bf16(hi[3]) << 16)};
         }
+        xl0[swz(row, ch)] = v;
       }
-      store_x_tile<C>(xl[0], xr, tid);
       const int cbeg = dpart * C::CPT;
 #pragma unroll
-      for (int c2 = 0; c2 < C::CPT; c2 += 2) {
-        const int ra = r0 + cbeg + c2;
-        const uint32_t lo = (row_ok && ra < a.r_cat) ? a.b_cat[grow * a.r_cat + ra] : 0u;
-        const uint32_t hi = (row_ok && ra + 1 < a.r_cat) ? a.b_cat[grow * a.r_cat + ra + 1] : 0u;
-        wl[0][drow * kLdsRow + (cbeg + c2) / 2] = lo | (hi << 16);
+      for (int c8 = 0; c8 < C::CPT; c8 += 8) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ra = r0 + cbeg + c8 + 2 * e;
+          const uint32_t lo = (row_ok && ra < a.r_cat) ? a.b_cat[grow * a.r_cat + ra] : 0u;
+          const uint32_t hi = (row_ok && ra + 1 < a.r_cat) ? a.b_cat[grow * a.r_cat + ra + 1] : 0u;
+          w[e] = lo | (hi << 16);
+        }
+        wl0[swz(drow, (cbeg + c8) / 8)] = u32x4_t{w[0], w[1], w[2], w[3]};
       }
       __syncthreads();
-      mfma_tile(xl[0], wl[0]);
+      mfma_tile(xl0, wl0);
       __syncthreads();
     }
   }

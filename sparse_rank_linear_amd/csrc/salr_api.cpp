@@ -60,9 +60,10 @@ int t_splits_large(int64_t M, int64_t K) {
   const int64_t mblocks = cdiv(M, 64);
   const int64_t nk = cdiv(K, 64);
   // splits only while mblocks * splits <= 256 (bounded partial buffer and
-  // counter block)
+  // counter block), and each at least 8 tiles of 64 columns: the forward
+  // kernel sums the splits for every T element it reads
   int64_t s = std::max<int64_t>(1, 256 / mblocks);
-  return (int)std::min<int64_t>(s, nk);
+  return (int)std::min<int64_t>(s, std::max<int64_t>(1, nk / 8));
 }
 
 struct FwdLayout {
