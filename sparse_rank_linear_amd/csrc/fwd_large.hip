@@ -22,6 +22,8 @@
 // W rows are streams of packed values: a row's running kept count gives the
 // first value of each tile, so no lookup table is needed when K is walked
 // from column 0.
+#include <algorithm>
+
 #include "salr_device.hpp"
 #include "salr_kernels.hpp"
 
@@ -29,6 +31,7 @@ namespace salr {
 namespace {
 
 constexpr int kDies = 8;         // XCDs of the GPU, each with its own L2
+constexpr int64_t kFillItems = 256;  // work items wanted to occupy the CUs
 constexpr int kLdsRow = 36;      // words per 64-column bf16 tile row (+16 B pad)
 constexpr int kVRow = 40;        // words per row of staged values (9 chunks + window)
 
@@ -87,15 +90,20 @@ __global__ __launch_bounds__(64 * WM * WN) void fwd_large_kernel(LargeFwdArgs a)
   // contiguous run of them, so the workgroups on one die share the same X
   // slab (read into that die's L2 once) instead of every die streaming every
   // slab.
+  // With K splits, consecutive work items of a die take the same split of
+  // neighbouring tiles.
   const int nb = (int)((a.N + C::BN - 1) / C::BN);
   const int total = nb * ((a.M + C::BM - 1) / C::BM);
-  const int per_die = (total + kDies - 1) / kDies;
+  const int items = total * a.ksplit;
+  const int per_die = (items + kDies - 1) / kDies;
   const int id = (int)blockIdx.x;  // grid: per_die * kDies workgroups
-  const int tile = (id % kDies) * per_die + id / kDies;
-  if (tile >= total) return;
+  const int item = (id % kDies) * per_die + id / kDies;
+  if (item >= items) return;
+  const int tile = item % total, split = item / total;
   const int64_t n0 = (int64_t)(tile % nb) * C::BN;
   const int m0 = (tile / nb) * C::BM;
-  const int nk = (a.K + 63) / 64;
+  const int kt0 = split * a.kt_per;                        // this split's first K tile
+  const int nk = min((a.K + 63) / 64, kt0 + a.kt_per);    // one past its last
 
   if (tid < 16) lut[tid] = nibble_selectors(tid);
 
@@ -107,7 +115,7 @@ __global__ __launch_bounds__(64 * WM * WN) void fwd_large_kernel(LargeFwdArgs a)
   const uint64_t* mrow = a.masks + (row_ok ? grow * a.kw : 0);
   // (the raw word of a clamped, unconditional load; mask_ok() applies the
   // bounds where the word is used, so that it is not waited for at once)
-  auto mask_raw = [&](int kt) -> uint64_t { return mrow[min(kt, nk - 1)]; };
+  auto mask_raw = [&](int kt) -> uint64_t { return mrow[min(kt, a.kw - 1)]; };
   auto mask_ok = [&](uint64_t w, int kt) -> uint64_t { return (row_ok && kt < nk) ? w : 0ull; };
 
   // Stage the packed values of one tile of this row: chunks covering
@@ -175,22 +183,37 @@ __global__ __launch_bounds__(64 * WM * WN) void fwd_large_kernel(LargeFwdArgs a)
 
   // ---- prologue: X tile 0 and the values of tiles 0 and 1 in LDS, tile 0
   // decoded
-  const uint64_t mk0 = mask_ok(mask_raw(0), 0);
-  uint64_t mk1 = mask_ok(mask_raw(1), 1);
-  uint64_t mk2raw = mask_raw(2);
+  // kept values of the row before this split: the lookup table entry at the
+  // last 1024-column boundary, plus the bitmap words after it
+  uint32_t run0 = 0;
+  if (kt0 > 0) {
+    // (all loads issued together: fixed count, clamped indices, masked sums)
+    const int w0 = kt0 & ~15;
+    uint64_t wd[15];
+#pragma unroll
+    for (int u = 0; u < 15; ++u) wd[u] = mrow[min(w0 + u, a.kw - 1)];
+    const uint32_t base = a.offsets[(row_ok ? grow : 0) * a.ng + (kt0 >> 4)];
+    uint32_t sum = 0;
+#pragma unroll
+    for (int u = 0; u < 15; ++u) sum += (w0 + u < kt0) ? (uint32_t)__popcll(wd[u]) : 0u;
+    run0 = row_ok ? base + sum : 0u;
+  }
+  const uint64_t mk0 = mask_ok(mask_raw(kt0), kt0);
+  uint64_t mk1 = mask_ok(mask_raw(kt0 + 1), kt0 + 1);
+  uint64_t mk2raw = mask_raw(kt0 + 2);
   {
-    dma_x_tile<C>(xl0, a.X, a.M, a.K, m0, 0, wave, lane);
+    dma_x_tile<C>(xl0, a.X, a.M, a.K, m0, kt0 * 64, wave, lane);
     u32x4_t vr[C::VCH];
-    int n = load_v(vr, 0u, mk0);
+    int n = load_v(vr, run0, mk0);
     store_v(vl0, vr, n);
-    n = load_v(vr, (uint32_t)__popcll(mk0), mk1);
+    n = load_v(vr, run0 + (uint32_t)__popcll(mk0), mk1);
     store_v(vl1, vr, n);
     __syncthreads();
-    decode(wl0, vl0, 0u, mk0);
+    decode(wl0, vl0, run0, mk0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
-  uint32_t run1 = (uint32_t)__popcll(mk0);  // first value of tile kt+1
+  uint32_t run1 = run0 + (uint32_t)__popcll(mk0);  // first value of tile kt+1
 
   // One K tile, one barrier: X of tile kt+1 goes straight to LDS and the
   // values of tile kt+2 to registers while the matrix cores work on tile kt
@@ -213,7 +236,7 @@ __global__ __launch_bounds__(64 * WM * WN) void fwd_large_kernel(LargeFwdArgs a)
     mk2raw = mk3raw;
     run1 = run2;
   };
-  for (int kt = 0; kt < nk; kt += 2) {
+  for (int kt = kt0; kt < nk; kt += 2) {
     step(kt, xl0, xl1, wl0, wl1, vl0, vl1);
     if (kt + 1 < nk) step(kt + 1, xl1, xl0, wl1, wl0, vl1, vl0);
   }
@@ -221,7 +244,7 @@ __global__ __launch_bounds__(64 * WM * WN) void fwd_large_kernel(LargeFwdArgs a)
   // ---- low-rank term as extra K tiles: Y^T += B_cat^T[n, :] T[m, :]^T, where
   // T = X A_cat is the sum of the K-split partials (written by the previous
   // launch), rounded to bf16 before it meets B_cat.
-  if (a.r_cat > 0) {
+  if (a.r_cat > 0 && split == 0) {
     const size_t split_stride = (size_t)a.M * a.r_pad;
     for (int r0 = 0; r0 < a.r_cat; r0 += 64) {
 #pragma unroll
@@ -265,6 +288,25 @@ __global__ __launch_bounds__(64 * WM * WN) void fwd_large_kernel(LargeFwdArgs a)
   }
 
   // ---- epilogue: lane holds Y[m][n .. n+3]
+  if (a.ksplit > 1) {
+    float* part = a.ypart + (size_t)split * a.M * a.N;
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) {
+      const int64_t n = n0 + wn * 64 + tn * 16 + 4 * g;
+#pragma unroll
+      for (int tm = 0; tm < 4; ++tm) {
+        const int m = m0 + wm * 64 + tm * 16 + i;
+        if (m >= a.M) continue;
+        float* dst = part + (size_t)m * a.N + n;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = acc[tn][tm][e];  // (scalar copy first: see the few-row kernel)
+          if (n + e < a.N) dst[e] = v;
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int tn = 0; tn < 4; ++tn) {
     const int64_t n = n0 + wn * 64 + tn * 16 + 4 * g;
@@ -351,13 +393,77 @@ hipError_t launch_lowrank_t(const LowRankTArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+int64_t fwd_large_tiles(int64_t N, int64_t M) {
+  using C = Cfg<4, 2>;
+  return ((N + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM);
+}
+
+int fwd_large_ksplit(int64_t N, int64_t K, int64_t M) {
+  // enough work items for every CU, each split at least 8 K tiles, at most 8
+  const int64_t tiles = fwd_large_tiles(N, M), nk = (K + 63) / 64;
+  int64_t s = std::min<int64_t>({kFillItems / std::max<int64_t>(tiles, 1), nk / 8, 8});
+  return (int)std::max<int64_t>(s, 1);
+}
+
+size_t fwd_large_part_bytes(int64_t N, int64_t K, int64_t M_max) {
+  // ksplit * tiles <= kFillItems, so the partials never exceed kFillItems
+  // whole tiles; nothing when no M <= M_max splits
+  using C = Cfg<4, 2>;
+  size_t most = 0;
+  for (int64_t M = C::BM; M - C::BM < M_max; M += C::BM) {
+    const int s = fwd_large_ksplit(N, K, std::min<int64_t>(M, M_max));
+    if (s > 1) most = std::max(most, (size_t)s * std::min<int64_t>(M, M_max) * N * 4);
+    if (fwd_large_tiles(N, M) >= kFillItems) break;
+  }
+  return most;
+}
+
+namespace {
+// Y = bf16(sum of the K-split partials, in split order): 8 outputs a thread
+// (16-byte loads and store when MN is a multiple of 8, as it is whenever N is).
+__global__ __launch_bounds__(256) void sum_splits_kernel(const float* part, uint16_t* Y, int64_t MN, int ksplit) {
+  const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (e0 >= MN) return;
+  if ((MN & 7) == 0) {
+    f32x4_t lo = zero4(), hi = zero4();
+    for (int s = 0; s < ksplit; ++s) {
+      const float* src = part + (size_t)s * MN + e0;
+      lo += *reinterpret_cast<const f32x4_t*>(src);
+      hi += *reinterpret_cast<const f32x4_t*>(src + 4);
+    }
+    *reinterpret_cast<u32x4_t*>(Y + e0) =
+        u32x4_t{(uint32_t)f32_to_bf16(lo[0]) | ((uint32_t)f32_to_bf16(lo[1]) << 16),
+                (uint32_t)f32_to_bf16(lo[2]) | ((uint32_t)f32_to_bf16(lo[3]) << 16),
+                (uint32_t)f32_to_bf16(hi[0]) | ((uint32_t)f32_to_bf16(hi[1]) << 16),
+                (uint32_t)f32_to_bf16(hi[2]) | ((uint32_t)f32_to_bf16(hi[3]) << 16)};
+    return;
+  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int n = (int)min<int64_t>(8, MN - e0);
+  for (int s = 0; s < ksplit; ++s) {
+    const float* src = part + (size_t)s * MN + e0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (e < n) acc[e] += src[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (e < n) Y[e0 + e] = f32_to_bf16(acc[e]);
+}
+}  // namespace
+
 hipError_t launch_fwd_large(const LargeFwdArgs& a, hipStream_t s) {
   // 256 tokens x 128 outputs per workgroup, 8 waves.
   using C = Cfg<4, 2>;
-  // (ceil(tiles / 8) workgroups per die: see the tile mapping)
-  const int64_t tiles = ((a.N + C::BN - 1) / C::BN) * (int64_t)((a.M + C::BM - 1) / C::BM);
-  const dim3 grid((unsigned)((tiles + kDies - 1) / kDies * kDies));
+  // (ceil(work items / 8) workgroups per die: see the tile mapping)
+  const int64_t items = fwd_large_tiles(a.N, a.M) * a.ksplit;
+  const dim3 grid((unsigned)((items + kDies - 1) / kDies * kDies));
   hipLaunchKernelGGL((fwd_large_kernel<4, 2>), grid, dim3(C::kThreads), 0, s, a);
+  if (a.ksplit > 1) {
+    const int64_t mn = a.N * (int64_t)a.M;
+    hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((mn + 2047) / 2048)), dim3(256), 0, s, a.ypart, a.Y, mn,
+                       a.ksplit);
+  }
   return hipGetLastError();
 }
 

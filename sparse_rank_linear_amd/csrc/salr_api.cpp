@@ -60,10 +60,10 @@ int t_splits_large(int64_t M, int64_t K) {
   const int64_t mblocks = cdiv(M, 64);
   const int64_t nk = cdiv(K, 64);
   // splits only while mblocks * splits <= 256 (bounded partial buffer and
-  // counter block), and each at least 8 tiles of 64 columns: the forward
+  // counter block), and each at least 4 tiles of 64 columns: the forward
   // kernel sums the splits for every T element it reads
   int64_t s = std::max<int64_t>(1, 256 / mblocks);
-  return (int)std::min<int64_t>(s, std::max<int64_t>(1, nk / 8));
+  return (int)std::min<int64_t>(s, std::max<int64_t>(1, nk / 4));
 }
 
 struct FwdLayout {
@@ -74,7 +74,7 @@ struct FwdLayout {
   int64_t m_max;
   int r_pad_large;
   // offsets (bytes)
-  size_t tsum, tfinal, ypart, T, ltpart, total;
+  size_t tsum, tfinal, ypart, T, ltpart, ylarge, total;
 };
 
 FwdLayout fwd_layout(int64_t N, int64_t K, int32_t n_keep, int32_t r_cat, int64_t M_max) {
@@ -131,6 +131,9 @@ FwdLayout fwd_layout(int64_t N, int64_t K, int32_t n_keep, int32_t r_cat, int64_
     const size_t rows = (size_t)std::max<int64_t>(64 * 256, cdiv(L.m_max, 64) * 64);
     off = align_up(off + rows * L.r_pad_large * 4, 256);
   }
+  // many-row path: fp32 K-split partials of Y (few output tiles only)
+  L.ylarge = off;
+  if (L.m_max > kSmallM) off = align_up(off + salr::fwd_large_part_bytes(N, K, L.m_max), 256);
   L.total = off;
   return L;
 }
@@ -316,6 +319,13 @@ int salr_linear_forward(const salr_layer_t* L, const uint16_t* X, int64_t M, uin
     a.M = (int32_t)M;
     a.kw = (int32_t)cdiv(L->K, 64);
     a.vchunks = cdiv(L->N * (int64_t)L->n_keep, 8);
+    a.offsets = L->offsets;
+    a.ng = (int32_t)cdiv(L->K, 1024);
+    a.ksplit = salr::fwd_large_ksplit(L->N, L->K, M);
+    const int64_t nk = cdiv(L->K, 64);
+    a.kt_per = (int32_t)(cdiv(cdiv(nk, a.ksplit), 8) * 8);  // (whole groups of 8 tiles)
+    a.ksplit = (int32_t)cdiv(nk, a.kt_per);
+    a.ypart = at<float>(ws, W.ylarge);
     err = salr::launch_fwd_large(a, s);
   }
   return err == hipSuccess ? SALR_OK : SALR_ERR_HIP;

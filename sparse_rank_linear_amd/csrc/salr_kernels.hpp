@@ -87,8 +87,21 @@ struct LargeFwdArgs {
   int32_t t_splits;
   int32_t kw;
   int64_t vchunks;         // ceil(N * n_keep / 8): 16-byte chunks of values
+  // K splits (1 = none): split s covers 64-column tiles [s*kt_per, +kt_per)
+  // and, when ksplit > 1, writes fp32 partials to ypart[s][M][N], summed in
+  // split order by a second launch
+  const uint32_t* offsets; // [N][ng] kept counts before every 1024th column
+  int32_t ng;
+  int32_t ksplit, kt_per;
+  float* ypart;
 };
 hipError_t launch_fwd_large(const LargeFwdArgs& a, hipStream_t s);
+// Output tiles of the many-row kernel and the K splits it takes for M rows
+// (more workgroups when the tiles alone cannot fill the GPU).
+int64_t fwd_large_tiles(int64_t N, int64_t M);
+int fwd_large_ksplit(int64_t N, int64_t K, int64_t M);
+// Bytes of fp32 split partials the many-row kernel may need for up to M_max rows.
+size_t fwd_large_part_bytes(int64_t N, int64_t K, int64_t M_max);
 
 // ----------------------------------------------------------------------------
 // Encode kernels.
