@@ -44,6 +44,7 @@ namespace salr {
 namespace {
 
 constexpr int kThreads = 512;
+constexpr int64_t kCus = 256;  // compute units of the GPU
 constexpr int kWaves = kThreads / 64;
 constexpr int kRows = 16;
 constexpr int kMaxSteps = kMaxRangeCols / 32 / kWaves;  // 32-column steps per wave
@@ -152,6 +153,9 @@ __device__ __forceinline__ void copy_chunks_to_lds(const uint32_t* src, uint32_t
   }
 }
 
+// kOneRound: every weight workgroup is resident at once, so the T producers
+// sit on CUs beside some of them (see the producer section).
+template <bool kOneRound>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void fwd_small_kernel(SmallFwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -206,6 +210,9 @@ void fwd_small_kernel(SmallFwdArgs a) {
   };
 
   if (!producer) {
+    // (beside a T producer, this workgroup's waves take every issue slot
+    // first)
+    if (kOneRound) __builtin_amdgcn_s_setprio(3);
     load_x_frags();
     if (tid < 16) L.lut[tid] = nibble_selectors(tid);
     const int lw = wave, lws = kWaves;
@@ -274,6 +281,10 @@ void fwd_small_kernel(SmallFwdArgs a) {
   // tile is held up by it.
   if (producer) {
     if (tid == 0) drawn = draw_ticket(a.tickets, blockIdx.x, n_wgs);
+    // With all weight workgroups resident, a producer shares its CU with one
+    // of them, whose loads it would otherwise delay while they are issued:
+    // start about 1 us later (T is needed only after the decode).
+    if (kOneRound) __builtin_amdgcn_s_sleep(40);
     const int piece = c;
     const int j = piece / a.t_pieces, kp = piece % a.t_pieces;
     const int rank = 16 * j + i;
@@ -506,8 +517,12 @@ size_t fwd_small_lds_bytes(int vcap, int tl_bytes, int bl_bytes) {
 
 hipError_t launch_fwd_small(const SmallFwdArgs& a, hipStream_t s) {
   const int grid = a.n_tiles * a.splits + a.r_tiles * a.t_pieces;
-  hipLaunchKernelGGL(fwd_small_kernel, dim3(grid), dim3(kThreads), fwd_small_lds_bytes(a.vcap, a.tl_bytes, a.bl_bytes),
-                     s, a);
+  const size_t lds = fwd_small_lds_bytes(a.vcap, a.tl_bytes, a.bl_bytes);
+  // one weight workgroup per CU at most: all resident in one round
+  if ((int64_t)a.n_tiles * a.splits <= kCus)
+    hipLaunchKernelGGL(fwd_small_kernel<true>, dim3(grid), dim3(kThreads), lds, s, a);
+  else
+    hipLaunchKernelGGL(fwd_small_kernel<false>, dim3(grid), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
