@@ -208,6 +208,150 @@ __global__ __launch_bounds__(kSmallThreads) void chol_inv_kernel(const float* G,
   }
 }
 
+// The same factorization with the matrix in registers (l <= kRegChol):
+// thread (ty, tx) of a 32 x 32 grid holds the entries (ty + 32x, tx + 32y),
+// x, y < NB.  Cholesky step j: the holders of column j publish it (pivot
+// included) to LDS, the holder of the pivot also its square root and
+// reciprocal, then after one barrier every thread applies the rank-1 update
+// to its own entries.  The published columns stay in LDS (packed, column j
+// at pk(j) = j*l - j*(j-1)/2) and give L for the inverse, which runs the same
+// way over the rows of Li = L^{-1} (one published row per step, two row
+// buffers in turn).  Every LDS access of a step is a broadcast or
+// consecutive doubles, so no bank conflicts.  A zero pivot gives a zero
+// column of L and a zero row of Li, as in chol_inv_kernel; the arithmetic
+// differs from it only in multiplying by the reciprocal of the pivot.
+constexpr int kRegChol = 160;
+
+__device__ inline int packed_col(int j, int l) { return j * l - (j * (j - 1)) / 2; }
+
+template <int NB>
+__global__ __launch_bounds__(kSmallThreads) void chol_inv_reg_kernel(const float* G, float* C, int l, double tol_rel) {
+  extern __shared__ double sm[];
+  double* Lt = sm;                          // packed columns of L before scaling
+  double* rowb = Lt + (l * (l + 1)) / 2;    // [2][l] published rows of Li
+  double* dv = rowb + 2 * l;                // pivots' square roots (diagonal of L)
+  double* rdv = dv + l;                     // their reciprocals (0 for a zero pivot)
+  __shared__ double wmax[kSmallThreads / 64];
+  const int tid = threadIdx.x;
+  const int tx = tid & 31, ty = tid >> 5;
+  double a[NB][NB];
+#pragma unroll
+  for (int x = 0; x < NB; ++x)
+#pragma unroll
+    for (int y = 0; y < NB; ++y) {
+      const int i = ty + 32 * x, k = tx + 32 * y;
+      a[x][y] = (i < l && k < l) ? (double)G[(int64_t)i * l + k] : 0.0;
+    }
+  // tolerance from the largest diagonal entry
+  double m = 0.0;
+#pragma unroll
+  for (int x = 0; x < NB; ++x)
+#pragma unroll
+    for (int y = 0; y < NB; ++y)
+      if (ty + 32 * x == tx + 32 * y && ty + 32 * x < l) m = fmax(m, a[x][y]);
+  for (int o = 32; o > 0; o >>= 1) m = fmax(m, __shfl_xor(m, o));
+  if ((tid & 63) == 0) wmax[tid >> 6] = m;
+  __syncthreads();
+  double maxd = 0.0;
+  for (int w = 0; w < kSmallThreads / 64; ++w) maxd = fmax(maxd, wmax[w]);
+  const double tol = tol_rel * maxd;
+
+  for (int j = 0; j < l; ++j) {
+    const int pj = packed_col(j, l);
+    if (tx == (j & 31)) {
+#pragma unroll
+      for (int y = 0; y < NB; ++y) {
+        if (y != (j >> 5)) continue;
+#pragma unroll
+        for (int x = 0; x < NB; ++x) {
+          const int i = ty + 32 * x;
+          if (i < j || i >= l) continue;
+          Lt[pj + i - j] = a[x][y];
+          if (i == j) {
+            const double p = a[x][y];
+            const double d = (p > tol && p > 0.0) ? sqrt(p) : 0.0;
+            dv[j] = d;
+            rdv[j] = d > 0.0 ? 1.0 / d : 0.0;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    const double rd = rdv[j];
+    double li[NB], lk[NB];
+#pragma unroll
+    for (int x = 0; x < NB; ++x) {
+      const int i = ty + 32 * x;
+      li[x] = (i > j && i < l) ? Lt[pj + i - j] * rd : 0.0;
+      const int k = tx + 32 * x;
+      lk[x] = (k > j && k < l) ? Lt[pj + k - j] * rd : 0.0;
+    }
+#pragma unroll
+    for (int x = 0; x < NB; ++x)
+#pragma unroll
+      for (int y = 0; y < NB; ++y) a[x][y] -= li[x] * lk[y];
+  }
+
+  // Li by rows: row k is final once divided by L[k][k]; rows below take
+  // X[i][c] -= L[i][k] * Li[k][c] (c <= k)
+#pragma unroll
+  for (int x = 0; x < NB; ++x)
+#pragma unroll
+    for (int y = 0; y < NB; ++y) a[x][y] = (ty + 32 * x == tx + 32 * y) ? 1.0 : 0.0;
+  for (int k = 0; k < l; ++k) {
+    double* rb = rowb + (k & 1) * l;
+    const double rk = rdv[k];
+    if (ty == (k & 31)) {
+#pragma unroll
+      for (int x = 0; x < NB; ++x) {
+        if (x != (k >> 5)) continue;
+#pragma unroll
+        for (int y = 0; y < NB; ++y) {
+          const int c = tx + 32 * y;
+          if (c > k) continue;
+          a[x][y] *= rk;
+          rb[c] = a[x][y];
+        }
+      }
+    }
+    __syncthreads();
+    const int pk = packed_col(k, l);
+    double lik[NB], xr[NB];
+#pragma unroll
+    for (int x = 0; x < NB; ++x) {
+      const int i = ty + 32 * x;
+      lik[x] = (i > k && i < l) ? Lt[pk + i - k] * rk : 0.0;
+      const int c = tx + 32 * x;
+      xr[x] = c <= k ? rb[c] : 0.0;
+    }
+#pragma unroll
+    for (int x = 0; x < NB; ++x)
+#pragma unroll
+      for (int y = 0; y < NB; ++y) a[x][y] -= lik[x] * xr[y];
+  }
+  // C = Li^T
+#pragma unroll
+  for (int x = 0; x < NB; ++x)
+#pragma unroll
+    for (int y = 0; y < NB; ++y) {
+      const int i = ty + 32 * x, c = tx + 32 * y;
+      if (i < l && c < l) C[(int64_t)c * l + i] = (float)a[x][y];
+    }
+}
+
+size_t chol_reg_lds_bytes(int l) { return ((size_t)l * (l + 1) / 2 + 4 * (size_t)l) * 8; }
+
+void launch_chol_inv_reg(hipStream_t s, const float* G, float* C, int l, double tol_rel) {
+  const size_t sh = chol_reg_lds_bytes(l);
+  switch ((l + 31) / 32) {
+    case 1: hipLaunchKernelGGL(chol_inv_reg_kernel<1>, dim3(1), dim3(kSmallThreads), sh, s, G, C, l, tol_rel); break;
+    case 2: hipLaunchKernelGGL(chol_inv_reg_kernel<2>, dim3(1), dim3(kSmallThreads), sh, s, G, C, l, tol_rel); break;
+    case 3: hipLaunchKernelGGL(chol_inv_reg_kernel<3>, dim3(1), dim3(kSmallThreads), sh, s, G, C, l, tol_rel); break;
+    case 4: hipLaunchKernelGGL(chol_inv_reg_kernel<4>, dim3(1), dim3(kSmallThreads), sh, s, G, C, l, tol_rel); break;
+    default: hipLaunchKernelGGL(chol_inv_reg_kernel<5>, dim3(1), dim3(kSmallThreads), sh, s, G, C, l, tol_rel); break;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // One-workgroup fp64 cyclic Jacobi eigensolver of a symmetric l x l matrix
 // (fp32 input S).  Rotations of one round act on disjoint index pairs from
@@ -323,6 +467,122 @@ __global__ __launch_bounds__(kSmallThreads) void jacobi_kernel(const float* S, d
   }
 }
 
+// The same eigensolver with A and V in LDS (l <= kLdsJacobi) and the row and
+// column updates on a 32 x 32 thread grid (no index division): same
+// rotations, same order per element, as jacobi_kernel.  Rows are l + 1
+// doubles apart, so the column updates (32 lanes down one column) fall in
+// distinct banks.
+constexpr int kLdsJacobi = 96;
+
+__global__ __launch_bounds__(kSmallThreads) void jacobi_lds_kernel(const float* S, double* evals, float* U, int l,
+                                                                   int max_sweeps) {
+  extern __shared__ double sm[];
+  double* A = sm;           // [l][l + 1]
+  double* V = sm + l * (l + 1);   // [l][l + 1]
+  __shared__ double cs[kMaxPairs], sn[kMaxPairs];
+  __shared__ int pp[kMaxPairs], qq[kMaxPairs];
+  __shared__ double red[2 * (kSmallThreads / 64)];  // per-wave sums (off, diagonal)
+  __shared__ int order[512];
+  const int tid = threadIdx.x;
+  const int ld = l + 1;
+  const int tx = tid & 31, ty = tid >> 5;
+  const int n = l + (l & 1);  // even number of players; index l (if any) is a dummy
+  const int npairs = n / 2;
+  for (int i = ty; i < l; i += 32)
+    for (int j = tx; j < l; j += 32) {
+      A[i * ld + j] = 0.5 * ((double)S[i * l + j] + (double)S[j * l + i]);
+      V[i * ld + j] = (i == j) ? 1.0 : 0.0;
+    }
+  __syncthreads();
+  for (int sweep = 0; sweep < max_sweeps; ++sweep) {
+    // convergence: off-diagonal mass vs diagonal mass
+    double off = 0.0, dia = 0.0;
+    for (int i = ty; i < l; i += 32)
+      for (int j = tx; j < l; j += 32) {
+        const double v = A[i * ld + j] * A[i * ld + j];
+        if (i == j) dia += v; else off += v;
+      }
+    for (int o = 32; o > 0; o >>= 1) {
+      off += __shfl_xor(off, o);
+      dia += __shfl_xor(dia, o);
+    }
+    if ((tid & 63) == 0) {
+      red[2 * (tid >> 6)] = off;
+      red[2 * (tid >> 6) + 1] = dia;
+    }
+    __syncthreads();
+    double off_t = 0.0, dia_t = 0.0;
+    for (int w = 0; w < kSmallThreads / 64; ++w) {
+      off_t += red[2 * w];
+      dia_t += red[2 * w + 1];
+    }
+    __syncthreads();
+    if (off_t <= 1e-30 * (dia_t + 1e-300) || off_t == 0.0) break;
+
+    for (int round = 0; round < n - 1; ++round) {
+      if (tid < npairs) {
+        int p, q;
+        if (tid == 0) { p = n - 1; q = round; }
+        else { p = (round + tid) % (n - 1); q = (round - tid + (n - 1)) % (n - 1); }
+        if (p > q) { const int t = p; p = q; q = t; }
+        double c = 1.0, sv = 0.0;
+        if (q < l) {
+          const double apq = A[p * ld + q];
+          if (fabs(apq) > 1e-300) {
+            const double theta = (A[q * ld + q] - A[p * ld + p]) / (2.0 * apq);
+            const double t = (theta >= 0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
+            c = 1.0 / sqrt(t * t + 1.0);
+            sv = t * c;
+          }
+        }
+        pp[tid] = p; qq[tid] = q; cs[tid] = c; sn[tid] = sv;
+      }
+      __syncthreads();
+      // rows: A <- J^T A
+      for (int k = ty; k < npairs; k += 32) {
+        const int p = pp[k], q = qq[k];
+        if (q >= l) continue;
+        const double c = cs[k], sv = sn[k];
+        for (int j = tx; j < l; j += 32) {
+          const double ap = A[p * ld + j], aq = A[q * ld + j];
+          A[p * ld + j] = c * ap - sv * aq;
+          A[q * ld + j] = sv * ap + c * aq;
+        }
+      }
+      __syncthreads();
+      // columns: A <- A J, V <- V J
+      for (int k = ty; k < npairs; k += 32) {
+        const int p = pp[k], q = qq[k];
+        if (q >= l) continue;
+        const double c = cs[k], sv = sn[k];
+        for (int i = tx; i < l; i += 32) {
+          const double ap = A[i * ld + p], aq = A[i * ld + q];
+          A[i * ld + p] = c * ap - sv * aq;
+          A[i * ld + q] = sv * ap + c * aq;
+          const double vp = V[i * ld + p], vq = V[i * ld + q];
+          V[i * ld + p] = c * vp - sv * vq;
+          V[i * ld + q] = sv * vp + c * vq;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // sort eigenvalues descending (rank by counting)
+  for (int i = tid; i < l; i += kSmallThreads) {
+    const double di = A[i * ld + i];
+    int rank = 0;
+    for (int j = 0; j < l; ++j) {
+      const double dj = A[j * ld + j];
+      rank += (dj > di) || (dj == di && j < i);
+    }
+    order[rank] = i;
+  }
+  __syncthreads();
+  for (int r = tid; r < l; r += kSmallThreads) evals[r] = A[order[r] * ld + order[r]];
+  for (int i = ty; i < l; i += 32)
+    for (int r = tx; r < l; r += 32) U[i * l + r] = (float)V[i * ld + order[r]];
+}
+
 // a_cat rows [0, r): a_cat[i][k] = bf16(P[k][i] / sqrt(sigma_i)), P = Bt U_r.
 __global__ void write_a_kernel(const float* P, const double* evals, uint16_t* a_cat, int64_t K, int r) {
   const int i = blockIdx.y;
@@ -427,8 +687,11 @@ hipError_t orth(hipStream_t s, float* Y, float* tmp, int64_t rows, int l, const 
     // G = Y^T Y
     hipError_t e = gemm(s, l, l, rows, Y, false, 1, l, Y, l, 1, G, l, 1, skinny_split(l, l, rows));
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(chol_inv_kernel, dim3(1), dim3(kSmallThreads), 0, s, G, C, at<double>(ws, E.dA),
-                       at<double>(ws, E.dB), l, 1e-10);
+    if (l <= kRegChol)
+      launch_chol_inv_reg(s, G, C, l, 1e-10);
+    else
+      hipLaunchKernelGGL(chol_inv_kernel, dim3(1), dim3(kSmallThreads), 0, s, G, C, at<double>(ws, E.dA),
+                         at<double>(ws, E.dB), l, 1e-10);
     // tmp = Y C, then copy back
     e = gemm(s, rows, l, l, Y, false, l, 1, C, l, 1, tmp, l, 1);
     if (e != hipSuccess) return e;
@@ -508,8 +771,12 @@ int encode_run(const EncodeParams& p) {
     CK(gemm(s, l, l, K, Z, false, 1, l, Z, l, 1, G, l, 1, skinny_split(l, l, K)));
     double* evals = at<double>(ws, E.evals);
     float* U = at<float>(ws, E.U);
-    hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(kSmallThreads), 0, s, G, at<double>(ws, E.dA),
-                       at<double>(ws, E.dB), evals, U, l, 30);
+    if (l <= kLdsJacobi)
+      hipLaunchKernelGGL(jacobi_lds_kernel, dim3(1), dim3(kSmallThreads), (size_t)2 * l * (l + 1) * 8, s, G, evals, U, l,
+                         30);
+    else
+      hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(kSmallThreads), 0, s, G, at<double>(ws, E.dA),
+                         at<double>(ws, E.dB), evals, U, l, 30);
     // P = Bt U_r (K x r) in Z2; S2 = Q U_r (N x r) in Q
     CK(gemm(s, K, r, l, Z, false, l, 1, U, l, 1, Z2, r, 1));
     CK(gemm(s, N, r, l, Y, false, l, 1, U, l, 1, Q, r, 1));
