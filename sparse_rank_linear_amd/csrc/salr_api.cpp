@@ -16,6 +16,7 @@ namespace {
 using salr::LargeFwdArgs;
 using salr::LowRankTArgs;
 using salr::SmallFwdArgs;
+using salr::StreamFwdArgs;
 
 constexpr int64_t kMaxK = int64_t(1) << 20;
 constexpr int64_t kMaxNK = int64_t(1) << 40;
@@ -70,6 +71,9 @@ struct FwdLayout {
   // few-row path
   int n_tiles, splits, range, vcap, r_tiles, r_pad_small, t_pieces, t_chunks;
   int vals_bytes, tl_bytes, bl_bytes;
+  // few-row streaming path (layers with more than one round of 16-row work)
+  bool stream;
+  int tiles_per_wg, svcap;
   // many-row path
   int64_t m_max;
   int r_pad_large;
@@ -115,6 +119,22 @@ FwdLayout fwd_layout(int64_t N, int64_t K, int32_t n_keep, int32_t r_cat, int64_
     const int64_t chunks = cdiv(K, 1024);
     L.t_chunks = (int)cdiv(chunks, 8);
     L.t_pieces = (int)cdiv(chunks, L.t_chunks);
+  }
+  // More 16-row work than one round of workgroups, with rows cut into
+  // column ranges: persistent streaming workgroups, one per CU, each with a
+  // run of whole row tiles (needs every T piece to have a workgroup and at
+  // most 64 lookup entries per row).  Whole-row layers keep the one-round
+  // kernel in several rounds: two of its workgroups per CU have both tiles'
+  // loads in flight at once, more than the streaming kernel's one chunk.
+  // So do layers whose tile runs would leave more than 15% of the CUs idle
+  // (the streaming kernel does not split a tile's K).
+  {
+    L.tiles_per_wg = (int)cdiv(L.n_tiles, kFillWgs);
+    const int64_t n_wg = cdiv(L.n_tiles, L.tiles_per_wg);
+    L.svcap = std::max(salr::fwd_small_vcap(std::min<int64_t>(salr::kChunk, n_keep), false), 65);
+    const bool fills = (int64_t)L.n_tiles * 100 >= (int64_t)L.tiles_per_wg * kFillWgs * 85;
+    L.stream = L.splits > 1 && fills && (int64_t)L.n_tiles * L.splits > kFillWgs && cdiv(K, 1024) <= 64 &&
+               (int64_t)L.r_tiles * L.t_pieces <= n_wg && salr::fwd_stream_lds_bytes(L.svcap) <= 160 * 1024;
   }
   L.m_max = std::max<int64_t>(M_max, 0);
   L.r_pad_large = (int)align_up((size_t)r_cat, 16);
@@ -250,7 +270,36 @@ int salr_linear_forward(const salr_layer_t* L, const uint16_t* X, int64_t M, uin
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   hipError_t err;
-  if (M <= kSmallM) {
+  if (M <= kSmallM && W.stream) {
+    StreamFwdArgs a{};
+    a.masks = L->masks;
+    a.values = L->values;
+    a.offsets = L->offsets;
+    a.b_cat = L->b_cat;
+    a.X = X;
+    a.Y = Y;
+    a.a_cat = L->a_cat;
+    a.tpiece = at<uint64_t>(ws, W.tsum);
+    a.tfinal = at<uint64_t>(ws, W.tfinal);
+    a.tcount = at<uint32_t>(ws, kCounterT);
+    a.N = L->N;
+    a.K = (int32_t)L->K;
+    a.n_keep = L->n_keep;
+    a.r_cat = L->r_cat;
+    a.M = (int32_t)M;
+    a.kw = (int32_t)cdiv(L->K, 64);
+    a.ng = (int32_t)cdiv(L->K, 1024);
+    a.n_tiles = W.n_tiles;
+    a.tiles_per_wg = W.tiles_per_wg;
+    a.vcap = W.svcap;
+    a.r_tiles = L->r_cat > 0 ? W.r_tiles : 0;
+    a.r_pad = L->r_cat > 0 ? W.r_pad_small : 0;
+    a.t_pieces = W.t_pieces;
+    a.t_chunks = W.t_chunks;
+    a.tickets = at<uint64_t>(ws, kCounterTickets);
+    a.err = at<uint32_t>(ws, kCounterSync + 8);
+    err = salr::launch_fwd_stream(a, s);
+  } else if (M <= kSmallM) {
     SmallFwdArgs a{};
     a.masks = L->masks;
     a.values = L->values;

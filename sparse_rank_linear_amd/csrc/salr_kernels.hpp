@@ -63,6 +63,40 @@ inline int fwd_small_vcap(int64_t cap, bool aligned_start) {
 }
 
 // ----------------------------------------------------------------------------
+// Forward, M <= 16, layers with more than one round of 16-row work: one
+// launch of persistent workgroups (one per CU), each streaming a run of
+// whole row tiles through two LDS buffers in chunks of kChunk columns; the
+// first r_tiles * t_pieces workgroups also compute the pieces of T (same
+// pieces, tagged words and counters as the one-round kernel).
+// ----------------------------------------------------------------------------
+constexpr int kChunk = 2048;  // columns per streamed chunk (a multiple of 1024)
+struct StreamFwdArgs {
+  const uint64_t* masks;
+  const uint16_t* values;
+  const uint32_t* offsets;
+  const uint16_t* b_cat;   // [N][r_cat]
+  const uint16_t* X;       // [M][K]
+  uint16_t* Y;             // [M][N]
+  const uint16_t* a_cat;   // [r_cat][K]
+  uint64_t* tpiece;        // [r_tiles * t_pieces][256] tagged fp32 pieces of T
+  uint64_t* tfinal;        // [r_tiles][128] tagged bf16 pairs: T per rank tile
+  uint32_t* tcount;        // [r_tiles] pieces published per rank tile
+  int64_t N;
+  int32_t K, n_keep, r_cat, M;
+  int32_t kw, ng;          // words / lookup entries per row (ng <= 64)
+  int32_t n_tiles;         // ceil(N/16)
+  int32_t tiles_per_wg;    // run of row tiles per workgroup
+  int32_t vcap;            // 16-byte LDS chunks per row per buffer
+  int32_t r_tiles, r_pad;  // ceil(r_cat/16); ranks rounded up to a multiple of 32
+  int32_t t_pieces, t_chunks;
+  uint64_t* tickets;
+  uint32_t* err;
+};
+hipError_t launch_fwd_stream(const StreamFwdArgs& a, hipStream_t s);
+// Dynamic LDS bytes of one streaming workgroup.
+size_t fwd_stream_lds_bytes(int vcap);
+
+// ----------------------------------------------------------------------------
 // Forward, M > 16: T = X * A_cat (bf16, [M][r_pad]) then the tiled
 // decode + MFMA kernel with the low-rank term as extra K steps.
 // ----------------------------------------------------------------------------

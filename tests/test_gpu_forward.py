@@ -27,6 +27,17 @@ CASES = [
     (64, 9216, 4608, 8, (32,), (1, 16, 20)),      # T pieces of 2048 columns, ranges
     (16, 1024, 512, 0, (200,), (4, 16)),          # one workgroup computes 13 T pieces
     (30, 64, 32, 0, (256,), (16,)),               # the largest r_cat, tiny K
+    # more than one round of 16-row work (> 256 tiles x ranges): whole rows
+    # in several rounds of the one-round kernel (ragged last tile, r_cat not
+    # a multiple of 8), and ranged rows on the streaming kernel
+    (4200, 2056, 1028, 8, (4,), (1, 16)),
+    (4110, 1000, 500, 0, (), (3, 16)),
+    (4100, 1024, 0, 0, (8,), (2,)),               # everything pruned
+    (1100, 16384, 8192, 0, (40,), (1, 16)),       # ranges in several rounds (too few tiles to stream)
+    (3500, 8200, 4100, 0, (12,), (1, 16)),        # streaming: 5 chunks (the last of 8 columns), r_cat 12
+    (7000, 4104, 2052, 0, (40,), (1, 16)),        # streaming: two tiles per workgroup, 3 chunks
+    (3520, 6144, 6144, 0, (16,), (16,)),          # streaming, nothing pruned: whole chunks of values
+    (3600, 5120, 0, 0, (), (5,)),                 # streaming, everything pruned, no adapters
 ]
 
 
