@@ -73,15 +73,6 @@ __device__ __forceinline__ u32x4_t load_x_frag(const uint16_t* X, int M, int K, 
   return zero_u4();
 }
 
-// Workgroup barrier that waits for the wave's LDS operations but not for its
-// outstanding global ones (__syncthreads waits for both).
-__device__ __forceinline__ void lds_barrier() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 // Sum the waves' accumulators into wave 0 (fixed order).  Other waves return
 // false and must leave; wave 0 returns true with the total.
 __device__ __forceinline__ bool reduce_waves(f32x4_t& acc, f32x4_t* red, int wave, int lane) {

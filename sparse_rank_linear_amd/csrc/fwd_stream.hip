@@ -214,9 +214,9 @@ __global__ __launch_bounds__(kSThreads) void fwd_stream_kernel(StreamFwdArgs a) 
       }
     }
     // waves' sums in the second buffer's values area (no chunk there yet)
-    __syncthreads();
+    lds_barrier();
     if (wave > 0) red[(wave - 1) * 64 + lane] = t;
-    __syncthreads();
+    lds_barrier();
     if (wave == 0) {
 #pragma unroll
       for (int w = 0; w < kSWaves - 1; ++w) t += red[w * 64 + lane];
@@ -284,7 +284,10 @@ __global__ __launch_bounds__(kSThreads) void fwd_stream_kernel(StreamFwdArgs a) 
     const int t = t_begin + q / nc, c = q % nc;
     const bool tile_end = c == nc - 1;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of chunk q (and everything before) have landed
-    __syncthreads();
+    // (LDS-only barriers throughout: __syncthreads would also wait for the
+    // next chunk's loads, which must stay in flight across the tile-end and
+    // T-piece barriers)
+    lds_barrier();
     if (q + 1 < n_q) issue(q + 1, bnxt, bsel ^ 1, xn);
 
     // decode + multiply this wave's steps of chunk q
@@ -351,7 +354,7 @@ __global__ __launch_bounds__(kSThreads) void fwd_stream_kernel(StreamFwdArgs a) 
           if (lane == 0) H.tag = tag;
         }
       }
-      __syncthreads();
+      lds_barrier();
       // (T is read once, at the first tile's end; its loads queue behind the
       // next chunk's, a one-time wait)
       if (!t_have) {
@@ -367,7 +370,7 @@ __global__ __launch_bounds__(kSThreads) void fwd_stream_kernel(StreamFwdArgs a) 
       if (wave < n_chunks32 && a.r_cat > 0) acc = mfma_16x16x32(bc, tv, acc);
       f32x4_t* const rsum = reinterpret_cast<f32x4_t*>(bcur + (size_t)kSRows * kCMaskRow * 8);
       if (wave > 0) rsum[(wave - 1) * 64 + lane] = acc;
-      __syncthreads();
+      lds_barrier();
       if (wave == 0) {
 #pragma unroll
         for (int w = 0; w < kSWaves - 1; ++w) acc += rsum[w * 64 + lane];

@@ -184,6 +184,16 @@ __device__ __forceinline__ uint32_t tag_from_ticket(uint64_t* tickets, uint64_t 
   return (uint32_t)(drawn >> 32) + 1u;
 }
 
+// Workgroup barrier that waits for the wave's LDS operations but not for its
+// outstanding global ones (__syncthreads waits for both, which would also
+// wait for direct-to-LDS loads meant to stay in flight across it).
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 __device__ __forceinline__ u32x4_t load16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 __device__ __forceinline__ u32x4_t zero_u4() { return u32x4_t{0u, 0u, 0u, 0u}; }
 

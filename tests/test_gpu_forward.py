@@ -38,6 +38,8 @@ CASES = [
     (7000, 4104, 2052, 0, (40,), (1, 16)),        # streaming: two tiles per workgroup, 3 chunks
     (3520, 6144, 6144, 0, (16,), (16,)),          # streaming, nothing pruned: whole chunks of values
     (3600, 5120, 0, 0, (), (5,)),                 # streaming, everything pruned, no adapters
+    (4096, 520, 260, 0, (8,), (1, 16)),           # streaming, one-chunk tiles
+    (4000, 3000, 1500, 8, (8,), (7, 16)),         # streaming, last chunk ends inside a bitmap word
 ]
 
 
