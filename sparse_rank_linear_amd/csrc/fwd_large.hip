@@ -71,6 +71,20 @@ __device__ __forceinline__ void dma_x_tile(u32x4_t* xt, const uint16_t* X, int M
   }
 }
 
+// The same loads from per-thread byte offsets into X (row clamped, chunk
+// column within the tile) formed once, plus the tile's column offset: a few
+// instructions per tile instead of a 64-bit multiply per load.  Only for
+// tiles wholly inside K (the last tile of a ragged K takes dma_x_tile).
+template <class C>
+__device__ __forceinline__ void dma_x_tile_fast(u32x4_t* xt, const uint16_t* X, int k0, const uint32_t (&xoff)[C::XDMA],
+                                                int wave) {
+  const char* const xb = reinterpret_cast<const char*>(X + k0);
+#pragma unroll
+  for (int j = 0; j < C::XDMA; ++j)
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(xb + xoff[j]),
+                                     reinterpret_cast<uint32_t*>(xt + (C::XDMA * wave + j) * 64), 16, 0, 0);
+}
+
 template <int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN) void fwd_large_kernel(LargeFwdArgs a) {
   using C = Cfg<WM, WN>;
@@ -107,6 +121,20 @@ __global__ __launch_bounds__(64 * WM * WN) void fwd_large_kernel(LargeFwdArgs a)
 
   if (tid < 16) lut[tid] = nibble_selectors(tid);
 
+  // byte offsets of this thread's X tile loads (see dma_x_tile_fast; used
+  // when M * K * 2 < 2^32)
+  uint32_t xoff[C::XDMA];
+#pragma unroll
+  for (int j = 0; j < C::XDMA; ++j) {
+    const int row = 8 * (C::XDMA * wave + j) + (lane >> 3);
+    const int chunk = (lane & 7) ^ (row & 7);
+    xoff[j] = ((uint32_t)min(m0 + row, a.M - 1) * (uint32_t)a.K + 8u * (uint32_t)chunk) * 2u;
+  }
+  const auto load_x_tile = [&](u32x4_t* xt, int kt) {
+    if (a.x_off32 && (kt + 1) * 64 <= a.K) dma_x_tile_fast<C>(xt, a.X, kt * 64, xoff, wave);
+    else dma_x_tile<C>(xt, a.X, a.M, a.K, m0, kt * 64, wave, lane);
+  };
+
   // this thread's decode row and column part
   const int drow = tid / C::TPR, dpart = tid % C::TPR;
   const int64_t grow = n0 + drow;
@@ -120,29 +148,27 @@ __global__ __launch_bounds__(64 * WM * WN) void fwd_large_kernel(LargeFwdArgs a)
 
   // Stage the packed values of one tile of this row: chunks covering
   // [row_base + run, + popcount(mask)); returns how many.  The loads are
-  // unconditional (from clamped addresses; chunk 0 exists even for an empty
-  // layer thanks to the values buffer's tail padding) and their registers
-  // are not touched until stored, so the compiler counts them exactly and
-  // waits only at the store.
+  // unconditional: the first chunk starts at most at the end of the values,
+  // and the 9 chunks read from there stay inside the values buffer's
+  // 256-byte tail padding.  Their registers are not touched until stored,
+  // so the compiler counts them exactly and waits only at the store.
   auto load_v = [&](u32x4_t (&r)[C::VCH], uint32_t run, uint64_t mk) -> int {
     const int64_t va = row_base + run;
     const int cnt = __popcll(mk);
     const int64_t q0 = va >> 3;
     const int64_t q1 = min((va + cnt + 7) >> 3, a.vchunks);
+    const uint16_t* const vq = a.values + q0 * 8;
 #pragma unroll
-    for (int u = 0; u < C::VCH; ++u) {
-      const int ch = dpart + C::TPR * u;
-      int64_t q = q0 + ch < a.vchunks ? q0 + ch : a.vchunks - 1;
-      q = q > 0 ? q : 0;
-      r[u] = load16(a.values + q * 8);
-    }
+    for (int u = 0; u < C::VCH; ++u) r[u] = load16(vq + (dpart + C::TPR * u) * 8);
     return cnt ? (int)(q1 - q0) : 0;
   };
-  auto store_v = [&](uint32_t* vb, const u32x4_t (&r)[C::VCH], int n) {
+  // (chunks past the row's count hold other values: the decode never
+  // selects them, a zero selector byte stands for every pruned column)
+  auto store_v = [&](uint32_t* vb, const u32x4_t (&r)[C::VCH], int) {
 #pragma unroll
     for (int u = 0; u < C::VCH; ++u) {
       const int ch = dpart + C::TPR * u;
-      if (ch < 9) *reinterpret_cast<u32x4_t*>(&vb[drow * kVRow + ch * 4]) = ch < n ? r[u] : zero_u4();
+      if (ch < 9) *reinterpret_cast<u32x4_t*>(&vb[drow * kVRow + ch * 4]) = r[u];
     }
   };
   // Decode this thread's columns of one tile into dense bf16 in LDS.
@@ -202,7 +228,7 @@ __global__ __launch_bounds__(64 * WM * WN) void fwd_large_kernel(LargeFwdArgs a)
   uint64_t mk1 = mask_ok(mask_raw(kt0 + 1), kt0 + 1);
   uint64_t mk2raw = mask_raw(kt0 + 2);
   {
-    dma_x_tile<C>(xl0, a.X, a.M, a.K, m0, kt0 * 64, wave, lane);
+    load_x_tile(xl0, kt0);
     u32x4_t vr[C::VCH];
     int n = load_v(vr, run0, mk0);
     store_v(vl0, vr, n);
@@ -220,7 +246,7 @@ __global__ __launch_bounds__(64 * WM * WN) void fwd_large_kernel(LargeFwdArgs a)
   // and the decode builds tile kt+1; the values land in the buffer tile kt's
   // values just left.  (Unrolled by two so that every buffer is named.)
   auto step = [&](int kt, u32x4_t* xc, u32x4_t* xn, u32x4_t* wc, u32x4_t* wn_, uint32_t* vc, uint32_t* vn) {
-    if (kt + 1 < nk) dma_x_tile<C>(xn, a.X, a.M, a.K, m0, (kt + 1) * 64, wave, lane);
+    if (kt + 1 < nk) load_x_tile(xn, kt + 1);
     const uint64_t mk2 = mask_ok(mk2raw, kt + 2);
     const uint32_t run2 = run1 + (uint32_t)__popcll(mk1);
     u32x4_t vr[C::VCH];

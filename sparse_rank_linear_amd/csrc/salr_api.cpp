@@ -375,6 +375,7 @@ int salr_linear_forward(const salr_layer_t* L, const uint16_t* X, int64_t M, uin
     a.kt_per = (int32_t)(cdiv(cdiv(nk, a.ksplit), 8) * 8);  // (whole groups of 8 tiles)
     a.ksplit = (int32_t)cdiv(nk, a.kt_per);
     a.ypart = at<float>(ws, W.ylarge);
+    a.x_off32 = M * L->K * 2 < (int64_t(1) << 32) ? 1 : 0;
     err = salr::launch_fwd_large(a, s);
   }
   return err == hipSuccess ? SALR_OK : SALR_ERR_HIP;

@@ -128,6 +128,7 @@ struct LargeFwdArgs {
   int32_t ng;
   int32_t ksplit, kt_per;
   float* ypart;
+  int32_t x_off32;         // 1 when M * K * 2 < 2^32 (X tile loads from 32-bit offsets)
 };
 hipError_t launch_fwd_large(const LargeFwdArgs& a, hipStream_t s);
 // Output tiles of the many-row kernel and the K splits it takes for M rows
