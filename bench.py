@@ -24,6 +24,14 @@ Printed JSON fields beyond the common contract:
   prefill       a many-token case (11008x4096, 2048 tokens) against the bf16
                 matrix-core peak (dense-equivalent flops), for context
   encode        wall time of salr_encode for the headline layer
+
+    python bench.py --configs
+
+prints instead one JSON line per workload and token count of the synthetic
+workload table (sparse_rank_linear_amd/synth.py): the layer encoded on the
+GPU, enough rotating copies to exceed the Infinity Cache, the graph-replayed
+forward time, compressed-weight GB/s and the fraction of the roofline that
+bounds the regime (HBM for <= 16 tokens, bf16 matrix cores above).
 """
 
 from __future__ import annotations
@@ -123,6 +131,44 @@ def measure_decode(layers, X, ws, steps, warmup):
     return _time_replay(g) / steps
 
 
+def run_configs(dev):
+    """One JSON line per (workload, token count) of the synthetic table."""
+    import torch
+    import sparse_rank_linear_amd as srl
+    from sparse_rank_linear_amd import synth
+
+    for name, wl in synth.WORKLOADS.items():
+        inp = synth.make_inputs(wl, with_x=False)
+        W = _dev_bits(inp.W, dev)
+        As = [_dev_bits(a, dev) for a in inp.lora_A]
+        Bs = [_dev_bits(b, dev) for b in inp.lora_B]
+        layer, _ = srl.encode(W, wl.n_keep, wl.r_svd, As, Bs)  # (first call: warm-up)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        layer, _ = srl.encode(W, wl.n_keep, wl.r_svd, As, Bs)
+        torch.cuda.synchronize()
+        encode_ms = (time.perf_counter() - t0) * 1e3
+        del W, As, Bs
+        cbytes = layer.compressed_bytes()
+        copies = max(2, -(-600_000_000 // cbytes))
+        layers = [layer] + [layer.clone() for _ in range(copies - 1)]
+        tokens = sorted({1, 16, wl.M}) if wl.M <= 16 else [wl.M]
+        ws = srl.forward_workspace(layer, max(tokens))
+        for M in tokens:
+            X = _dev_bits(synth.make_x(wl.K, M, seed=11), dev)
+            t = measure_decode(layers, X, ws, 32, 4)
+            rec = {"workload": name, "N": wl.N, "K": wl.K, "n_keep": wl.n_keep, "r_cat": wl.r_cat, "M": M,
+                   "us": round(t * 1e6, 2), "compressed_GBs": round(cbytes / t / 1e9, 1),
+                   "tflops_dense_equiv": round(2 * M * wl.N * wl.K / t / 1e12, 2), "encode_ms": round(encode_ms, 1)}
+            if M <= 16:
+                rec["hbm_frac"] = round((cbytes + 2 * M * (wl.K + wl.N)) / t / 1e9 / HBM_PEAK_GBS, 4)
+            else:
+                rec["mfma_frac_dense_equiv"] = round(2 * M * wl.N * wl.K / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+            print(json.dumps(rec), flush=True)
+        del layers, layer, ws
+        torch.cuda.empty_cache()
+
+
 def cpu_baseline(wl, budget_s: float = 12.0):
     """The oracle's float64 forward on the headline shape, on host cores."""
     from oracle import salr as osl
@@ -166,6 +212,8 @@ def main():
     ap.add_argument("--steps", type=int, default=320)
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--no-extra", action="store_true", help="headline line only (no sweep/prefill/cpu)")
+    ap.add_argument("--configs", action="store_true",
+                    help="time every workload of the synthetic table instead of the headline line")
     ap.add_argument("--probe", choices=["copy"], default=None,
                     help="run a plain 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -188,6 +236,10 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"probe": "copy", "bytes_read_per_launch": a.numel() * 2,
                           "bytes_written_per_launch": a.numel() * 2, "launches": 5}))
+        return
+
+    if args.configs:
+        run_configs(dev)
         return
 
     wl = synth.WORKLOADS["llama7b_attn_4096"]
