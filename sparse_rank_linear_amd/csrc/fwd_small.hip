@@ -26,8 +26,8 @@
 //     their latencies overlap;
 //   * range partials of one row tile are combined by the last workgroup to
 //     finish, in range order (results do not depend on scheduling);
-//   * T = X A_cat is cut into pieces of 16 ranks x (a multiple of 1024)
-//     columns.  Extra workgroups at the front of the grid each compute one
+//   * T = X A_cat is cut into pieces of 16 ranks x (a multiple of 512 or
+//     1024) columns.  Extra workgroups at the front of the grid each compute one
 //     piece and nothing else, so T is complete long before any weight tile
 //     needs it; the last producer of a rank tile sums its pieces in a fixed
 //     order.  After its decode every weight workgroup reads T for its share
@@ -63,7 +63,12 @@ struct alignas(16) Lds {
   uint64_t masks[kRows * kMaskRowWords];
   uint32_t tag;
 };
-constexpr int kPieceSteps = 1024 / 32 / kWaves;  // steps per wave of a T piece's 1024-column chunk
+// T pieces are cut into chunks of piece_cols<kOneRound> columns (see the
+// producer section); steps per wave of one chunk:
+template <bool kOneRound>
+constexpr int piece_cols() { return kOneRound ? 512 : 1024; }
+template <bool kOneRound>
+constexpr int piece_steps() { return piece_cols<kOneRound>() / 32 / kWaves; }
 constexpr int kFinBatch = 4;                      // pieces requested together when finishing T
 constexpr int kMaxLoadRows = kRows / kWaves;      // rows per load-issuing wave
 static_assert(sizeof(Lds) % 16 == 0, "values area must stay 16-byte aligned");
@@ -262,7 +267,10 @@ void fwd_small_kernel(SmallFwdArgs a) {
 
   // ---------------- T pieces (producer workgroups)
   // Piece p = (rank tile j, K range kp) is T^T[16 ranks][16 tokens] summed
-  // over t_chunks * 1024 columns; producer workgroup p computes piece p with
+  // over t_chunks chunks of piece_cols columns (512 when every weight
+  // workgroup is resident at once: smaller pieces, spread over more
+  // producers, hold up the weight loads of the CUs they share less; 1024
+  // otherwise); producer workgroup p computes piece p with
   // all its waves (partials summed in LDS in wave order).  Wave 0 publishes
   // it as tagged words (lane (i, g) holds ranks 16j + 4g + e of token i) and
   // counts it; the producer that completes a rank tile's count sums the
@@ -281,15 +289,16 @@ void fwd_small_kernel(SmallFwdArgs a) {
     const int rank = 16 * j + i;
     f32x4_t t = zero4();
     for (int ch = 0; ch < a.t_chunks; ++ch) {
-      u32x4_t pav[kPieceSteps], pxv[kPieceSteps];
+      constexpr int kPS = piece_steps<kOneRound>();
+      u32x4_t pav[kPS], pxv[kPS];
 #pragma unroll
-      for (int q = 0; q < kPieceSteps; ++q) {
-        const int col = (kp * a.t_chunks + ch) * 1024 + 32 * (wave * kPieceSteps + q) + 8 * g;
+      for (int q = 0; q < kPS; ++q) {
+        const int col = (kp * a.t_chunks + ch) * piece_cols<kOneRound>() + 32 * (wave * kPS + q) + 8 * g;
         pav[q] = (rank < a.r_cat && col < a.K) ? load16(a.a_cat + (size_t)rank * a.K + col) : zero_u4();
         pxv[q] = load_x_frag(a.X, a.M, a.K, i, col);
       }
 #pragma unroll
-      for (int q = 0; q < kPieceSteps; ++q) t = mfma_16x16x32(pav[q], pxv[q], t);
+      for (int q = 0; q < kPS; ++q) t = mfma_16x16x32(pav[q], pxv[q], t);
     }
     if (!reduce_waves(t, red, wave, lane)) return;
     resolve_tag();

@@ -136,6 +136,13 @@ FwdLayout fwd_layout(int64_t N, int64_t K, int32_t n_keep, int32_t r_cat, int64_
     L.stream = L.splits > 1 && fills && (int64_t)L.n_tiles * L.splits > kFillWgs && cdiv(K, 1024) <= 64 &&
                (int64_t)L.r_tiles * L.t_pieces <= n_wg && salr::fwd_stream_lds_bytes(L.svcap) <= 160 * 1024;
   }
+  // The one-round few-row kernel (every weight workgroup resident at once)
+  // cuts its T pieces from 512-column chunks, at most 16 per rank tile.
+  if (!L.stream && (int64_t)L.n_tiles * L.splits <= kFillWgs) {
+    const int64_t pchunks = cdiv(K, 512);
+    L.t_chunks = (int)cdiv(pchunks, 16);
+    L.t_pieces = (int)cdiv(pchunks, L.t_chunks);
+  }
   L.m_max = std::max<int64_t>(M_max, 0);
   L.r_pad_large = (int)align_up((size_t)r_cat, 16);
 
