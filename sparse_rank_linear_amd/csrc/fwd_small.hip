@@ -282,8 +282,9 @@ void fwd_small_kernel(SmallFwdArgs a) {
     if (tid == 0) drawn = draw_ticket(a.tickets, blockIdx.x, n_wgs);
     // With all weight workgroups resident, a producer shares its CU with one
     // of them, whose loads it would otherwise delay while they are issued:
-    // start about 1 us later (T is needed only after the decode).
-    if (kOneRound) __builtin_amdgcn_s_sleep(40);
+    // start later (psleep x 64 clocks; T is needed only after the decode).
+    if (kOneRound)
+      for (int k = 0; k < a.psleep; ++k) __builtin_amdgcn_s_sleep(1);
     const int piece = c;
     const int j = piece / a.t_pieces, kp = piece % a.t_pieces;
     const int rank = 16 * j + i;

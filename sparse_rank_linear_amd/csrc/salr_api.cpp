@@ -336,6 +336,9 @@ int salr_linear_forward(const salr_layer_t* L, const uint16_t* X, int64_t M, uin
     a.vals_bytes = W.vals_bytes;
     a.tl_bytes = W.tl_bytes;
     a.bl_bytes = W.bl_bytes;
+    // (about 1 us with up to 48 producers; with more, T is on the critical
+    // path and they start at once: measured on 4096 x 4096 at r_cat 80 / 112)
+    a.psleep = W.r_tiles * W.t_pieces <= 48 ? 40 : 0;
     a.tickets = at<uint64_t>(ws, kCounterTickets);
     a.err = at<uint32_t>(ws, kCounterSync + 8);
     a.ycount = at<uint32_t>(ws, kCounterY);

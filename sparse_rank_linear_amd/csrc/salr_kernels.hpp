@@ -42,6 +42,7 @@ struct SmallFwdArgs {
   int32_t vals_bytes;      // LDS bytes of the values area
   int32_t tl_bytes;        // LDS bytes of the T operands (r_pad / 32 chunks x 1 KB)
   int32_t bl_bytes;        // LDS bytes of the B_cat rows (16 * r_cat * 2, rounded up to 16)
+  int32_t psleep;          // one-round launches: producers' start delay in units of 64 clocks
   uint64_t* tickets;       // {count, epoch} ticket words of the launch tags
   uint32_t* err;           // set nonzero when a wait times out
   uint32_t* ycount;        // [n_tiles]
