@@ -242,6 +242,37 @@ def forward_rows(X_bits, masks, values, K: int, A_cat_bits, B_cat_bits, rows) ->
     return X @ Ws.T + (X @ A) @ B
 
 
+# ---------------------------------------------------------------------------
+# Multi-projection fusion.  [summary] Methodology 3 runs every adapter as one
+# low-rank product on the shared input; projections that share an input
+# (q/k/v, gate/up) are fused the same way: W_s rows stacked, adapter ranks
+# stacked, each projection's up-projection kept on its own ranks only.
+# ---------------------------------------------------------------------------
+
+def fuse(parts):
+    """One encoding from `parts` (each with masks, values, offsets, A_cat
+    [K x r_p], B_cat [r_p x N_p]; all with the same K and n_keep): masks,
+    values and offsets stacked along N, A_cat = [A_0 | A_1 | ...] and B_cat
+    block diagonal (B_p at rows R_p.., columns N_0 + ... + N_{p-1}..).
+    Returns a dict with those five arrays."""
+    parts = list(parts)
+    Ns = [p.masks.shape[0] for p in parts]
+    ranks = [p.A_cat.shape[1] for p in parts]
+    B = np.zeros((sum(ranks), sum(Ns)), dtype=np.uint16)
+    r0 = n0 = 0
+    for p, n, r in zip(parts, Ns, ranks):
+        B[r0:r0 + r, n0:n0 + n] = p.B_cat
+        r0 += r
+        n0 += n
+    return {
+        "masks": np.concatenate([p.masks for p in parts], axis=0),
+        "values": np.concatenate([p.values for p in parts], axis=0),
+        "offsets": np.concatenate([p.offsets for p in parts], axis=0),
+        "A_cat": np.concatenate([p.A_cat for p in parts], axis=1),
+        "B_cat": B,
+    }
+
+
 def max_rel_err(Y_hat, Y) -> float:
     """Error metric for Y: max_ij |Y_hat - Y| / max(|Y_ij|, rms(Y)).
     A pure elementwise relative error is dominated by outputs that happen to

@@ -334,3 +334,48 @@ def test_error_metric():
     Yh = Y.copy()
     Yh[0, 1] *= 1.01
     assert abs(osl.max_rel_err(Yh, Y) - 0.01) < 1e-12
+
+
+# ------------------------------------------------------- fusion ----------
+
+def test_fused_forward_equals_the_parts():
+    """A fused encoding computes every part: its forward is the column-wise
+    concatenation of the parts' separate forwards (different code: one
+    product over stacked arrays against one product per part)."""
+    rng = np.random.default_rng(11)
+    K, n_keep, M = 192, 97, 5
+    parts = []
+    for N, r_svd, loras in ((40, 3, (2,)), (16, 0, (5, 1)), (24, 2, ())):
+        W = _rand_bits(rng, (N, K))
+        As = [_rand_bits(rng, (q, K), 0.01) for q in loras]
+        Bs = [_rand_bits(rng, (N, q), 0.01) for q in loras]
+        parts.append(osl.encode(W, n_keep, r_svd, As, Bs))
+    f = osl.fuse(parts)
+    X = _rand_bits(rng, (M, K), 1.0)
+    Y = osl.forward(X, f["masks"], f["values"], K, f["A_cat"], f["B_cat"])
+    ref = np.concatenate([osl.forward(X, p.masks, p.values, K, p.A_cat, p.B_cat) for p in parts], axis=1)
+    assert Y.shape == (M, 80)
+    np.testing.assert_allclose(Y, ref, rtol=1e-12, atol=1e-12)
+    # the lookup table of the stack is the stack of the tables
+    assert np.array_equal(f["offsets"][40:56], parts[1].offsets)
+    # off-diagonal blocks of B_cat hold nothing (ranks 5, 6 and 2 per part)
+    B = f["B_cat"]
+    assert B.shape == (13, 80)
+    assert not B[0:5, 40:].any() and not B[5:11, :40].any() and not B[5:11, 56:].any() and not B[11:, :56].any()
+
+
+def test_planted_misplaced_block_is_caught():
+    """A fusion that puts every part's B block at rank 0 (a plausible
+    off-by-offset mistake) fails the forward pin above."""
+    rng = np.random.default_rng(12)
+    K, n_keep = 128, 64
+    parts = [osl.encode(_rand_bits(rng, (N, K)), n_keep, r) for N, r in ((16, 2), (16, 3))]
+    f = osl.fuse(parts)
+    bad = f["B_cat"].copy()
+    bad[:] = 0
+    bad[0:2, 0:16] = parts[0].B_cat
+    bad[0:3, 16:32] = parts[1].B_cat
+    X = _rand_bits(rng, (3, K), 1.0)
+    ref = np.concatenate([osl.forward(X, p.masks, p.values, K, p.A_cat, p.B_cat) for p in parts], axis=1)
+    Y_bad = osl.forward(X, f["masks"], f["values"], K, f["A_cat"], bad)
+    assert not np.allclose(Y_bad, ref, rtol=1e-6, atol=1e-9)
