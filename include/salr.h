@@ -181,6 +181,35 @@ int salr_encode(const uint16_t* W, int64_t N, int64_t K, int32_t n_keep,
 int salr_linear_forward(const salr_layer_t* L, const uint16_t* X, int64_t M,
                         uint16_t* Y, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * salr_fuse_layers - one encoded layer from n_parts encoded layers that read
+ * the same input (q/k/v, or gate/up): a single forward call on the result
+ * computes every part.  This applies the pages' single low-rank product on
+ * a shared input (summary, Methodology 3) across projections:
+ *   masks, values, offsets  rows of part 0, then part 1, ... (along N);
+ *   a_cat                   ranks of part 0, then part 1, ... (along r_cat);
+ *   b_cat                   block diagonal: row n of part p holds part p's
+ *                           coefficients at columns [R_p, R_p + r_cat_p),
+ *                           R_p = r_cat_0 + ... + r_cat_{p-1}, and 0
+ *                           elsewhere.
+ * A forward on the fused layer returns Y = [Y_0 | Y_1 | ...] along N (part
+ * p's outputs are columns [N_0 + ... + N_{p-1}, + N_p)).  The zero blocks of
+ * b_cat are real bytes and multiplies: the price of one launch instead of
+ * n_parts.
+ *
+ * parts    host array of n_parts (>= 1) host pointers to encoded layers, all
+ *          with the same K and n_keep.
+ * out      host pointer; the caller fills N = sum N_p, K, n_keep,
+ *          r_cat = sum r_cat_p (<= 256) and the five buffer pointers, sized
+ *          by salr_query_sizes(N, K, n_keep, 0, r_cat, ...); its buffers must
+ *          not overlap any part's.  They are overwritten.
+ * Asynchronous on `stream` (device-to-device copies and one small kernel
+ * per part).  Errors: INVALID_ARG (nulls, alignment, mismatched K or n_keep,
+ * sums that disagree with `out`, limits), HIP.
+ */
+int salr_fuse_layers(const salr_layer_t* const* parts, int32_t n_parts,
+                     salr_layer_t* out, void* stream);
+
 /* Static English text for a status code (never NULL). */
 const char* salr_status_string(int status);
 

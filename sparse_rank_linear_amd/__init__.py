@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     SalrLayer,
     encode,
     forward_workspace,
+    fuse,
     lib,
     linear_forward,
     query_sizes,
@@ -23,6 +24,6 @@ from .binding import (  # noqa: F401
 )
 
 __all__ = [
-    "EXPORTS", "LIB_PATH", "SalrError", "SalrLayer", "encode", "forward_workspace", "lib", "linear_forward",
+    "EXPORTS", "LIB_PATH", "SalrError", "SalrLayer", "encode", "forward_workspace", "fuse", "lib", "linear_forward",
     "query_sizes", "workspace",
 ]

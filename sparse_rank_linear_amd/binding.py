@@ -30,6 +30,7 @@ EXPORTS = (
     "salr_query_sizes",
     "salr_encode",
     "salr_linear_forward",
+    "salr_fuse_layers",
     "salr_status_string",
     "salr_version",
 )
@@ -92,6 +93,9 @@ def _lib():
         lib.salr_linear_forward.argtypes = [C.POINTER(salr_layer_t), C.c_void_p, C.c_int64, C.c_void_p,
                                             C.c_void_p, C.c_size_t, C.c_void_p]
         lib.salr_linear_forward.restype = C.c_int
+        lib.salr_fuse_layers.argtypes = [C.POINTER(C.POINTER(salr_layer_t)), C.c_int32, C.POINTER(salr_layer_t),
+                                         C.c_void_p]
+        lib.salr_fuse_layers.restype = C.c_int
         lib.salr_status_string.argtypes = [C.c_int]
         lib.salr_status_string.restype = C.c_char_p
         lib.salr_version.argtypes = []
@@ -297,3 +301,22 @@ def linear_forward(layer: SalrLayer, X, Y=None, ws=None, stream=None):
                                     C.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), _stream_ptr(stream))
     _check(st, "salr_linear_forward")
     return Y
+
+
+def fuse(layers, stream=None) -> SalrLayer:
+    """One encoded layer computing every layer in `layers` (same K and
+    n_keep) in a single forward: rows stacked along N, ranks stacked along
+    r_cat, B_cat block diagonal (include/salr.h, salr_fuse_layers)."""
+    layers = list(layers)
+    if not layers:
+        raise ValueError("fuse needs at least one layer")
+    K, n_keep = layers[0].K, layers[0].n_keep
+    N = sum(l.N for l in layers)
+    r_cat = sum(l.r_cat for l in layers)
+    out = SalrLayer.empty(N, K, n_keep, 0, r_cat, layers[0].masks.device)
+    descs = [l.descriptor() for l in layers]
+    arr = (C.POINTER(salr_layer_t) * len(descs))(*[C.pointer(d) for d in descs])
+    od = out.descriptor()
+    st = _lib().salr_fuse_layers(arr, len(descs), C.byref(od), _stream_ptr(stream))
+    _check(st, "salr_fuse_layers")
+    return out

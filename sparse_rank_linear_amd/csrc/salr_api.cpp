@@ -174,6 +174,53 @@ T* at(void* base, size_t off) {
 
 extern "C" {
 
+int salr_fuse_layers(const salr_layer_t* const* parts, int32_t n_parts, salr_layer_t* out, void* stream) {
+  if (!parts || !out || n_parts < 1) return SALR_ERR_INVALID_ARG;
+  int64_t N = 0;
+  int32_t r_cat = 0;
+  for (int32_t p = 0; p < n_parts; ++p) {
+    const salr_layer_t* L = parts[p];
+    if (!L || !dims_ok(L->N, L->K, L->n_keep, L->r_cat)) return SALR_ERR_INVALID_ARG;
+    if (L->K != out->K || L->n_keep != out->n_keep) return SALR_ERR_INVALID_ARG;
+    if (!L->masks || !L->offsets || (L->n_keep > 0 && !L->values)) return SALR_ERR_INVALID_ARG;
+    if (L->r_cat > 0 && (!L->a_cat || !L->b_cat)) return SALR_ERR_INVALID_ARG;
+    const void* ptrs[] = {L->masks, L->values, L->offsets, L->a_cat, L->b_cat};
+    for (const void* q : ptrs)
+      if (q && !aligned16(q)) return SALR_ERR_INVALID_ARG;
+    N += L->N;
+    r_cat += L->r_cat;
+    if (r_cat > kMaxRank) return SALR_ERR_INVALID_ARG;
+  }
+  if (out->N != N || out->r_cat != r_cat || !dims_ok(N, out->K, out->n_keep, r_cat)) return SALR_ERR_INVALID_ARG;
+  if (!out->masks || !out->offsets || (out->n_keep > 0 && !out->values)) return SALR_ERR_INVALID_ARG;
+  if (r_cat > 0 && (!out->a_cat || !out->b_cat)) return SALR_ERR_INVALID_ARG;
+  const void* optrs[] = {out->masks, out->values, out->offsets, out->a_cat, out->b_cat};
+  for (const void* q : optrs)
+    if (q && !aligned16(q)) return SALR_ERR_INVALID_ARG;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t K = out->K, kw = cdiv(K, 64), ng = cdiv(K, 1024);
+  int64_t row0 = 0;
+  int32_t rank0 = 0;
+  for (int32_t p = 0; p < n_parts; ++p) {
+    const salr_layer_t* L = parts[p];
+    const auto copy = [&](void* dst, const void* src, size_t bytes) {
+      return bytes == 0 || hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s) == hipSuccess;
+    };
+    bool ok = copy(out->masks + row0 * kw, L->masks, (size_t)L->N * kw * 8) &&
+              copy(out->offsets + row0 * ng, L->offsets, (size_t)L->N * ng * 4);
+    if (ok && out->n_keep > 0) ok = copy(out->values + row0 * out->n_keep, L->values, (size_t)L->N * out->n_keep * 2);
+    if (ok && L->r_cat > 0) ok = copy(out->a_cat + (int64_t)rank0 * K, L->a_cat, (size_t)L->r_cat * K * 2);
+    if (!ok) return SALR_ERR_HIP;
+    if (r_cat > 0 &&
+        salr::launch_fuse_b(L->b_cat, L->N, L->r_cat, out->b_cat + row0 * r_cat, r_cat, rank0, s) != hipSuccess)
+      return SALR_ERR_HIP;
+    row0 += L->N;
+    rank0 += L->r_cat;
+  }
+  return hipGetLastError() == hipSuccess ? SALR_OK : SALR_ERR_HIP;
+}
+
 const char* salr_status_string(int status) {
   switch (status) {
     case SALR_OK: return "ok";

@@ -140,6 +140,13 @@ int fwd_large_ksplit(int64_t N, int64_t K, int64_t M);
 size_t fwd_large_part_bytes(int64_t N, int64_t K, int64_t M_max);
 
 // ----------------------------------------------------------------------------
+// Multi-projection fusion: rows [0, rows) of a fused B_cat (row stride r_dst)
+// from one part's B_cat [rows][r_src], placed at columns [col0, col0 + r_src),
+// zeros elsewhere.
+hipError_t launch_fuse_b(const uint16_t* src, int64_t rows, int r_src, uint16_t* dst, int r_dst, int col0,
+                         hipStream_t s);
+
+// ----------------------------------------------------------------------------
 // Encode kernels.
 // ----------------------------------------------------------------------------
 struct PrunePackArgs {

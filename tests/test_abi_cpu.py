@@ -140,6 +140,33 @@ def test_encode_validation_paths():
     assert _enc(ws_bytes=4096) == -3
 
 
+def _fuse(parts, out):
+    arr = (C.POINTER(B.salr_layer_t) * max(len(parts), 1))(*[C.pointer(p) for p in parts])
+    return srl.lib().salr_fuse_layers(arr if parts else None, len(parts), C.byref(out) if out is not None else None,
+                                      None)
+
+
+def test_fuse_validation_paths():
+    # Every case fails validation, which happens before any HIP call.
+    a = _layer(64, 64, 32, 8, base=0x10000000)
+    b = _layer(32, 64, 32, 4, base=0x20000000)
+    out = _layer(96, 64, 32, 12, base=0x30000000)
+    assert _fuse([], out) == -1                           # no parts
+    assert _fuse([a, b], None) == -1                      # null output
+    assert _fuse([a, b], _layer(95, 64, 32, 12, base=0x30000000)) == -1   # N != sum
+    assert _fuse([a, b], _layer(96, 64, 32, 11, base=0x30000000)) == -1   # r_cat != sum
+    assert _fuse([a, _layer(32, 72, 36, 4, base=0x20000000)], out) == -1  # K differs
+    assert _fuse([a, _layer(32, 64, 31, 4, base=0x20000000)], out) == -1  # n_keep differs
+    big = [_layer(16, 64, 32, 200, base=0x10000000 * (i + 1)) for i in range(2)]
+    assert _fuse(big, _layer(32, 64, 32, 400, base=0x50000000)) == -1    # sum of ranks > 256
+    c = _layer(32, 64, 32, 4, base=0x20000000)
+    c.b_cat = None
+    assert _fuse([a, c], out) == -1                       # adapters missing
+    d = _layer(96, 64, 32, 12, base=0x30000000)
+    d.values = 0x30100008
+    assert _fuse([a, b], d) == -1                         # misaligned output
+
+
 def test_python_wrapper_requires_library(monkeypatch, tmp_path):
     """With the shared library missing, the product path raises instead of
     falling back to anything else."""

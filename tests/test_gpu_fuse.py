@@ -1,0 +1,59 @@
+"""Multi-projection fusion on the GPU (salr_fuse_layers through the C ABI):
+the fused encoding must equal the oracle's fusion of the same parts byte
+for byte, and a forward on it must match the oracle's forward of the fused
+encoding (which the CPU pins tie to the parts' separate forwards)."""
+
+import numpy as np
+import pytest
+
+from oracle import bf16 as ob
+from oracle import salr as osl
+from sparse_rank_linear_amd import synth
+from tests.gpu_util import TOL_MAX_REL, TOL_NORMWISE, errors, say, to_dev, to_host_bits, upload_encoded, wait_error
+
+pytestmark = pytest.mark.gpu
+
+# (K, n_keep, [(N, r_svd, LoRA ranks) per part], token counts)
+CASES = [
+    (512, 256, [(64, 4, (4,)), (16, 2, ()), (48, 0, (3, 2))], (1, 16, 40)),      # ragged ranks, small
+    (2048, 1024, [(1024, 16, (8,)), (256, 8, (8,)), (256, 8, (8,))], (1, 16, 300)),  # q/k/v-like
+    (1032, 500, [(200, 0, (8,)), (200, 0, (8,))], (3, 16, 64)),                   # gate/up-like, ragged K
+    (4096, 2048, [(80, 0, ()), (48, 0, ())], (16,)),                              # no adapters at all
+]
+
+
+def _part(N, K, n_keep, r_svd, loras, seed):
+    rng = np.random.default_rng(seed)
+    W = synth.make_w(N, K, seed)
+    As = [ob.f64_to_bits(rng.standard_normal((q, K)).astype(np.float32) * 0.01) for q in loras]
+    Bs = [ob.f64_to_bits(rng.standard_normal((N, q)).astype(np.float32) * 0.01) for q in loras]
+    return osl.encode(W, n_keep, r_svd, As, Bs)
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"K{c[0]}_parts{len(c[2])}")
+def test_fuse_matches_oracle(case):
+    import sparse_rank_linear_amd as srl
+
+    K, n_keep, specs, Ms = case
+    parts = [_part(N, K, n_keep, rs, lr, seed=100 * i + N) for i, (N, rs, lr) in enumerate(specs)]
+    layers = [upload_encoded(p, K, rs) for p, (N, rs, lr) in zip(parts, specs)]
+    say(f"fuse K={K} n_keep={n_keep} parts={[(l.N, l.r_cat) for l in layers]}")
+    fused = srl.fuse(layers)
+    ref = osl.fuse(parts)
+    got = fused.to_numpy()
+    assert fused.N == sum(l.N for l in layers) and fused.r_cat == sum(l.r_cat for l in layers)
+    assert np.array_equal(got["masks"], ref["masks"])
+    assert np.array_equal(got["values"], ref["values"])
+    assert np.array_equal(got["offsets"], ref["offsets"])
+    assert np.array_equal(got["a_cat"], ref["A_cat"].T)
+    assert np.array_equal(got["b_cat"], ref["B_cat"].T)
+
+    ws = srl.forward_workspace(fused, max(Ms))
+    for M in Ms:
+        say(f"fused forward K={K} N={fused.N} r_cat={fused.r_cat} M={M}")
+        X = synth.make_x(K, M, seed=M + 3)
+        Y = srl.linear_forward(fused, to_dev(X), ws=ws)
+        Yref = osl.forward(X, ref["masks"], ref["values"], K, ref["A_cat"], ref["B_cat"])
+        mr, nw = errors(to_host_bits(Y), Yref)
+        assert wait_error(ws) == 0
+        assert mr <= TOL_MAX_REL and nw <= TOL_NORMWISE, (M, mr, nw)
