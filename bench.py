@@ -169,6 +169,55 @@ def run_configs(dev):
         torch.cuda.empty_cache()
 
 
+# Projections that read the same input, fused into one call (salr_fuse_layers):
+# name -> [(workload, rows)].  Parts of one group share K, sparsity and ranks;
+# a part with fewer rows than its workload takes the workload's first rows
+# (the Llama-7B attention block's k/v projections are 4096 x 4096 too; the
+# Llama-3-8B ones are 1024 x 4096).
+FUSED_GROUPS = {
+    "llama7b_qkv": [("llama7b_attn_4096", 4096)] * 3,
+    "llama3_8b_kv": [("llama3_8b_kv", 1024)] * 2,
+    "llama3_8b_gate_up": [("llama3_8b_gate_up", 14336)] * 2,
+}
+
+
+def run_fused(dev):
+    """One JSON line per (group, token count): the fused layer against the
+    parts called one after another, same inputs, rotating copies."""
+    import torch
+    import sparse_rank_linear_amd as srl
+    from sparse_rank_linear_amd import synth
+
+    for gname, group in FUSED_GROUPS.items():
+        parts = []
+        for i, (wname, rows) in enumerate(group):
+            wl = synth.WORKLOADS[wname]
+            wl = synth.Workload(**{**wl.__dict__, "N": rows, "seed": wl.seed + i})
+            inp = synth.make_inputs(wl, with_x=False)
+            layer, _ = srl.encode(_dev_bits(inp.W, dev), wl.n_keep, wl.r_svd,
+                                  [_dev_bits(a, dev) for a in inp.lora_A], [_dev_bits(b, dev) for b in inp.lora_B])
+            parts.append(layer)
+        fused = srl.fuse(parts)
+        torch.cuda.synchronize()
+        K = fused.K
+        for M in (1, 16, 2048):
+            X = _dev_bits(synth.make_x(K, M, seed=11), dev)
+            copies = 1 if M > 16 else max(2, -(-600_000_000 // fused.compressed_bytes()))
+            sep = 0.0
+            for p in parts:
+                ls = [p] + [p.clone() for _ in range(copies - 1)]
+                sep += measure_decode(ls, X, srl.forward_workspace(p, M), 32, 4)
+                del ls
+            fl = [fused] + [fused.clone() for _ in range(copies - 1)]
+            t = measure_decode(fl, X, srl.forward_workspace(fused, M), 32, 4)
+            del fl
+            print(json.dumps({"fused": gname, "N": fused.N, "K": K, "r_cat": fused.r_cat, "M": M,
+                              "separate_us": round(sep * 1e6, 2), "fused_us": round(t * 1e6, 2),
+                              "speedup": round(sep / t, 3)}), flush=True)
+            torch.cuda.empty_cache()
+        del parts, fused
+
+
 def cpu_baseline(wl, budget_s: float = 12.0):
     """The oracle's float64 forward on the headline shape, on host cores."""
     from oracle import salr as osl
@@ -212,6 +261,8 @@ def main():
     ap.add_argument("--steps", type=int, default=320)
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--no-extra", action="store_true", help="headline line only (no sweep/prefill/cpu)")
+    ap.add_argument("--fused", action="store_true",
+                    help="time fused projections (salr_fuse_layers) against separate calls, then exit")
     ap.add_argument("--configs", action="store_true",
                     help="time every workload of the synthetic table instead of the headline line")
     ap.add_argument("--probe", choices=["copy"], default=None,
@@ -238,6 +289,9 @@ def main():
                           "bytes_written_per_launch": a.numel() * 2, "launches": 5}))
         return
 
+    if args.fused:
+        run_fused(dev)
+        return
     if args.configs:
         run_configs(dev)
         return
