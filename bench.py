@@ -218,6 +218,29 @@ def run_fused(dev):
         del parts, fused
 
 
+def run_layer(dev, name: str, M: int, steps: int, warmup: int):
+    """One workload of the synthetic table at M tokens: GPU encode, then
+    `steps` graph-replayed forward calls (for kernel traces and counters).
+    One JSON line with the mean time per call."""
+    import torch
+    import sparse_rank_linear_amd as srl
+    from sparse_rank_linear_amd import synth
+
+    wl = synth.WORKLOADS[name]
+    inp = synth.make_inputs(wl, with_x=False)
+    layer, _ = srl.encode(_dev_bits(inp.W, dev), wl.n_keep, wl.r_svd, [_dev_bits(a, dev) for a in inp.lora_A],
+                          [_dev_bits(b, dev) for b in inp.lora_B])
+    torch.cuda.synchronize()
+    cbytes = layer.compressed_bytes()
+    copies = 1 if M > 16 else max(2, -(-600_000_000 // cbytes))
+    layers = [layer] + [layer.clone() for _ in range(copies - 1)]
+    X = _dev_bits(synth.make_x(wl.K, M, seed=11), dev)
+    t = measure_decode(layers, X, srl.forward_workspace(layer, M), steps, warmup)
+    print(json.dumps({"workload": name, "N": wl.N, "K": wl.K, "r_cat": wl.r_cat, "M": M, "steps": steps,
+                      "us": round(t * 1e6, 2), "tflops_dense_equiv": round(2 * M * wl.N * wl.K / t / 1e12, 2),
+                      "compressed_GBs": round(cbytes / t / 1e9, 1)}), flush=True)
+
+
 def cpu_baseline(wl, budget_s: float = 12.0):
     """The oracle's float64 forward on the headline shape, on host cores."""
     from oracle import salr as osl
@@ -261,6 +284,9 @@ def main():
     ap.add_argument("--steps", type=int, default=320)
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--no-extra", action="store_true", help="headline line only (no sweep/prefill/cpu)")
+    ap.add_argument("--layer", default=None,
+                    help="time one workload of the synthetic table (with --tokens) and exit")
+    ap.add_argument("--tokens", type=int, default=16, help="token count for --layer")
     ap.add_argument("--fused", action="store_true",
                     help="time fused projections (salr_fuse_layers) against separate calls, then exit")
     ap.add_argument("--configs", action="store_true",
@@ -289,6 +315,9 @@ def main():
                           "bytes_written_per_launch": a.numel() * 2, "launches": 5}))
         return
 
+    if args.layer:
+        run_layer(dev, args.layer, args.tokens, args.steps, args.warmup)
+        return
     if args.fused:
         run_fused(dev)
         return
