@@ -14,8 +14,11 @@
 //     Q = orth(Y);  Bt = R^T Q;  eig(Bt^T Bt) = U diag(lambda) U^T;
 //     sigma = sqrt(lambda),  A'^T = diag(sigma^-1/2) U_r^T Bt^T,
 //     B'^T = Q U_r diag(sigma^1/2).
-// orth() is Cholesky QR applied twice (the second pass repairs the first
-// pass's loss of orthogonality).  The big products run on fp32 matrix cores
+// orth() is Cholesky QR: once per half-step inside the iteration (only the
+// span matters there; the next product and orth() carry on from any
+// well-conditioned basis), twice for the final Q, whose orthonormality the
+// small eigenproblem relies on (the second pass repairs the first one's
+// loss of orthogonality).  The big products run on fp32 matrix cores
 // (v_mfma_f32_16x16x4_f32); the l x l Cholesky and the symmetric eigen
 // problem run in fp64 inside one workgroup (cyclic Jacobi, round-robin
 // pairing).  Omega is Gaussian from a counter-based generator (SplitMix64,
@@ -679,11 +682,13 @@ int skinny_split(int64_t M, int64_t N, int64_t K) {
 }
 
 // Y (rows x l, row-major) <- orthonormal basis of its column span; `tmp` has
-// the same shape.  Cholesky QR twice.
-hipError_t orth(hipStream_t s, float* Y, float* tmp, int64_t rows, int l, const EncodeLayout& E, void* ws) {
+// the same shape.  Cholesky QR `passes` times (the second pass repairs the
+// first one's loss of orthogonality).
+hipError_t orth(hipStream_t s, float* Y, float* tmp, int64_t rows, int l, const EncodeLayout& E, void* ws,
+                int passes) {
   float* G = at<float>(ws, E.G);
   float* C = at<float>(ws, E.C);
-  for (int pass = 0; pass < 2; ++pass) {
+  for (int pass = 0; pass < passes; ++pass) {
     // G = Y^T Y
     hipError_t e = gemm(s, l, l, rows, Y, false, 1, l, Y, l, 1, G, l, 1, skinny_split(l, l, rows));
     if (e != hipSuccess) return e;
@@ -756,14 +761,14 @@ int encode_run(const EncodeParams& p) {
     // Y = R Z
     CK(gemm(s, N, l, K, R, true, K, 1, Z, l, 1, Y, l, 1, skinny_split(N, l, K)));
     for (int it = 0; it < p.iters; ++it) {
-      CK(orth(s, Y, Q, N, l, E, ws));
+      CK(orth(s, Y, Q, N, l, E, ws, 1));
       // Z = R^T Y
       CK(gemm(s, K, l, N, R, true, 1, K, Y, l, 1, Z, l, 1, skinny_split(K, l, N)));
-      CK(orth(s, Z, Z2, K, l, E, ws));
+      CK(orth(s, Z, Z2, K, l, E, ws, 1));
       // Y = R Z
       CK(gemm(s, N, l, K, R, true, K, 1, Z, l, 1, Y, l, 1, skinny_split(N, l, K)));
     }
-    CK(orth(s, Y, Q, N, l, E, ws));
+    CK(orth(s, Y, Q, N, l, E, ws, 2));
     // Bt = R^T Q  (K x l), in Z
     CK(gemm(s, K, l, N, R, true, 1, K, Y, l, 1, Z, l, 1, skinny_split(K, l, N)));
     // G = Bt^T Bt
