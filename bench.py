@@ -330,6 +330,7 @@ def main():
     W = _dev_bits(inp.W, dev)
     As = [_dev_bits(a, dev) for a in inp.lora_A]
     Bs = [_dev_bits(b, dev) for b in inp.lora_B]
+    layer, _ = srl.encode(W, wl.n_keep, wl.r_svd, As, Bs)  # (first call also loads the code objects)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     layer, _ = srl.encode(W, wl.n_keep, wl.r_svd, As, Bs)
@@ -369,7 +370,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "fwd_small_kernel", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic()},
-        "encode": {"seconds": round(encode_s, 4), "iters": 24, "oversample": 32},
+        "encode": {"seconds": round(encode_s, 4), "iters": 24, "oversample": 32, "call": "second"},
     }
     if not args.no_extra:
         sweep = []
