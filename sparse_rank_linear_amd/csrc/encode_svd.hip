@@ -126,6 +126,134 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
       }
 }
 
+// ---------------------------------------------------------------------------
+// Products with the residual on the bf16 matrix cores.  R is exact in bf16;
+// the fp32 basis B is split into two bf16 parts, B = B_hi + B_lo + e with
+// |e| <= 2^-17 |B|, and C = R B_hi + R B_lo accumulates in fp32
+// (v_mfma_f32_16x16x32_bf16, exact products).  Both operands are read
+// k-contiguous: A row-major [M][Kd] (R, or R^T materialised once), B as
+// transposed parts Bh/Bl [l_pad][ld] with zeros past l and past Kd.
+// ---------------------------------------------------------------------------
+
+// dst[c][r] = src[r][c] for a rows x cols bf16 matrix (64 x 64 tiles via LDS);
+// the 32 elements after dst's end (its tail room) are zeroed, so that a
+// product reading past the last row meets finite values.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* src, int64_t rows, int64_t cols,
+                                                             uint16_t* dst) {
+  __shared__ uint16_t t[64][66];
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 32) dst[rows * cols + threadIdx.x] = 0;
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int y = ty; y < 64; y += 4) {
+    const int64_t r = r0 + y, c = c0 + tx;
+    t[y][tx] = (r < rows && c < cols) ? src[r * cols + c] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int y = ty; y < 64; y += 4) {
+    const int64_t c = c0 + y, r = r0 + tx;
+    if (c < cols && r < rows) dst[c * rows + r] = t[tx][y];
+  }
+}
+
+// Bh[c][k] = bf16(B[k][c]), Bl[c][k] = bf16(B[k][c] - Bh[c][k]) (both
+// round to nearest even); zero for c >= l or k >= kd.  B fp32 [kd][l];
+// tiles of 64 k x 32 c via LDS.
+__global__ __launch_bounds__(256) void split_t_kernel(const float* B, int64_t kd, int l, uint16_t* Bh, uint16_t* Bl,
+                                                      int64_t ld) {
+  __shared__ float t[64][33];
+  const int64_t k0 = (int64_t)blockIdx.x * 64;
+  const int c0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int y = ty; y < 64; y += 8) {
+    const int64_t k = k0 + y;
+    const int c = c0 + tx;
+    t[y][tx] = (k < kd && c < l) ? B[k * l + c] : 0.f;
+  }
+  __syncthreads();
+  const int kx = threadIdx.x & 63, cy = threadIdx.x >> 6;
+  for (int y = cy; y < 32; y += 4) {
+    const float v = t[kx][y];
+    const uint16_t hi = f32_to_bf16(v);
+    const uint16_t lo = f32_to_bf16(v - bf16_to_f32(hi));
+    const int64_t o = (int64_t)(c0 + y) * ld + k0 + kx;
+    Bh[o] = hi;
+    Bl[o] = lo;
+  }
+}
+
+// C[m][c] (+)= sum_k A[m][k] (Bh[c][k] + Bl[c][k]) over this workgroup's K
+// range [blockIdx.y * k_chunk, +k_chunk).  Workgroup: 4 waves, 64 rows (4
+// MFMA row tiles); wave w takes the column tiles w, w + 4, ... (CT of them),
+// so the waves share the row tiles' loads in L1.  Rows past M read row M-1
+// and columns past Kd read a group ending at most 7 past the row (their B
+// is zero); neither is
+// stored.  With split K the partial sums are added atomically (C zeroed
+// first).  A needs 16 bytes of readable room past its last row.
+template <int CT>
+__global__ __launch_bounds__(256) void gemm_bf16x2_kernel(const uint16_t* A, int64_t lda, const uint16_t* Bh,
+                                                          const uint16_t* Bl, int64_t ldb, float* C, int64_t M, int l,
+                                                          int64_t Kd, int64_t k_chunk, int atomic) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int lt = (l + 15) / 16;
+  const int64_t m0 = (int64_t)blockIdx.x * 64;
+  const int64_t kb = (int64_t)blockIdx.y * k_chunk, ke = std::min<int64_t>(Kd, kb + k_chunk);
+  const int64_t kd8 = (Kd + 7) / 8 * 8;
+  const uint16_t* arow[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) arow[t] = A + std::min<int64_t>(m0 + 16 * t + i, M - 1) * lda;
+  const uint16_t* bhr[CT];
+  const uint16_t* blr[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    const int ct = std::min(wave + 4 * c, lt - 1);
+    bhr[c] = Bh + (int64_t)(16 * ct + i) * ldb + 8 * g;
+    blr[c] = Bl + (int64_t)(16 * ct + i) * ldb + 8 * g;
+  }
+  f32x4_t acc[4][CT];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int c = 0; c < CT; ++c) acc[t][c] = zero4();
+  for (int64_t k = kb; k < ke; k += 32) {
+    // (Kd need not be a multiple of 8: the last group may read up to 7
+    // elements past a row, which meet B's zeros; the buffers have tail room)
+    const int64_t ka = std::min<int64_t>(k + 8 * g, kd8 - 8);
+    u32x4_t a[4], bh[CT], bl[CT];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) a[t] = load16(arow[t] + ka);
+#pragma unroll
+    for (int c = 0; c < CT; ++c) {
+      bh[c] = load16(bhr[c] + k);
+      bl[c] = load16(blr[c] + k);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int c = 0; c < CT; ++c) {
+        acc[t][c] = mfma_16x16x32(a[t], bh[c], acc[t][c]);
+        acc[t][c] = mfma_16x16x32(a[t], bl[c], acc[t][c]);
+      }
+  }
+  // lane holds C[m0 + 16t + 4g + e][16 ct + i]
+#pragma unroll
+  for (int c = 0; c < CT; ++c) {
+    const int ct = wave + 4 * c;
+    const int col = 16 * ct + i;
+    if (ct >= lt || col >= l) continue;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t m = m0 + 16 * t + 4 * g + e;
+        if (m >= M) continue;
+        const float v = acc[t][c][e];  // (scalar copy first: see the few-row forward)
+        if (atomic) atomicAdd(&C[m * l + col], v);
+        else C[m * l + col] = v;
+      }
+  }
+}
+
 __global__ void fill_f32_kernel(float* p, int64_t n, float v) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
 }
@@ -625,7 +753,8 @@ __global__ void copy_lora_kernel(const uint16_t* la, const uint16_t* lb, uint16_
 
 struct EncodeLayout {
   int l;
-  size_t R, Y, Q, Z, Z2, G, C, dA, dB, dC, evals, U, flags, total;
+  int64_t ldb;  // row stride of the split basis parts (max(N, K) rounded up to 64)
+  size_t R, Rt, Bh, Bl, Y, Q, Z, Z2, G, C, dA, dB, dC, evals, U, flags, total;
 };
 
 EncodeLayout encode_layout(int64_t N, int64_t K, int32_t r_svd, int32_t oversample) {
@@ -635,7 +764,12 @@ EncodeLayout encode_layout(int64_t N, int64_t K, int32_t r_svd, int32_t oversamp
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes, 256); return o; };
   L.flags = take(64);
-  L.R = take((size_t)N * K * 2);
+  L.R = take((size_t)N * K * 2 + 64);   // (+ tail room for the product's last group)
+  L.Rt = take((size_t)N * K * 2 + 64);
+  L.ldb = (std::max(N, K) + 63) / 64 * 64;
+  const size_t lp = (l + 31) / 32 * 32;
+  L.Bh = take(lp * (size_t)L.ldb * 2);
+  L.Bl = take(lp * (size_t)L.ldb * 2);
   L.Y = take((size_t)N * l * 4);
   L.Q = take((size_t)N * l * 4);
   L.Z = take((size_t)K * l * 4);
@@ -671,6 +805,32 @@ hipError_t gemm(hipStream_t s, int64_t M, int64_t N, int64_t K, const void* A, b
   }
   dim3 grid((unsigned)cdiv(N, 64), (unsigned)cdiv(M, 64), (unsigned)g.k_split);
   hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
+// C [M][l] = A [M][Kd] (bf16, row-major, row stride lda) * B [Kd][l] (fp32)
+// on the bf16 matrix cores (B split into two bf16 parts).
+hipError_t gemm_r(hipStream_t s, const uint16_t* A, int64_t lda, int64_t M, int64_t Kd, const float* B, int l, float* C,
+                  const EncodeLayout& E, void* ws) {
+  uint16_t* Bh = at<uint16_t>(ws, E.Bh);
+  uint16_t* Bl = at<uint16_t>(ws, E.Bl);
+  const int lp = (l + 31) / 32;
+  hipLaunchKernelGGL(split_t_kernel, dim3((unsigned)cdiv(Kd, 64), (unsigned)lp), dim3(256), 0, s, B, Kd, l, Bh, Bl,
+                     E.ldb);
+  const int64_t mb = cdiv(M, 64);
+  const int64_t splits = std::max<int64_t>(1, std::min<int64_t>(cdiv(512, mb), Kd / 512));
+  const int64_t k_chunk = align_up((size_t)cdiv(Kd, splits), 32);
+  const int64_t ks = cdiv(Kd, k_chunk);
+  const int atomic = ks > 1 ? 1 : 0;
+  if (atomic) hipLaunchKernelGGL(fill_f32_kernel, dim3(256), dim3(256), 0, s, C, M * l, 0.0f);
+  const dim3 grid((unsigned)mb, (unsigned)ks);
+  switch (cdiv((l + 15) / 16, 4)) {
+    case 1: hipLaunchKernelGGL(gemm_bf16x2_kernel<1>, grid, dim3(256), 0, s, A, lda, Bh, Bl, E.ldb, C, M, l, Kd, k_chunk, atomic); break;
+    case 2: hipLaunchKernelGGL(gemm_bf16x2_kernel<2>, grid, dim3(256), 0, s, A, lda, Bh, Bl, E.ldb, C, M, l, Kd, k_chunk, atomic); break;
+    case 3: hipLaunchKernelGGL(gemm_bf16x2_kernel<3>, grid, dim3(256), 0, s, A, lda, Bh, Bl, E.ldb, C, M, l, Kd, k_chunk, atomic); break;
+    case 4: hipLaunchKernelGGL(gemm_bf16x2_kernel<4>, grid, dim3(256), 0, s, A, lda, Bh, Bl, E.ldb, C, M, l, Kd, k_chunk, atomic); break;
+    default: hipLaunchKernelGGL(gemm_bf16x2_kernel<5>, grid, dim3(256), 0, s, A, lda, Bh, Bl, E.ldb, C, M, l, Kd, k_chunk, atomic); break;
+  }
   return hipGetLastError();
 }
 
@@ -757,20 +917,23 @@ int encode_run(const EncodeParams& p) {
     float* Q = at<float>(ws, E.Q);
     float* Z = at<float>(ws, E.Z);
     float* Z2 = at<float>(ws, E.Z2);
+    uint16_t* Rt = at<uint16_t>(ws, E.Rt);
+    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)cdiv(K, 64), (unsigned)cdiv(N, 64)), dim3(256), 0, s, R,
+                       N, K, Rt);
     hipLaunchKernelGGL(gaussian_kernel, dim3(1024), dim3(256), 0, s, Z, K * l, p.seed);
     // Y = R Z
-    CK(gemm(s, N, l, K, R, true, K, 1, Z, l, 1, Y, l, 1, skinny_split(N, l, K)));
+    CK(gemm_r(s, R, K, N, K, Z, l, Y, E, ws));
     for (int it = 0; it < p.iters; ++it) {
       CK(orth(s, Y, Q, N, l, E, ws, 1));
       // Z = R^T Y
-      CK(gemm(s, K, l, N, R, true, 1, K, Y, l, 1, Z, l, 1, skinny_split(K, l, N)));
+      CK(gemm_r(s, Rt, N, K, N, Y, l, Z, E, ws));
       CK(orth(s, Z, Z2, K, l, E, ws, 1));
       // Y = R Z
-      CK(gemm(s, N, l, K, R, true, K, 1, Z, l, 1, Y, l, 1, skinny_split(N, l, K)));
+      CK(gemm_r(s, R, K, N, K, Z, l, Y, E, ws));
     }
     CK(orth(s, Y, Q, N, l, E, ws, 2));
     // Bt = R^T Q  (K x l), in Z
-    CK(gemm(s, K, l, N, R, true, 1, K, Y, l, 1, Z, l, 1, skinny_split(K, l, N)));
+    CK(gemm_r(s, Rt, N, K, N, Y, l, Z, E, ws));
     // G = Bt^T Bt
     float* G = at<float>(ws, E.G);
     CK(gemm(s, l, l, K, Z, false, 1, l, Z, l, 1, G, l, 1, skinny_split(l, l, K)));
