@@ -18,8 +18,10 @@
 // span matters there; the next product and orth() carry on from any
 // well-conditioned basis), twice for the final Q, whose orthonormality the
 // small eigenproblem relies on (the second pass repairs the first one's
-// loss of orthogonality).  The big products run on fp32 matrix cores
-// (v_mfma_f32_16x16x4_f32); the l x l Cholesky and the symmetric eigen
+// loss of orthogonality).  The products with R run on bf16 matrix cores
+// with the fp32 basis split into two bf16 parts (v_mfma_f32_16x16x32_bf16),
+// the basis' own products on fp32 ones (v_mfma_f32_16x16x4_f32); the l x l
+// Cholesky and the symmetric eigen
 // problem run in fp64 inside one workgroup (cyclic Jacobi, round-robin
 // pairing).  Omega is Gaussian from a counter-based generator (SplitMix64,
 // Steele, Lea and Flood 2014, fed to the Box-Muller transform).
