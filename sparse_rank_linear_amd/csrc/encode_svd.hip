@@ -716,6 +716,120 @@ __global__ __launch_bounds__(kSmallThreads) void jacobi_lds_kernel(const float* 
     for (int r = tx; r < l; r += 32) U[i * l + r] = (float)V[i * ld + order[r]];
 }
 
+// The same eigensolver for bases too wide for two fp64 matrices in LDS
+// (l <= kMidJacobi): A in LDS as fp32 (its input, the Gram matrix, is fp32
+// already), the eigenvectors in global memory (fp32, L2-resident), and a
+// stopping test suited to fp32 entries.
+constexpr int kMidJacobi = 190;  // 4 l (l + 1) bytes of LDS
+__global__ __launch_bounds__(kSmallThreads) void jacobi_mid_kernel(const float* S, double* evals, float* U, float* V, int l,
+                                                                   int max_sweeps) {
+  extern __shared__ float smf[];
+  float* A = smf;           // [l][l + 1] in LDS; V [l][l + 1] in global memory
+  __shared__ double cs[kMaxPairs], sn[kMaxPairs];
+  __shared__ int pp[kMaxPairs], qq[kMaxPairs];
+  __shared__ double red[2 * (kSmallThreads / 64)];  // per-wave sums (off, diagonal)
+  __shared__ int order[512];
+  const int tid = threadIdx.x;
+  const int ld = l + 1;
+  const int tx = tid & 31, ty = tid >> 5;
+  const int n = l + (l & 1);  // even number of players; index l (if any) is a dummy
+  const int npairs = n / 2;
+  for (int i = ty; i < l; i += 32)
+    for (int j = tx; j < l; j += 32) {
+      A[i * ld + j] = 0.5f * (S[i * l + j] + S[j * l + i]);
+      V[i * ld + j] = (i == j) ? 1.f : 0.f;
+    }
+  __syncthreads();
+  for (int sweep = 0; sweep < max_sweeps; ++sweep) {
+    // convergence: off-diagonal mass vs diagonal mass
+    double off = 0.0, dia = 0.0;
+    for (int i = ty; i < l; i += 32)
+      for (int j = tx; j < l; j += 32) {
+        const double v = (double)A[i * ld + j] * (double)A[i * ld + j];
+        if (i == j) dia += v; else off += v;
+      }
+    for (int o = 32; o > 0; o >>= 1) {
+      off += __shfl_xor(off, o);
+      dia += __shfl_xor(dia, o);
+    }
+    if ((tid & 63) == 0) {
+      red[2 * (tid >> 6)] = off;
+      red[2 * (tid >> 6) + 1] = dia;
+    }
+    __syncthreads();
+    double off_t = 0.0, dia_t = 0.0;
+    for (int w = 0; w < kSmallThreads / 64; ++w) {
+      off_t += red[2 * w];
+      dia_t += red[2 * w + 1];
+    }
+    __syncthreads();
+    // (fp32 entries: stop once the off-diagonal norm is 1e-6 of the diagonal's)
+    if (off_t <= 1e-12 * (dia_t + 1e-300) || off_t == 0.0) break;
+
+    for (int round = 0; round < n - 1; ++round) {
+      if (tid < npairs) {
+        int p, q;
+        if (tid == 0) { p = n - 1; q = round; }
+        else { p = (round + tid) % (n - 1); q = (round - tid + (n - 1)) % (n - 1); }
+        if (p > q) { const int t = p; p = q; q = t; }
+        double c = 1.0, sv = 0.0;
+        if (q < l) {
+          const double apq = A[p * ld + q];
+          if (fabs(apq) > 1e-30) {
+            const double theta = ((double)A[q * ld + q] - (double)A[p * ld + p]) / (2.0 * apq);
+            const double t = (theta >= 0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
+            c = 1.0 / sqrt(t * t + 1.0);
+            sv = t * c;
+          }
+        }
+        pp[tid] = p; qq[tid] = q; cs[tid] = c; sn[tid] = sv;
+      }
+      __syncthreads();
+      // rows: A <- J^T A
+      for (int k = ty; k < npairs; k += 32) {
+        const int p = pp[k], q = qq[k];
+        if (q >= l) continue;
+        const float c = (float)cs[k], sv = (float)sn[k];
+        for (int j = tx; j < l; j += 32) {
+          const float ap = A[p * ld + j], aq = A[q * ld + j];
+          A[p * ld + j] = c * ap - sv * aq;
+          A[q * ld + j] = sv * ap + c * aq;
+        }
+      }
+      __syncthreads();
+      // columns: A <- A J, V <- V J
+      for (int k = ty; k < npairs; k += 32) {
+        const int p = pp[k], q = qq[k];
+        if (q >= l) continue;
+        const float c = (float)cs[k], sv = (float)sn[k];
+        for (int i = tx; i < l; i += 32) {
+          const float ap = A[i * ld + p], aq = A[i * ld + q];
+          A[i * ld + p] = c * ap - sv * aq;
+          A[i * ld + q] = sv * ap + c * aq;
+          const float vp = V[i * ld + p], vq = V[i * ld + q];
+          V[i * ld + p] = c * vp - sv * vq;
+          V[i * ld + q] = sv * vp + c * vq;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // sort eigenvalues descending (rank by counting)
+  for (int i = tid; i < l; i += kSmallThreads) {
+    const float di = A[i * ld + i];
+    int rank = 0;
+    for (int j = 0; j < l; ++j) {
+      const float dj = A[j * ld + j];
+      rank += (dj > di) || (dj == di && j < i);
+    }
+    order[rank] = i;
+  }
+  __syncthreads();
+  for (int r = tid; r < l; r += kSmallThreads) evals[r] = (double)A[order[r] * ld + order[r]];
+  for (int i = ty; i < l; i += 32)
+    for (int r = tx; r < l; r += 32) U[i * l + r] = V[i * ld + order[r]];
+}
+
 // a_cat rows [0, r): a_cat[i][k] = bf16(P[k][i] / sqrt(sigma_i)), P = Bt U_r.
 __global__ void write_a_kernel(const float* P, const double* evals, uint16_t* a_cat, int64_t K, int r) {
   const int i = blockIdx.y;
@@ -944,6 +1058,9 @@ int encode_run(const EncodeParams& p) {
     if (l <= kLdsJacobi)
       hipLaunchKernelGGL(jacobi_lds_kernel, dim3(1), dim3(kSmallThreads), (size_t)2 * l * (l + 1) * 8, s, G, evals, U, l,
                          30);
+    else if (l <= kMidJacobi)
+      hipLaunchKernelGGL(jacobi_mid_kernel, dim3(1), dim3(kSmallThreads), (size_t)4 * l * (l + 1), s, G, evals, U,
+                         at<float>(ws, E.dA), l, 30);
     else
       hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(kSmallThreads), 0, s, G, at<double>(ws, E.dA),
                          at<double>(ws, E.dB), evals, U, l, 30);
