@@ -184,21 +184,25 @@ __global__ __launch_bounds__(256) void split_t_kernel(const float* B, int64_t kd
 }
 
 // C[m][c] (+)= sum_k A[m][k] (Bh[c][k] + Bl[c][k]) over this workgroup's K
-// range [blockIdx.y * k_chunk, +k_chunk).  Workgroup: 4 waves, 64 rows (4
-// MFMA row tiles); wave w takes the column tiles w, w + 4, ... (CT of them),
-// so the waves share the row tiles' loads in L1.  Rows past M read row M-1
+// range [blockIdx.y * k_chunk, +k_chunk).  Workgroup: 4 waves in CG column
+// groups x 4/CG row groups of 64 rows (4 MFMA row tiles each); wave w takes
+// row group w / CG and the column tiles w % CG, w % CG + CG, ... (CT of
+// them).  Waves of one row group share its row tiles' loads in L1, and the
+// basis is read once per 64 x 4/CG rows.  Rows past M read row M-1
 // and columns past Kd read a group ending at most 7 past the row (their B
 // is zero); neither is
 // stored.  With split K the partial sums are added atomically (C zeroed
 // first).  A needs 16 bytes of readable room past its last row.
-template <int CT>
+template <int CT, int CG>
 __global__ __launch_bounds__(256) void gemm_bf16x2_kernel(const uint16_t* A, int64_t lda, const uint16_t* Bh,
                                                           const uint16_t* Bl, int64_t ldb, float* C, int64_t M, int l,
                                                           int64_t Kd, int64_t k_chunk, int atomic) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = lane & 15, g = lane >> 4;
   const int lt = (l + 15) / 16;
-  const int64_t m0 = (int64_t)blockIdx.x * 64;
+  constexpr int RG = 4 / CG;
+  const int cg = wave % CG;
+  const int64_t m0 = (int64_t)blockIdx.x * 64 * RG + 64 * (wave / CG);
   const int64_t kb = (int64_t)blockIdx.y * k_chunk, ke = std::min<int64_t>(Kd, kb + k_chunk);
   const int64_t kd8 = (Kd + 7) / 8 * 8;
   const uint16_t* arow[4];
@@ -208,7 +212,7 @@ __global__ __launch_bounds__(256) void gemm_bf16x2_kernel(const uint16_t* A, int
   const uint16_t* blr[CT];
 #pragma unroll
   for (int c = 0; c < CT; ++c) {
-    const int ct = std::min(wave + 4 * c, lt - 1);
+    const int ct = std::min(cg + CG * c, lt - 1);
     bhr[c] = Bh + (int64_t)(16 * ct + i) * ldb + 8 * g;
     blr[c] = Bl + (int64_t)(16 * ct + i) * ldb + 8 * g;
   }
@@ -240,7 +244,7 @@ __global__ __launch_bounds__(256) void gemm_bf16x2_kernel(const uint16_t* A, int
   // lane holds C[m0 + 16t + 4g + e][16 ct + i]
 #pragma unroll
   for (int c = 0; c < CT; ++c) {
-    const int ct = wave + 4 * c;
+    const int ct = cg + CG * c;
     const int col = 16 * ct + i;
     if (ct >= lt || col >= l) continue;
 #pragma unroll
@@ -933,20 +937,37 @@ hipError_t gemm_r(hipStream_t s, const uint16_t* A, int64_t lda, int64_t M, int6
   const int lp = (l + 31) / 32;
   hipLaunchKernelGGL(split_t_kernel, dim3((unsigned)cdiv(Kd, 64), (unsigned)lp), dim3(256), 0, s, B, Kd, l, Bh, Bl,
                      E.ldb);
-  const int64_t mb = cdiv(M, 64);
-  const int64_t splits = std::max<int64_t>(1, std::min<int64_t>(cdiv(512, mb), Kd / 512));
+  // two column groups (128-row workgroups) while a wave's share of the
+  // basis fits its registers (l <= 160), else four (64-row workgroups)
+  const int lt = (l + 15) / 16;
+  const int cg = cdiv(lt, 2) <= 5 ? 2 : 4;
+  const int64_t rows_wg = 64 * (4 / cg);
+  const int64_t mb = cdiv(M, rows_wg);
+  const int64_t splits = std::max<int64_t>(1, std::min<int64_t>(cdiv(256, mb), Kd / 512));
   const int64_t k_chunk = align_up((size_t)cdiv(Kd, splits), 32);
   const int64_t ks = cdiv(Kd, k_chunk);
   const int atomic = ks > 1 ? 1 : 0;
   if (atomic) hipLaunchKernelGGL(fill_f32_kernel, dim3(256), dim3(256), 0, s, C, M * l, 0.0f);
   const dim3 grid((unsigned)mb, (unsigned)ks);
-  switch (cdiv((l + 15) / 16, 4)) {
-    case 1: hipLaunchKernelGGL(gemm_bf16x2_kernel<1>, grid, dim3(256), 0, s, A, lda, Bh, Bl, E.ldb, C, M, l, Kd, k_chunk, atomic); break;
-    case 2: hipLaunchKernelGGL(gemm_bf16x2_kernel<2>, grid, dim3(256), 0, s, A, lda, Bh, Bl, E.ldb, C, M, l, Kd, k_chunk, atomic); break;
-    case 3: hipLaunchKernelGGL(gemm_bf16x2_kernel<3>, grid, dim3(256), 0, s, A, lda, Bh, Bl, E.ldb, C, M, l, Kd, k_chunk, atomic); break;
-    case 4: hipLaunchKernelGGL(gemm_bf16x2_kernel<4>, grid, dim3(256), 0, s, A, lda, Bh, Bl, E.ldb, C, M, l, Kd, k_chunk, atomic); break;
-    default: hipLaunchKernelGGL(gemm_bf16x2_kernel<5>, grid, dim3(256), 0, s, A, lda, Bh, Bl, E.ldb, C, M, l, Kd, k_chunk, atomic); break;
+#define SALR_GEMM_R(CT, CG)                                                                                  \
+  hipLaunchKernelGGL((gemm_bf16x2_kernel<CT, CG>), grid, dim3(256), 0, s, A, lda, Bh, Bl, E.ldb, C, M, l, Kd, \
+                     k_chunk, atomic)
+  if (cg == 2) {
+    switch (cdiv(lt, 2)) {
+      case 1: SALR_GEMM_R(1, 2); break;
+      case 2: SALR_GEMM_R(2, 2); break;
+      case 3: SALR_GEMM_R(3, 2); break;
+      case 4: SALR_GEMM_R(4, 2); break;
+      default: SALR_GEMM_R(5, 2); break;
+    }
+  } else {
+    switch (cdiv(lt, 4)) {
+      case 3: SALR_GEMM_R(3, 4); break;
+      case 4: SALR_GEMM_R(4, 4); break;
+      default: SALR_GEMM_R(5, 4); break;
+    }
   }
+#undef SALR_GEMM_R
   return hipGetLastError();
 }
 
