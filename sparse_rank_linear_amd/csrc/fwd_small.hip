@@ -37,6 +37,8 @@
 //     low-rank work and its gather traffic are spread over the ranges;
 //   * pieces and range partials handed between workgroups travel as tagged
 //     words (see salr_device.hpp), so no cache-wide fence is ever executed.
+#include <cstddef>
+
 #include "salr_device.hpp"
 #include "salr_kernels.hpp"
 
@@ -72,6 +74,8 @@ constexpr int piece_steps() { return piece_cols<kOneRound>() / 32 / kWaves; }
 constexpr int kFinBatch = 4;                      // pieces requested together when finishing T
 constexpr int kMaxLoadRows = kRows / kWaves;      // rows per load-issuing wave
 static_assert(sizeof(Lds) % 16 == 0, "values area must stay 16-byte aligned");
+static_assert(offsetof(Lds, masks) % 16 == 0 && sizeof(Lds::masks) >= 8 * 1024,
+              "the T operands of up to 256 ranks live in the bitmap-word area");
 
 __device__ __forceinline__ u32x4_t load_x_frag(const uint16_t* X, int M, int K, int m, int col) {
   if (m < M && col < K) return load16(X + (size_t)m * K + col);
@@ -158,10 +162,13 @@ void fwd_small_kernel(SmallFwdArgs a) {
   Lds& L = *reinterpret_cast<Lds*>(smem);
   uint32_t* const vals = reinterpret_cast<uint32_t*>(smem + sizeof(Lds));
   f32x4_t* const red = reinterpret_cast<f32x4_t*>(vals);
-  // after the values area: this workgroup's T chunks as MFMA operands
-  // [chunk][64 lanes] (bf16 pairs), then the tile's B_cat rows [16][r_cat]
-  u32x4_t* const tl = reinterpret_cast<u32x4_t*>(smem + sizeof(Lds) + a.vals_bytes);
-  uint16_t* const bl = reinterpret_cast<uint16_t*>(smem + sizeof(Lds) + a.vals_bytes + a.tl_bytes);
+  // This workgroup's T chunks as MFMA operands [chunk][64 lanes] (bf16
+  // pairs) reuse the bitmap-word area: they are written only after the
+  // barrier that ends every wave's decode, and the decode keeps its bitmap
+  // words in registers (so two workgroups with 112 adapter ranks still share
+  // a CU).  After the values area: the tile's B_cat rows [16][r_cat].
+  u32x4_t* const tl = reinterpret_cast<u32x4_t*>(L.masks);
+  uint16_t* const bl = reinterpret_cast<uint16_t*>(smem + sizeof(Lds) + a.vals_bytes);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -512,13 +519,14 @@ size_t fwd_small_vals_bytes(int vcap) {
   return ((vals > red ? vals : red) + 15) / 16 * 16;
 }
 
-size_t fwd_small_lds_bytes(int vcap, int tl_bytes, int bl_bytes) {
-  return sizeof(Lds) + fwd_small_vals_bytes(vcap) + (size_t)tl_bytes + (size_t)bl_bytes;
+size_t fwd_small_lds_bytes(int vcap, int bl_bytes) {
+  return sizeof(Lds) + fwd_small_vals_bytes(vcap) + (size_t)bl_bytes;
 }
 
 hipError_t launch_fwd_small(const SmallFwdArgs& a, hipStream_t s) {
   const int grid = a.n_tiles * a.splits + a.r_tiles * a.t_pieces;
-  const size_t lds = fwd_small_lds_bytes(a.vcap, a.tl_bytes, a.bl_bytes);
+  if (a.tl_bytes > 8 * 1024) return hipErrorInvalidValue;  // (r_cat <= 256)
+  const size_t lds = fwd_small_lds_bytes(a.vcap, a.bl_bytes);
   // one weight workgroup per CU at most: all resident in one round
   if ((int64_t)a.n_tiles * a.splits <= kCus)
     hipLaunchKernelGGL(fwd_small_kernel<true>, dim3(grid), dim3(kThreads), lds, s, a);

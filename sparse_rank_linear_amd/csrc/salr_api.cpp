@@ -95,7 +95,7 @@ FwdLayout fwd_layout(int64_t N, int64_t K, int32_t n_keep, int32_t r_cat, int64_
   const auto vcap_for = [&](int64_t range) {
     return salr::fwd_small_vcap(std::min<int64_t>(range, n_keep), range >= K && n_keep % 8 == 0);
   };
-  const auto lds_for = [&](int64_t range) { return salr::fwd_small_lds_bytes(vcap_for(range), L.tl_bytes, L.bl_bytes); };
+  const auto lds_for = [&](int64_t range) { return salr::fwd_small_lds_bytes(vcap_for(range), L.bl_bytes); };
   L.range = 0;
   if (K <= salr::kMaxRangeCols && lds_for(K) <= kSmallLdsBudget && (L.n_tiles >= kFillWgs || K <= 1024)) {
     L.range = (int)K;

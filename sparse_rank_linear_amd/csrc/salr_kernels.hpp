@@ -40,7 +40,7 @@ struct SmallFwdArgs {
   int32_t t_pieces;        // K ranges of T pieces, t_chunks * 1024 columns each
   int32_t t_chunks;
   int32_t vals_bytes;      // LDS bytes of the values area
-  int32_t tl_bytes;        // LDS bytes of the T operands (r_pad / 32 chunks x 1 KB)
+  int32_t tl_bytes;        // bytes of the T operands (r_pad / 32 chunks x 1 KB, in the bitmap-word area)
   int32_t bl_bytes;        // LDS bytes of the B_cat rows (16 * r_cat * 2, rounded up to 16)
   int32_t psleep;          // one-round launches: producers' start delay in units of 64 clocks
   uint64_t* tickets;       // {count, epoch} ticket words of the launch tags
@@ -51,7 +51,7 @@ struct SmallFwdArgs {
 hipError_t launch_fwd_small(const SmallFwdArgs& a, hipStream_t s);
 size_t fwd_small_vals_bytes(int vcap);
 // Dynamic LDS bytes of one few-row workgroup.
-size_t fwd_small_lds_bytes(int vcap, int tl_bytes, int bl_bytes);
+size_t fwd_small_lds_bytes(int vcap, int bl_bytes);
 // LDS chunks per row for rows whose staged values never exceed `cap`.  The
 // first value sits at slot 0..7 of the first chunk (always 0 when
 // `aligned_start`), and a decode window reads at most 5 slots past one past
