@@ -83,7 +83,19 @@ typedef struct salr_layer {
   uint32_t* offsets;/* [N][ceil(K/1024)]                                    */
   uint16_t* a_cat;  /* [r_cat][K]                                           */
   uint16_t* b_cat;  /* [N][r_cat]                                           */
+  /* Parts of a fused layer (salr_fuse_layers fills these; 0 = one part).
+   * Part p owns rows part_rows[0] + ... + part_rows[p-1] onward and the
+   * adapter ranks part_ranks[0] + ... + part_ranks[p-1] onward; b_cat is
+   * zero outside each part's block.  The forward then reads and multiplies
+   * only a row tile's own block (when every part has a multiple of 16 rows
+   * and of 8 ranks); results are the same either way. */
+  int32_t n_parts;  /* 0 (set it so for an encoded layer) or 1: one part;
+                     * at most SALR_MAX_PARTS; the parts' rows must sum to
+                     * N and their ranks to r_cat (else INVALID_ARG)        */
+  int32_t part_rows[8];
+  int32_t part_ranks[8];
 } salr_layer_t;
+#define SALR_MAX_PARTS 8
 
 /* Byte sizes of every caller-allocated buffer. */
 typedef struct salr_sizes {
@@ -203,9 +215,11 @@ int salr_linear_forward(const salr_layer_t* L, const uint16_t* X, int64_t M,
  *          r_cat = sum r_cat_p (<= 256) and the five buffer pointers, sized
  *          by salr_query_sizes(N, K, n_keep, 0, r_cat, ...); its buffers must
  *          not overlap any part's.  They are overwritten.
- * Asynchronous on `stream` (device-to-device copies and one small kernel
- * per part).  Errors: INVALID_ARG (nulls, alignment, mismatched K or n_keep,
- * sums that disagree with `out`, limits), HIP.
+ * The parts' rows and ranks are recorded in out->n_parts, part_rows and
+ * part_ranks.  Asynchronous on `stream` (device-to-device copies and one
+ * small kernel per part).  Errors: INVALID_ARG (nulls, alignment, mismatched
+ * K or n_keep, sums that disagree with `out`, more than 8 parts, limits),
+ * HIP.
  */
 int salr_fuse_layers(const salr_layer_t* const* parts, int32_t n_parts,
                      salr_layer_t* out, void* stream);

@@ -54,6 +54,9 @@ class salr_layer_t(C.Structure):
         ("offsets", C.c_void_p),
         ("a_cat", C.c_void_p),
         ("b_cat", C.c_void_p),
+        ("n_parts", C.c_int32),
+        ("part_rows", C.c_int32 * 8),
+        ("part_ranks", C.c_int32 * 8),
     ]
 
 
@@ -164,6 +167,7 @@ class SalrLayer:
     offsets: object
     a_cat: object
     b_cat: object
+    parts: tuple = ()  # ((rows, ranks), ...) of a fused layer (salr_fuse_layers)
 
     @classmethod
     def empty(cls, N, K, n_keep, r_svd, r_cat, device="cuda"):
@@ -210,10 +214,14 @@ class SalrLayer:
         d.offsets = self.offsets.data_ptr()
         d.a_cat = self.a_cat.data_ptr() if self.r_cat else None
         d.b_cat = self.b_cat.data_ptr() if self.r_cat else None
+        d.n_parts = len(self.parts)
+        for p, (rows, ranks) in enumerate(self.parts):
+            d.part_rows[p], d.part_ranks[p] = rows, ranks
         return d
 
     def clone(self) -> "SalrLayer":
         c = SalrLayer.empty(self.N, self.K, self.n_keep, self.r_svd, self.r_cat, self.masks.device)
+        c.parts = self.parts
         for name in ("masks", "values", "offsets", "a_cat", "b_cat"):
             getattr(c, name).copy_(getattr(self, name))
         return c
@@ -319,4 +327,5 @@ def fuse(layers, stream=None) -> SalrLayer:
     od = out.descriptor()
     st = _lib().salr_fuse_layers(arr, len(descs), C.byref(od), _stream_ptr(stream))
     _check(st, "salr_fuse_layers")
+    out.parts = tuple((od.part_rows[p], od.part_ranks[p]) for p in range(od.n_parts))
     return out

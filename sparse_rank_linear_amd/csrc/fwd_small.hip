@@ -198,6 +198,17 @@ void fwd_small_kernel(SmallFwdArgs a) {
   const int64_t row0 = (int64_t)tile * kRows;
   const int col0 = rng * a.range;
   const int ncols = min(a.range, a.K - col0);
+  // This tile's adapter ranks [rlo, rlo + rn): all of them, or in a fused
+  // layer the block of the part that owns the tile (B_cat is zero outside
+  // it); its B_cat rows sit in LDS with row stride bstride.
+  int rlo = 0, rn = a.r_cat;
+  for (int p = 0; p < a.nparts; ++p)
+    if (tile < a.part_tile_end[p]) {
+      rlo = a.part_rank0[p];
+      rn = a.part_nrank[p];
+      break;
+    }
+  const int bstride = a.nparts > 0 ? rn : a.r_cat;
   const int nsteps = (ncols + 31) / 32;
   // steps per wave, even so that every wave starts on a bitmap word (<= kMaxSteps)
   const int spw = 2 * ((nsteps + 2 * kWaves - 1) / (2 * kWaves));
@@ -264,8 +275,21 @@ void fwd_small_kernel(SmallFwdArgs a) {
         }
       }
     }
-    // This tile's B_cat rows.
-    if (a.r_cat > 0) {
+    // This tile's B_cat rows (in a fused layer only its part's ranks, 16-byte
+    // chunks: every part's rank count and offset is a multiple of 8).
+    if (a.nparts > 0) {
+      const int cpr = rn / 8;
+      const int nch = rows_here * cpr;
+      const uint32_t* src0 = reinterpret_cast<const uint32_t*>(a.b_cat + row0 * a.r_cat + rlo);
+      for (int b = lw; b * 64 < nch; b += lws) {
+        const int cc = b * 64 + lane;
+        if (cc < nch) {
+          const int r = cc / cpr, q = cc - r * cpr;
+          __builtin_amdgcn_global_load_lds(src0 + ((size_t)r * a.r_cat + 8 * q) / 2,
+                                           reinterpret_cast<uint32_t*>(bl) + b * 256, 16, 0, 0);
+        }
+      }
+    } else if (a.r_cat > 0) {
       const int64_t bbytes = (int64_t)rows_here * a.r_cat * 2;
       copy_chunks_to_lds(reinterpret_cast<const uint32_t*>(a.b_cat + row0 * a.r_cat), reinterpret_cast<uint32_t*>(bl),
                          (bbytes + 15) / 16, lw, lws, lane);
@@ -362,9 +386,9 @@ void fwd_small_kernel(SmallFwdArgs a) {
   // rng + splits, ...; wave k reads chunk k's T operand after the decode.
   // Lane (i, g) needs T[token i][32q + 8g .. +7]: tile 2q + g/2, i.e. the
   // words of lanes i + 16 g' (g' = 2(g % 2), +1) there.
-  const int n_chunks = a.r_pad / 32;
-  const int n_own = a.r_cat > 0 && rng < n_chunks ? (n_chunks - rng + a.splits - 1) / a.splits : 0;
-  const int my_chunk = rng + wave * a.splits;
+  const int clo = rlo / 32, n_chunks = (rlo + rn + 31) / 32 - clo;  // 32-rank chunks of [rlo, rlo + rn)
+  const int n_own = rn > 0 && rng < n_chunks ? (n_chunks - rng + a.splits - 1) / a.splits : 0;
+  const int my_chunk = clo + rng + wave * a.splits;
   const int tj = 2 * my_chunk + (g >> 1);
   const bool t_live = wave < n_own && tj < a.r_tiles;
   const uint64_t* tsrc = a.tfinal + ((size_t)tj * 64 + i + 32 * (g & 1)) * 2;
@@ -477,11 +501,14 @@ void fwd_small_kernel(SmallFwdArgs a) {
   // Low-rank term for this workgroup's chunks: acc += B_cat^T[rows, chunk]
   // T^T[chunk, :], as extra K steps (T already rounded to bf16).
   for (int k = 0; k < n_own; ++k) {
-    const int rb = 32 * (rng + k * a.splits) + 8 * g;
+    const int rb = 32 * (clo + rng + k * a.splits) + 8 * g;
     u32x4_t wv;
-    if (a.r_cat % 8 == 0) {
-      // eight ranks in one aligned 16-byte read (ranks past r_cat: zero)
-      wv = (i < rows_here && rb < a.r_cat) ? *reinterpret_cast<const u32x4_t*>(bl + i * a.r_cat + rb) : zero_u4();
+    if (bstride % 8 == 0) {
+      // eight ranks in one aligned 16-byte read (ranks outside the tile's
+      // block: zero)
+      const int rr = rb - rlo;
+      wv = (i < rows_here && rr >= 0 && rr < rn) ? *reinterpret_cast<const u32x4_t*>(bl + i * bstride + rr)
+                                                  : zero_u4();
     } else {
       uint32_t w[4];
 #pragma unroll

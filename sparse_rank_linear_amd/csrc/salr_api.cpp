@@ -81,13 +81,16 @@ struct FwdLayout {
   size_t tsum, tfinal, ypart, T, ltpart, ylarge, total;
 };
 
-FwdLayout fwd_layout(int64_t N, int64_t K, int32_t n_keep, int32_t r_cat, int64_t M_max) {
+// r_win: the most adapter ranks one row tile multiplies (r_cat, or a fused
+// layer's largest part block); it sizes the few-row B_cat rows in LDS.
+FwdLayout fwd_layout(int64_t N, int64_t K, int32_t n_keep, int32_t r_cat, int64_t M_max, int32_t r_win = -1) {
+  if (r_win < 0) r_win = r_cat;
   FwdLayout L{};
   L.n_tiles = (int)cdiv(N, 16);
   L.r_tiles = (int)cdiv(r_cat, 16);
   L.r_pad_small = (int)align_up((size_t)std::max(L.r_tiles, 1) * 16, 32);
   L.tl_bytes = r_cat > 0 ? (L.r_pad_small / 32) * 1024 : 0;
-  L.bl_bytes = r_cat > 0 ? (int)align_up((size_t)16 * r_cat * 2, 16) : 0;
+  L.bl_bytes = r_win > 0 ? (int)align_up((size_t)16 * r_win * 2, 16) : 0;
   // Few-row column ranges: whole rows when they fit (no lookup-table round
   // trip), else the widest range that fits; narrower ranges while there are
   // too few workgroups to occupy the GPU.
@@ -177,7 +180,7 @@ extern "C" {
 int salr_fuse_layers(const salr_layer_t* const* parts, int32_t n_parts, salr_layer_t* out, void* stream) {
   if (!parts || !out || n_parts < 1) return SALR_ERR_INVALID_ARG;
   int64_t N = 0;
-  int32_t r_cat = 0;
+  int32_t r_cat = 0, n_rec = 0;  // n_rec: parts recorded (a fused part counts its own)
   for (int32_t p = 0; p < n_parts; ++p) {
     const salr_layer_t* L = parts[p];
     if (!L || !dims_ok(L->N, L->K, L->n_keep, L->r_cat)) return SALR_ERR_INVALID_ARG;
@@ -190,7 +193,10 @@ int salr_fuse_layers(const salr_layer_t* const* parts, int32_t n_parts, salr_lay
     N += L->N;
     r_cat += L->r_cat;
     if (r_cat > kMaxRank) return SALR_ERR_INVALID_ARG;
+    if (L->n_parts < 0 || L->n_parts > SALR_MAX_PARTS) return SALR_ERR_INVALID_ARG;
+    n_rec += L->n_parts > 1 ? L->n_parts : 1;
   }
+  if (n_rec > SALR_MAX_PARTS) return SALR_ERR_INVALID_ARG;
   if (out->N != N || out->r_cat != r_cat || !dims_ok(N, out->K, out->n_keep, r_cat)) return SALR_ERR_INVALID_ARG;
   if (!out->masks || !out->offsets || (out->n_keep > 0 && !out->values)) return SALR_ERR_INVALID_ARG;
   if (r_cat > 0 && (!out->a_cat || !out->b_cat)) return SALR_ERR_INVALID_ARG;
@@ -218,6 +224,23 @@ int salr_fuse_layers(const salr_layer_t* const* parts, int32_t n_parts, salr_lay
     row0 += L->N;
     rank0 += L->r_cat;
   }
+  // record the parts (a fused part's own parts in its place)
+  int32_t q = 0;
+  for (int32_t p = 0; p < n_parts; ++p) {
+    const salr_layer_t* L = parts[p];
+    if (L->n_parts > 1) {
+      for (int32_t e = 0; e < L->n_parts; ++e, ++q) {
+        out->part_rows[q] = L->part_rows[e];
+        out->part_ranks[q] = L->part_ranks[e];
+      }
+    } else {
+      out->part_rows[q] = (int32_t)L->N;
+      out->part_ranks[q] = L->r_cat;
+      ++q;
+    }
+  }
+  for (int32_t e = q; e < SALR_MAX_PARTS; ++e) out->part_rows[e] = out->part_ranks[e] = 0;
+  out->n_parts = q;
   return hipGetLastError() == hipSuccess ? SALR_OK : SALR_ERR_HIP;
 }
 
@@ -319,7 +342,25 @@ int salr_linear_forward(const salr_layer_t* L, const uint16_t* X, int64_t M, uin
     if (p && !aligned16(p)) return SALR_ERR_INVALID_ARG;
   if (static_cast<const void*>(X) == static_cast<const void*>(Y)) return SALR_ERR_INVALID_ARG;
   if (!ws || !aligned16(ws)) return SALR_ERR_WORKSPACE;
-  const FwdLayout W = fwd_layout(L->N, L->K, L->n_keep, L->r_cat, M);
+  // A fused layer's parts: each row tile multiplies only its part's block
+  // of ranks when every part has whole row tiles and 8-aligned ranks.
+  if (L->n_parts < 0 || L->n_parts > SALR_MAX_PARTS) return SALR_ERR_INVALID_ARG;
+  bool windows = L->n_parts > 1;
+  int32_t r_win = L->r_cat;
+  if (L->n_parts > 1) {
+    int64_t rows = 0, ranks = 0;
+    int32_t widest = 0;
+    for (int p = 0; p < L->n_parts; ++p) {
+      if (L->part_rows[p] < 1 || L->part_ranks[p] < 0) return SALR_ERR_INVALID_ARG;
+      rows += L->part_rows[p];
+      ranks += L->part_ranks[p];
+      widest = std::max(widest, L->part_ranks[p]);
+      windows = windows && L->part_rows[p] % 16 == 0 && L->part_ranks[p] % 8 == 0;
+    }
+    if (rows != L->N || ranks != L->r_cat) return SALR_ERR_INVALID_ARG;
+    if (windows) r_win = widest;
+  }
+  const FwdLayout W = fwd_layout(L->N, L->K, L->n_keep, L->r_cat, M, r_win);
   if (ws_bytes < W.total) return SALR_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
@@ -386,6 +427,18 @@ int salr_linear_forward(const salr_layer_t* L, const uint16_t* X, int64_t M, uin
     // (about 1 us with up to 48 producers; with more, T is on the critical
     // path and they start at once: measured on 4096 x 4096 at r_cat 80 / 112)
     a.psleep = W.r_tiles * W.t_pieces <= 48 ? 40 : 0;
+    a.nparts = 0;
+    if (windows) {
+      int32_t tile_end = 0, rank0 = 0;
+      for (int p = 0; p < L->n_parts; ++p) {
+        tile_end += L->part_rows[p] / 16;
+        a.part_tile_end[p] = tile_end;
+        a.part_rank0[p] = rank0;
+        a.part_nrank[p] = L->part_ranks[p];
+        rank0 += L->part_ranks[p];
+      }
+      a.nparts = L->n_parts;
+    }
     a.tickets = at<uint64_t>(ws, kCounterTickets);
     a.err = at<uint32_t>(ws, kCounterSync + 8);
     a.ycount = at<uint32_t>(ws, kCounterY);

@@ -43,6 +43,10 @@ struct SmallFwdArgs {
   int32_t tl_bytes;        // bytes of the T operands (r_pad / 32 chunks x 1 KB, in the bitmap-word area)
   int32_t bl_bytes;        // LDS bytes of the B_cat rows (16 * r_cat * 2, rounded up to 16)
   int32_t psleep;          // one-round launches: producers' start delay in units of 64 clocks
+  // fused layers (0 parts: one block of r_cat ranks): part p owns the row
+  // tiles below part_tile_end[p] and the ranks [part_rank0[p], + part_nrank[p])
+  int32_t nparts;
+  int32_t part_tile_end[8], part_rank0[8], part_nrank[8];
   uint64_t* tickets;       // {count, epoch} ticket words of the launch tags
   uint32_t* err;           // set nonzero when a wait times out
   uint32_t* ycount;        // [n_tiles]

@@ -108,6 +108,16 @@ def test_forward_validation_paths():
     assert _fwd(_layer(), ws=0) == -3                     # null workspace
     assert _fwd(_layer(), ws_bytes=1024) == -3            # workspace too small
     assert _fwd(_layer(), ws=0x40000008) == -3            # misaligned workspace
+    d = _layer(N=64, r_cat=16)
+    d.n_parts = 9
+    assert _fwd(d) == -1                                  # more parts than recorded slots
+    d.n_parts = 2
+    d.part_rows[0], d.part_rows[1], d.part_ranks[0], d.part_ranks[1] = 32, 16, 8, 8
+    assert _fwd(d) == -1                                  # parts' rows do not sum to N
+    d.part_rows[1], d.part_ranks[1] = 32, 16
+    assert _fwd(d) == -1                                  # parts' ranks do not sum to r_cat
+    d.part_rows[0], d.part_rows[1], d.part_ranks[0], d.part_ranks[1] = 64, 0, 16, 0
+    assert _fwd(d) == -1                                  # an empty part
 
 
 def _enc(W=0x50000000, N=64, K=64, n_keep=32, r_svd=4, out=None, ws=0x60000000, ws_bytes=1 << 30, opts=None,
@@ -165,6 +175,14 @@ def test_fuse_validation_paths():
     d = _layer(96, 64, 32, 12, base=0x30000000)
     d.values = 0x30100008
     assert _fuse([a, b], d) == -1                         # misaligned output
+    nine = [_layer(16, 64, 32, 0, base=0x10000000 * (i + 1)) for i in range(9)]
+    assert _fuse(nine, _layer(144, 64, 32, 0, base=0xa0000000)) == -1   # more than 8 parts
+    f = _layer(96, 64, 32, 12, base=0x30000000)
+    f.n_parts = 8
+    for p in range(8):
+        f.part_rows[p], f.part_ranks[p] = 12, 0
+    f.part_ranks[0] = 12
+    assert _fuse([a, f], _layer(160, 64, 32, 20, base=0x50000000)) == -1  # 1 + 8 recorded parts
 
 
 def test_python_wrapper_requires_library(monkeypatch, tmp_path):

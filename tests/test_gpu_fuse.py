@@ -19,6 +19,7 @@ CASES = [
     (2048, 1024, [(1024, 16, (8,)), (256, 8, (8,)), (256, 8, (8,))], (1, 16, 300)),  # q/k/v-like
     (1032, 500, [(200, 0, (8,)), (200, 0, (8,))], (3, 16, 64)),                   # gate/up-like, ragged K
     (4096, 2048, [(80, 0, ()), (48, 0, ())], (16,)),                              # no adapters at all
+    (1024, 400, [(256, 32, (8,)), (512, 0, (8,)), (128, 48, (8,)), (64, 0, ())], (1, 5, 16, 48)),  # rank windows
 ]
 
 
@@ -47,6 +48,7 @@ def test_fuse_matches_oracle(case):
     assert np.array_equal(got["offsets"], ref["offsets"])
     assert np.array_equal(got["a_cat"], ref["A_cat"].T)
     assert np.array_equal(got["b_cat"], ref["B_cat"].T)
+    assert fused.parts == tuple((l.N, l.r_cat) for l in layers)
 
     ws = srl.forward_workspace(fused, max(Ms))
     for M in Ms:
@@ -57,3 +59,26 @@ def test_fuse_matches_oracle(case):
         mr, nw = errors(to_host_bits(Y), Yref)
         assert wait_error(ws) == 0
         assert mr <= TOL_MAX_REL and nw <= TOL_NORMWISE, (M, mr, nw)
+
+
+def test_fuse_of_a_fused_layer_records_the_inner_parts():
+    """Fusing a fused layer keeps its parts: the record lists the innermost
+    parts in row order, and the forward still matches the oracle."""
+    import sparse_rank_linear_amd as srl
+
+    K, n_keep = 512, 200
+    specs = [(128, 8, ()), (64, 0, (8,)), (96, 16, (8,))]
+    parts = [_part(N, K, n_keep, rs, lr, seed=7 + i) for i, (N, rs, lr) in enumerate(specs)]
+    layers = [upload_encoded(p, K, rs) for p, (N, rs, lr) in zip(parts, specs)]
+    inner = srl.fuse(layers[:2])
+    outer = srl.fuse([inner, layers[2]])
+    assert outer.parts == ((128, 8), (64, 8), (96, 24))
+    ref = osl.fuse(parts)
+    ws = srl.forward_workspace(outer, 16)
+    X = synth.make_x(K, 16, seed=11)
+    say(f"nested fuse K={K} N={outer.N} r_cat={outer.r_cat} M=16")
+    Y = srl.linear_forward(outer, to_dev(X), ws=ws)
+    Yref = osl.forward(X, ref["masks"], ref["values"], K, ref["A_cat"], ref["B_cat"])
+    mr, nw = errors(to_host_bits(Y), Yref)
+    assert wait_error(ws) == 0
+    assert mr <= TOL_MAX_REL and nw <= TOL_NORMWISE, (mr, nw)
