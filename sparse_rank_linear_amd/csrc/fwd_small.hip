@@ -155,7 +155,9 @@ __device__ __forceinline__ void copy_chunks_to_lds(const uint32_t* src, uint32_t
 
 // kOneRound: every weight workgroup is resident at once, so the T producers
 // sit on CUs beside some of them (see the producer section).
-template <bool kOneRound>
+// kWin: a fused layer's parts bound each row tile's adapter ranks (a.nparts
+// > 0); the plain instance keeps the whole-r_cat code.
+template <bool kOneRound, bool kWin>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void fwd_small_kernel(SmallFwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -202,13 +204,14 @@ void fwd_small_kernel(SmallFwdArgs a) {
   // layer the block of the part that owns the tile (B_cat is zero outside
   // it); its B_cat rows sit in LDS with row stride bstride.
   int rlo = 0, rn = a.r_cat;
-  for (int p = 0; p < a.nparts; ++p)
-    if (tile < a.part_tile_end[p]) {
-      rlo = a.part_rank0[p];
-      rn = a.part_nrank[p];
-      break;
-    }
-  const int bstride = a.nparts > 0 ? rn : a.r_cat;
+  if (kWin)
+    for (int p = 0; p < a.nparts; ++p)
+      if (tile < a.part_tile_end[p]) {
+        rlo = a.part_rank0[p];
+        rn = a.part_nrank[p];
+        break;
+      }
+  const int bstride = kWin ? rn : a.r_cat;
   const int nsteps = (ncols + 31) / 32;
   // steps per wave, even so that every wave starts on a bitmap word (<= kMaxSteps)
   const int spw = 2 * ((nsteps + 2 * kWaves - 1) / (2 * kWaves));
@@ -277,7 +280,7 @@ void fwd_small_kernel(SmallFwdArgs a) {
     }
     // This tile's B_cat rows (in a fused layer only its part's ranks, 16-byte
     // chunks: every part's rank count and offset is a multiple of 8).
-    if (a.nparts > 0) {
+    if (kWin) {
       const int cpr = rn / 8;
       const int nch = rows_here * cpr;
       const uint32_t* src0 = reinterpret_cast<const uint32_t*>(a.b_cat + row0 * a.r_cat + rlo);
@@ -386,7 +389,8 @@ void fwd_small_kernel(SmallFwdArgs a) {
   // rng + splits, ...; wave k reads chunk k's T operand after the decode.
   // Lane (i, g) needs T[token i][32q + 8g .. +7]: tile 2q + g/2, i.e. the
   // words of lanes i + 16 g' (g' = 2(g % 2), +1) there.
-  const int clo = rlo / 32, n_chunks = (rlo + rn + 31) / 32 - clo;  // 32-rank chunks of [rlo, rlo + rn)
+  // 32-rank chunks of [rlo, rlo + rn)
+  const int clo = kWin ? rlo / 32 : 0, n_chunks = kWin ? (rlo + rn + 31) / 32 - clo : a.r_pad / 32;
   const int n_own = rn > 0 && rng < n_chunks ? (n_chunks - rng + a.splits - 1) / a.splits : 0;
   const int my_chunk = clo + rng + wave * a.splits;
   const int tj = 2 * my_chunk + (g >> 1);
@@ -503,12 +507,15 @@ void fwd_small_kernel(SmallFwdArgs a) {
   for (int k = 0; k < n_own; ++k) {
     const int rb = 32 * (clo + rng + k * a.splits) + 8 * g;
     u32x4_t wv;
-    if (bstride % 8 == 0) {
+    if (kWin) {
       // eight ranks in one aligned 16-byte read (ranks outside the tile's
       // block: zero)
       const int rr = rb - rlo;
       wv = (i < rows_here && rr >= 0 && rr < rn) ? *reinterpret_cast<const u32x4_t*>(bl + i * bstride + rr)
                                                   : zero_u4();
+    } else if (a.r_cat % 8 == 0) {
+      // eight ranks in one aligned 16-byte read (ranks past r_cat: zero)
+      wv = (i < rows_here && rb < a.r_cat) ? *reinterpret_cast<const u32x4_t*>(bl + i * a.r_cat + rb) : zero_u4();
     } else {
       uint32_t w[4];
 #pragma unroll
@@ -555,10 +562,17 @@ hipError_t launch_fwd_small(const SmallFwdArgs& a, hipStream_t s) {
   if (a.tl_bytes > 8 * 1024) return hipErrorInvalidValue;  // (r_cat <= 256)
   const size_t lds = fwd_small_lds_bytes(a.vcap, a.bl_bytes);
   // one weight workgroup per CU at most: all resident in one round
-  if ((int64_t)a.n_tiles * a.splits <= kCus)
-    hipLaunchKernelGGL(fwd_small_kernel<true>, dim3(grid), dim3(kThreads), lds, s, a);
-  else
-    hipLaunchKernelGGL(fwd_small_kernel<false>, dim3(grid), dim3(kThreads), lds, s, a);
+  const bool one_round = (int64_t)a.n_tiles * a.splits <= kCus;
+  if (a.nparts > 0) {
+    if (one_round)
+      hipLaunchKernelGGL((fwd_small_kernel<true, true>), dim3(grid), dim3(kThreads), lds, s, a);
+    else
+      hipLaunchKernelGGL((fwd_small_kernel<false, true>), dim3(grid), dim3(kThreads), lds, s, a);
+  } else if (one_round) {
+    hipLaunchKernelGGL((fwd_small_kernel<true, false>), dim3(grid), dim3(kThreads), lds, s, a);
+  } else {
+    hipLaunchKernelGGL((fwd_small_kernel<false, false>), dim3(grid), dim3(kThreads), lds, s, a);
+  }
   return hipGetLastError();
 }
 
