@@ -270,9 +270,18 @@ __global__ __launch_bounds__(64 * WM * WN) void fwd_large_kernel(LargeFwdArgs a)
   // ---- low-rank term as extra K tiles: Y^T += B_cat^T[n, :] T[m, :]^T, where
   // T = X A_cat is the sum of the K-split partials (written by the previous
   // launch), rounded to bf16 before it meets B_cat.
-  if (a.r_cat > 0 && split == 0) {
+  // (a fused layer: only the ranks of the part that owns rows n0.., B_cat
+  // being zero outside them; every part holds whole tiles)
+  int rlo = 0, rhi = a.r_cat;
+  for (int p = 0; p < a.nparts; ++p)
+    if (n0 < a.part_row_end[p]) {
+      rlo = a.part_rank0[p];
+      rhi = rlo + a.part_nrank[p];
+      break;
+    }
+  if (rhi > rlo && split == 0) {
     const size_t split_stride = (size_t)a.M * a.r_pad;
-    for (int r0 = 0; r0 < a.r_cat; r0 += 64) {
+    for (int r0 = rlo; r0 < rhi; r0 += 64) {
 #pragma unroll
       for (int u = 0; u < C::XDMA; ++u) {
         const int c = tid + C::kThreads * u;
@@ -301,8 +310,8 @@ __global__ __launch_bounds__(64 * WM * WN) void fwd_large_kernel(LargeFwdArgs a)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int ra = r0 + cbeg + c8 + 2 * e;
-          const uint32_t lo = (row_ok && ra < a.r_cat) ? a.b_cat[grow * a.r_cat + ra] : 0u;
-          const uint32_t hi = (row_ok && ra + 1 < a.r_cat) ? a.b_cat[grow * a.r_cat + ra + 1] : 0u;
+          const uint32_t lo = (row_ok && ra < rhi) ? a.b_cat[grow * a.r_cat + ra] : 0u;
+          const uint32_t hi = (row_ok && ra + 1 < rhi) ? a.b_cat[grow * a.r_cat + ra + 1] : 0u;
           w[e] = lo | (hi << 16);
         }
         wl0[swz(drow, (cbeg + c8) / 8)] = u32x4_t{w[0], w[1], w[2], w[3]};

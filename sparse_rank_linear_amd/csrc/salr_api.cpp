@@ -486,6 +486,22 @@ int salr_linear_forward(const salr_layer_t* L, const uint16_t* X, int64_t M, uin
     a.ksplit = (int32_t)cdiv(nk, a.kt_per);
     a.ypart = at<float>(ws, W.ylarge);
     a.x_off32 = M * L->K * 2 < (int64_t(1) << 32) ? 1 : 0;
+    a.nparts = 0;
+    if (windows) {
+      bool whole = true;
+      for (int p = 0; p < L->n_parts; ++p) whole = whole && L->part_rows[p] % 256 == 0;
+      if (whole) {
+        int32_t row_end = 0, rank0 = 0;
+        for (int p = 0; p < L->n_parts; ++p) {
+          row_end += L->part_rows[p];
+          a.part_row_end[p] = row_end;
+          a.part_rank0[p] = rank0;
+          a.part_nrank[p] = L->part_ranks[p];
+          rank0 += L->part_ranks[p];
+        }
+        a.nparts = L->n_parts;
+      }
+    }
     err = salr::launch_fwd_large(a, s);
   }
   return err == hipSuccess ? SALR_OK : SALR_ERR_HIP;

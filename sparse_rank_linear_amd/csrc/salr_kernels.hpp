@@ -134,6 +134,11 @@ struct LargeFwdArgs {
   int32_t ksplit, kt_per;
   float* ypart;
   int32_t x_off32;         // 1 when M * K * 2 < 2^32 (X tile loads from 32-bit offsets)
+  // Fused layer whose parts all have whole 256-row blocks (else nparts = 0):
+  // rows [part_row_end[p-1], part_row_end[p]) use adapter ranks
+  // [part_rank0[p], part_rank0[p] + part_nrank[p]) only.
+  int32_t nparts;
+  int32_t part_row_end[8], part_rank0[8], part_nrank[8];
 };
 hipError_t launch_fwd_large(const LargeFwdArgs& a, hipStream_t s);
 // Output tiles of the many-row kernel and the K splits it takes for M rows
