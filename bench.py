@@ -181,7 +181,7 @@ FUSED_GROUPS = {
 }
 
 
-def run_fused(dev):
+def run_fused(dev, only=None, tokens=None):
     """One JSON line per (group, token count): the fused layer against the
     parts called one after another, same inputs, rotating copies."""
     import torch
@@ -189,6 +189,8 @@ def run_fused(dev):
     from sparse_rank_linear_amd import synth
 
     for gname, group in FUSED_GROUPS.items():
+        if only and gname != only:
+            continue
         parts = []
         for i, (wname, rows) in enumerate(group):
             wl = synth.WORKLOADS[wname]
@@ -200,7 +202,7 @@ def run_fused(dev):
         fused = srl.fuse(parts)
         torch.cuda.synchronize()
         K = fused.K
-        for M in (1, 16, 2048):
+        for M in (tokens,) if tokens else (1, 16, 2048):
             X = _dev_bits(synth.make_x(K, M, seed=11), dev)
             copies = 1 if M > 16 else max(2, -(-600_000_000 // fused.compressed_bytes()))
             sep = 0.0
@@ -211,9 +213,17 @@ def run_fused(dev):
             fl = [fused] + [fused.clone() for _ in range(copies - 1)]
             t = measure_decode(fl, X, srl.forward_workspace(fused, M), 32, 4)
             del fl
-            print(json.dumps({"fused": gname, "N": fused.N, "K": K, "r_cat": fused.r_cat, "M": M,
-                              "separate_us": round(sep * 1e6, 2), "fused_us": round(t * 1e6, 2),
-                              "speedup": round(sep / t, 3)}), flush=True)
+            # algorithmic bytes: the parts' encodings (the zero blocks of the
+            # fused B_cat are not needed), X and Y
+            alg = sum(p.compressed_bytes() for p in parts) + 2 * M * K + 2 * M * fused.N
+            line = {"fused": gname, "N": fused.N, "K": K, "r_cat": fused.r_cat, "M": M,
+                    "separate_us": round(sep * 1e6, 2), "fused_us": round(t * 1e6, 2),
+                    "speedup": round(sep / t, 3), "algorithmic_bytes": alg,
+                    "fused_GBs": round(alg / t / 1e9, 1), "hbm_frac": round(alg / t / 1e9 / HBM_PEAK_GBS, 4)}
+            if M > 16:
+                tf = 2 * M * fused.N * K / t / 1e12
+                line.update(tflops_dense_equiv=round(tf, 2), mfma_frac_dense_equiv=round(tf / MFMA_BF16_PEAK_TFLOPS, 4))
+            print(json.dumps(line), flush=True)
             torch.cuda.empty_cache()
         del parts, fused
 
@@ -286,7 +296,10 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="headline line only (no sweep/prefill/cpu)")
     ap.add_argument("--layer", default=None,
                     help="time one workload of the synthetic table (with --tokens) and exit")
-    ap.add_argument("--tokens", type=int, default=16, help="token count for --layer")
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="token count for --layer (default 16) or --fused (default 1, 16 and 2048)")
+    ap.add_argument("--group", default=None, choices=sorted(FUSED_GROUPS),
+                    help="with --fused: only this projection group")
     ap.add_argument("--fused", action="store_true",
                     help="time fused projections (salr_fuse_layers) against separate calls, then exit")
     ap.add_argument("--configs", action="store_true",
@@ -316,10 +329,10 @@ def main():
         return
 
     if args.layer:
-        run_layer(dev, args.layer, args.tokens, args.steps, args.warmup)
+        run_layer(dev, args.layer, args.tokens or 16, args.steps, args.warmup)
         return
     if args.fused:
-        run_fused(dev)
+        run_fused(dev, args.group, args.tokens)
         return
     if args.configs:
         run_configs(dev)
