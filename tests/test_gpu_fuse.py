@@ -82,3 +82,51 @@ def test_fuse_of_a_fused_layer_records_the_inner_parts():
     mr, nw = errors(to_host_bits(Y), Yref)
     assert wait_error(ws) == 0
     assert mr <= TOL_MAX_REL and nw <= TOL_NORMWISE, (mr, nw)
+
+
+@pytest.mark.parametrize("M", [16, 2048])
+def test_fused_qkv_full_size_against_the_parts(M):
+    """The Llama-7B q/k/v projections (3 x 4096 x 4096, r_cat 3 x 80) fused
+    at full size: every sampled output row must match the oracle's forward
+    of its own part (the oracle's own encoding of that part's rows, seeded
+    adapters), so the rank windows of the few-row (M = 16) and many-row
+    (M = 2048) kernels are checked at the size the bench times."""
+    import torch
+    import sparse_rank_linear_amd as srl
+
+    wl = synth.WORKLOADS["llama7b_attn_4096"]
+    N, K, n_keep = wl.N, wl.K, wl.n_keep
+    rng = np.random.default_rng(77)
+    layers, refs = [], []
+    for p in range(3):
+        W = synth.make_w(N, K, seed=wl.seed + 30 + p)
+        a_cat = synth.make_w(wl.r_cat, K, seed=wl.seed + 40 + p, scale=0.01)   # [r][K]
+        b_cat = synth.make_w(N, wl.r_cat, seed=wl.seed + 50 + p, scale=0.01)   # [N][r]
+        enc, _ = srl.encode(to_dev(W), n_keep, 0)
+        layer = srl.SalrLayer.empty(N, K, n_keep, wl.r_svd, wl.r_cat)
+        for f in ("masks", "values", "offsets"):
+            getattr(layer, f).copy_(getattr(enc, f))
+        layer.a_cat.view(torch.int16).copy_(torch.from_numpy(a_cat.view(np.int16)))
+        layer.b_cat.view(torch.int16).copy_(torch.from_numpy(np.ascontiguousarray(b_cat).view(np.int16)))
+        rows = np.unique(np.concatenate([rng.choice(N, 10, replace=False), [0, N - 1]]))
+        keep = osl.select_keep(W[rows], n_keep)
+        refs.append((rows, osl.pack_masks(keep), osl.pack_values(W[rows], keep, n_keep), a_cat, b_cat[rows]))
+        layers.append(layer)
+        del enc
+    fused = srl.fuse(layers)
+    assert fused.parts == ((N, wl.r_cat),) * 3
+    del layers
+    X = synth.make_x(K, M, seed=wl.seed + 60 + M)
+    say(f"fused q/k/v full size: N={fused.N} K={K} r_cat={fused.r_cat} M={M}")
+    ws = srl.forward_workspace(fused, M)
+    Y = srl.linear_forward(fused, to_dev(X), ws=ws)
+    torch.cuda.synchronize()
+    assert wait_error(ws) == 0
+    tok = np.arange(M) if M <= 256 else np.sort(np.random.default_rng(M).choice(M, 256, replace=False))
+    for p, (rows, m_o, v_o, a_cat, b_rows) in enumerate(refs):
+        cols = torch.from_numpy(p * N + rows).cuda()
+        Yg = to_host_bits(Y[torch.from_numpy(tok).cuda()][:, cols])
+        Yref = osl.forward(X[tok], m_o, v_o, K, a_cat.T, b_rows.T)
+        mr, nw = errors(Yg, Yref)
+        say(f"  part {p}: {len(tok)} tokens x {len(rows)} rows: max_rel={mr:.3e} normwise={nw:.3e}")
+        assert mr <= TOL_MAX_REL and nw <= TOL_NORMWISE, (p, mr, nw)
