@@ -20,9 +20,20 @@ Printed JSON fields beyond the common contract:
                 per launch (compressed weight + X + Y) / mean launch time
   cpu_baseline  the float64 NumPy oracle's forward on the same layer shape
                 (host cores), for context
+  us_per_step_stats  median / p10 / p90 of the per-call mean over 10 more
+                replays of the timed graph
+  checks        the timed run checked: workspace wait-error word clear, the
+                timed output equal to an eager call bit for bit, and the same
+                launch configuration (with seeded adapters) against the
+                oracle on sampled rows; the script exits non-zero if any fails
+  measured_peaks  achievable HBM read rate and bf16 matrix-core rate from the
+                library's probe kernels; every fraction is also given
+                against them
   sweep         the same measurement at 1, 4 and 16 tokens
   prefill       a many-token case (11008x4096, 2048 tokens) against the bf16
-                matrix-core peak (dense-equivalent flops), for context
+                matrix-core peak (dense-equivalent and effective flops)
+  l70b_up_s50   the 70B-shaped layer (28672x8192, Student-t, 50%, r_cat 160)
+                at 8192 tokens, likewise
   encode        wall time of salr_encode for the headline layer
 
     python bench.py --configs
@@ -114,8 +125,11 @@ def _time_replay(g) -> float:
     return start.elapsed_time(end) / 1e3  # seconds
 
 
-def measure_decode(layers, X, ws, steps, warmup):
-    """Mean seconds per forward call over `steps` graph-replayed calls."""
+def measure_decode(layers, X, ws, steps, warmup, reps: int = 0, detail: bool = False):
+    """Mean seconds per forward call over `steps` graph-replayed calls (one
+    replay: the timed region).  With reps > 0, that many further replays
+    give the spread of the per-call mean (median, p10, p90).  With detail,
+    returns a dict with those, the output buffer and the last layer called."""
     import torch
     import sparse_rank_linear_amd as srl
 
@@ -128,7 +142,94 @@ def measure_decode(layers, X, ws, steps, warmup):
     g = _timed_graph(fns, steps)
     g.replay()  # first replay uploads the graph; untimed
     torch.cuda.synchronize()
-    return _time_replay(g) / steps
+    t = _time_replay(g) / steps
+    if not detail:
+        return t
+    extra = [_time_replay(g) / steps for _ in range(reps)]
+    q = np.percentile(np.array(extra), [10, 50, 90]) if extra else [t, t, t]
+    return {"mean": t, "p10": float(q[0]), "median": float(q[1]), "p90": float(q[2]), "replays": reps,
+            "Y": Y, "last_layer": layers[(steps - 1) % len(layers)]}
+
+
+def measure_peaks(dev):
+    """Achievable HBM read rate and bf16 matrix-core rate of this GPU from
+    the library's probe kernels (include/salr_probe.h): a 1 GiB buffer (four
+    times the Infinity Cache) read once per launch at several grid sizes,
+    and independent matrix-core chains in 4 waves per workgroup, 4
+    workgroups per CU.  Best of each, timed with events on the launch
+    stream."""
+    import torch
+    import sparse_rank_linear_amd as srl
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) / 1e3
+            best = t if best is None else min(best, t)
+        return best
+
+    buf = torch.zeros(1 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.empty(65536, dtype=torch.int32, device=dev)
+    read = {}
+    for wg in (256, 512, 1024, 2048, 4096):
+        nbytes = buf.numel()
+        t = timed(lambda: srl.probe_stream_read(buf, sink, wg), 5)
+        read[wg] = nbytes / t / 1e9
+    del buf
+    out = torch.empty(4096, dtype=torch.float32, device=dev)
+    mfma = {}
+    for shape in (0, 1):
+        flops = 1024 * 4 * 4000 * 131072
+        t = timed(lambda: srl.probe_mfma(out, 1024, 4000, shape), 3)
+        mfma["16x16x32" if shape == 0 else "32x32x16"] = flops / t / 1e12
+    best_wg = max(read, key=read.get)
+    return {"hbm_read_GBs": round(read[best_wg], 1), "hbm_read_workgroups": best_wg,
+            "hbm_read_by_grid": {str(k): round(v, 1) for k, v in read.items()},
+            "mfma_bf16_TFLOPs": round(max(mfma.values()), 1),
+            "mfma_bf16_by_shape": {k: round(v, 1) for k, v in mfma.items()}}
+
+
+def check_timed_output(wl, inp, layer, X_bits, X, ws, Y_timed, last_layer, dev):
+    """Checks of the timed run: (1) no bounded wait timed out (workspace
+    error word); (2) the timed output equals an eager call on the layer the
+    last timed step used, bit for bit (the kernels sum in a fixed order);
+    (3) the same launch configuration on this layer's bitmap and values with
+    seeded adapters of the same rank against the oracle's float64 forward
+    from its own encoding of sampled rows.  Returns a dict of results."""
+    import torch
+    import sparse_rank_linear_amd as srl
+    from oracle import bf16 as ob
+    from oracle import salr as osl
+    from sparse_rank_linear_amd import synth
+
+    res = {"wait_error": srl.wait_error(ws)}
+    Y2 = srl.linear_forward(last_layer, X, ws=ws)
+    torch.cuda.synchronize()
+    res["timed_equals_eager"] = bool(torch.equal(Y_timed.view(torch.int16), Y2.view(torch.int16)))
+    probe = layer.clone()
+    a_cat = synth.make_w(wl.r_cat, wl.K, seed=wl.seed + 201, scale=0.01)
+    b_cat = synth.make_w(wl.N, wl.r_cat, seed=wl.seed + 202, scale=0.01)
+    probe.a_cat.view(torch.int16).copy_(torch.from_numpy(a_cat.view(np.int16)))
+    probe.b_cat.view(torch.int16).copy_(torch.from_numpy(b_cat.view(np.int16)))
+    Y3 = srl.linear_forward(probe, X, ws=ws)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.random.default_rng(5).choice(wl.N, 14, replace=False), [0, wl.N - 1]]))
+    keep = osl.select_keep(inp.W[rows], wl.n_keep)
+    Yref = osl.forward(X_bits, osl.pack_masks(keep), osl.pack_values(inp.W[rows], keep, wl.n_keep), wl.K,
+                       a_cat.T, b_cat[rows].T)
+    Yg = ob.bits_to_f64(Y3[:, torch.from_numpy(rows).to(dev)].contiguous().view(torch.int16).cpu().numpy()
+                        .view(np.uint16))
+    res["oracle_max_rel_err"] = float(osl.max_rel_err(Yg, Yref))
+    res["wait_error"] = max(res["wait_error"], srl.wait_error(ws))
+    res["ok"] = res["wait_error"] == 0 and res["timed_equals_eager"] and res["oracle_max_rel_err"] <= 2e-2
+    return res
 
 
 def run_configs(dev):
@@ -353,15 +454,13 @@ def main():
     ws = srl.forward_workspace(layer, 16384)
     cbytes = layer.compressed_bytes()
 
-    def line_for(M, steps, warmup):
-        X = _dev_bits(synth.make_x(wl.K, M, seed=11), dev)
-        t = measure_decode(layers, X, ws, steps, warmup)
-        algo = cbytes + 2 * M * (wl.K + wl.N)
-        return t, algo
-
-    t, algo = line_for(wl.M, args.steps, args.warmup)
     M = wl.M
+    X = _dev_bits(inp.X, dev)
+    r = measure_decode(layers, X, ws, args.steps, args.warmup, reps=10, detail=True)
+    t = r["mean"]
+    algo = cbytes + 2 * M * (wl.K + wl.N)
     achieved = algo / t / 1e9
+    checks = check_timed_output(wl, inp, layer, inp.X, X, ws, r["Y"], r["last_layer"], dev)
     out = {
         "metric": METRIC,
         "value": round(cbytes / t / 1e9, 2),
@@ -378,35 +477,75 @@ def main():
         "config": {"workload": "llama7b_attn_4096x4096_decode", "N": wl.N, "K": wl.K, "M": M,
                    "sparsity": wl.sparsity, "n_keep": wl.n_keep, "r_svd": wl.r_svd, "r_cat": wl.r_cat,
                    "rotating_copies": COPIES, "compressed_weight_bytes": cbytes},
+        "us_per_step_stats": {"median": round(r["median"] * 1e6, 3), "p10": round(r["p10"] * 1e6, 3),
+                              "p90": round(r["p90"] * 1e6, 3), "replays": r["replays"], "steps_per_replay": args.steps},
         "tflops_dense_equiv": round(2 * M * wl.N * wl.K / t / 1e12, 4),
         "tflops_effective": round(2 * M * (wl.N * wl.n_keep + wl.r_cat * (wl.K + wl.N)) / t / 1e12, 4),
         "roofline": {"bound": "hbm", "kernel": "fwd_small_kernel", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic()},
         "encode": {"seconds": round(encode_s, 4), "iters": 24, "oversample": 32, "call": "second"},
+        "checks": {k: v for k, v in checks.items()},
     }
     if not args.no_extra:
+        peaks = measure_peaks(dev)
+        out["measured_peaks"] = peaks
+        out["roofline"]["peak_measured"] = peaks["hbm_read_GBs"]
+        out["roofline"]["frac_measured"] = round(achieved / peaks["hbm_read_GBs"], 4)
         sweep = []
         for m in (1, 4, 16):
-            tm, al = line_for(m, 128, 16)
+            Xm = _dev_bits(synth.make_x(wl.K, m, seed=11), dev)
+            tm = measure_decode(layers, Xm, ws, 128, 16)
+            al = cbytes + 2 * m * (wl.K + wl.N)
             sweep.append({"M": m, "us_per_step": round(tm * 1e6, 3), "compressed_GBs": round(cbytes / tm / 1e9, 1),
-                          "hbm_frac": round(al / tm / 1e9 / HBM_PEAK_GBS, 4)})
+                          "hbm_frac": round(al / tm / 1e9 / HBM_PEAK_GBS, 4),
+                          "hbm_frac_measured_peak": round(al / tm / 1e9 / peaks["hbm_read_GBs"], 4)})
         out["sweep"] = sweep
-        # many-token context: 11008 x 4096, 2048 tokens (matrix-core bound)
-        pw = synth.WORKLOADS["llama7b_mlp_up_11008"]
-        pin = synth.make_inputs(pw, with_x=False)
-        player, _ = srl.encode(_dev_bits(pin.W, dev), pw.n_keep, pw.r_svd, [_dev_bits(a, dev) for a in pin.lora_A],
-                               [_dev_bits(b, dev) for b in pin.lora_B])
         del layers
-        Xp = _dev_bits(synth.make_x(pw.K, pw.M, seed=12), dev)
-        pws = srl.forward_workspace(player, pw.M)
-        tp = measure_decode([player], Xp, pws, 20, 3)
-        dense = 2 * pw.M * pw.N * pw.K
-        out["prefill"] = {"workload": "llama7b_mlp_up_11008x4096_prefill", "M": pw.M, "ms_per_step": round(tp * 1e3, 4),
-                          "tflops_dense_equiv": round(dense / tp / 1e12, 2),
-                          "mfma_frac_dense_equiv": round(dense / tp / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        # many-token lines (matrix-core bound): 11008 x 4096 at 2048 tokens,
+        # and the 70B-shaped 28672 x 8192 layer at 8192 tokens
+        out["prefill"] = many_token_line(dev, "llama7b_mlp_up_11008", "llama7b_mlp_up_11008x4096_prefill", peaks,
+                                         steps=20, warmup=3)
+        out["l70b_up_s50"] = many_token_line(dev, "l70b_up_s50", "l70b_up_28672x8192_s50_m8192", peaks,
+                                             steps=5, warmup=2)
         out["cpu_baseline"] = cpu_baseline(wl)
-    print(json.dumps(out))
+    print(json.dumps(out), flush=True)
+    if not checks["ok"]:
+        print(f"bench.py: the timed run failed its checks: {checks}", file=sys.stderr)
+        sys.exit(1)
+
+
+def many_token_line(dev, name, label, peaks, steps, warmup):
+    """One many-token workload: GPU encode, then graph-replayed forwards on
+    one resident copy (the regime is matrix-core bound), against the bf16
+    matrix-core peak on dense-equivalent and on the method's own flops."""
+    import torch
+    import sparse_rank_linear_amd as srl
+    from sparse_rank_linear_amd import synth
+
+    wl = synth.WORKLOADS[name]
+    inp = synth.make_inputs(wl, with_x=False)
+    layer, _ = srl.encode(_dev_bits(inp.W, dev), wl.n_keep, wl.r_svd, [_dev_bits(a, dev) for a in inp.lora_A],
+                          [_dev_bits(b, dev) for b in inp.lora_B])
+    del inp
+    X = _dev_bits(synth.make_x(wl.K, wl.M, seed=12), dev)
+    ws = srl.forward_workspace(layer, wl.M)
+    r = measure_decode([layer], X, ws, steps, warmup, reps=4, detail=True)
+    werr = srl.wait_error(ws)
+    t = r["mean"]
+    dense = 2 * wl.M * wl.N * wl.K
+    eff = 2 * wl.M * (wl.N * wl.n_keep + wl.r_cat * (wl.K + wl.N))
+    line = {"workload": label, "N": wl.N, "K": wl.K, "M": wl.M, "n_keep": wl.n_keep, "r_cat": wl.r_cat,
+            "ms_per_step": round(t * 1e3, 4), "ms_median": round(r["median"] * 1e3, 4),
+            "ms_p10": round(r["p10"] * 1e3, 4), "ms_p90": round(r["p90"] * 1e3, 4),
+            "tflops_dense_equiv": round(dense / t / 1e12, 2), "tflops_effective": round(eff / t / 1e12, 2),
+            "mfma_frac_dense_equiv": round(dense / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "mfma_frac_effective": round(eff / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "mfma_frac_dense_equiv_measured_peak": round(dense / t / 1e12 / peaks["mfma_bf16_TFLOPs"], 4),
+            "wait_error": werr}
+    del layer, X, ws, r
+    torch.cuda.empty_cache()
+    return line
 
 
 if __name__ == "__main__":

@@ -83,12 +83,14 @@ typedef struct salr_layer {
   uint32_t* offsets;/* [N][ceil(K/1024)]                                    */
   uint16_t* a_cat;  /* [r_cat][K]                                           */
   uint16_t* b_cat;  /* [N][r_cat]                                           */
-  /* Parts of a fused layer (salr_fuse_layers fills these; 0 = one part).
+  /* Parts of a fused layer (salr_fuse_layers fills these; salr_encode
+   * sets n_parts = 0 and zeroes both arrays).
    * Part p owns rows part_rows[0] + ... + part_rows[p-1] onward and the
-   * adapter ranks part_ranks[0] + ... + part_ranks[p-1] onward; b_cat is
-   * zero outside each part's block.  The forward then reads and multiplies
-   * only a row tile's own block (when every part has a multiple of 16 rows
-   * and of 8 ranks); results are the same either way. */
+   * adapter ranks part_ranks[0] + ... + part_ranks[p-1] onward.  The
+   * forward TRUSTS b_cat to be zero outside each part's block: it then reads
+   * and multiplies only a row tile's own block (when every part has a
+   * multiple of 16 rows and of 8 ranks), so a record that does not match a
+   * block-diagonal b_cat gives a wrong Y without an error. */
   int32_t n_parts;  /* 0 (set it so for an encoded layer) or 1: one part;
                      * at most SALR_MAX_PARTS; the parts' rows must sum to
                      * N and their ranks to r_cat (else INVALID_ARG)        */

@@ -14,6 +14,12 @@ Parity status of each function (what pins it, see tests/test_oracle_*.py):
   salr.truncated_svd / residual_factors
                                    pinned: Eckart-Young, the per-entry MSE
                                    bound (1 - r/min(N,K)), full-rank case
+  salr.encode R_energy / tail_energy
+                                   pinned two-sided: a residual whose
+                                   singular values are known in closed form
+                                   (total and discarded energy at several
+                                   ranks), nothing pruned, a planted
+                                   undiscounted tail
   salr.forward                     pinned: per-set-bit triple loop, X = I
   The pages print no worked example and no intermediate values, so no
   function is pinned to a number printed on the pages.

@@ -14,16 +14,21 @@ from .binding import (  # noqa: F401
     LIB_PATH,
     SalrError,
     SalrLayer,
+    WaitTimeout,
     encode,
     forward_workspace,
     fuse,
     lib,
     linear_forward,
+    probe_mfma,
+    probe_stream_read,
     query_sizes,
+    wait_error,
     workspace,
 )
 
 __all__ = [
-    "EXPORTS", "LIB_PATH", "SalrError", "SalrLayer", "encode", "forward_workspace", "fuse", "lib", "linear_forward",
-    "query_sizes", "workspace",
+    "EXPORTS", "LIB_PATH", "SalrError", "SalrLayer", "WaitTimeout", "encode", "forward_workspace", "fuse", "lib",
+    "linear_forward", "probe_mfma", "probe_stream_read",
+    "query_sizes", "wait_error", "workspace",
 ]

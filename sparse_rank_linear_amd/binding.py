@@ -33,6 +33,9 @@ EXPORTS = (
     "salr_fuse_layers",
     "salr_status_string",
     "salr_version",
+    # include/salr_probe.h
+    "salr_probe_stream_read",
+    "salr_probe_mfma",
 )
 
 
@@ -103,6 +106,10 @@ def _lib():
         lib.salr_status_string.restype = C.c_char_p
         lib.salr_version.argtypes = []
         lib.salr_version.restype = C.c_int
+        lib.salr_probe_stream_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int32, C.c_void_p]
+        lib.salr_probe_stream_read.restype = C.c_int
+        lib.salr_probe_mfma.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p]
+        lib.salr_probe_mfma.restype = C.c_int
         _LIB = lib
     return _LIB
 
@@ -291,9 +298,32 @@ def forward_workspace(layer: SalrLayer, M_max: int, device="cuda"):
     return workspace(sz["forward_ws_bytes"], device)
 
 
-def linear_forward(layer: SalrLayer, X, Y=None, ws=None, stream=None):
+# Byte offset of the forward workspace's wait-error word (include/salr.h).
+WAIT_ERROR_OFFSET = 8
+
+
+class WaitTimeout(RuntimeError):
+    """A bounded cross-workgroup wait of a forward call timed out (Y is
+    unreliable)."""
+
+
+def wait_error(ws, stream=None) -> int:
+    """The forward workspace's wait-error word (uint32 at byte 8): nonzero
+    once any call on this workspace had a bounded wait time out.  Waits for
+    the work queued on `stream` (default: torch's current stream)."""
+    import torch
+
+    s = stream if stream is not None else torch.cuda.current_stream()
+    s.synchronize()
+    word = ws[WAIT_ERROR_OFFSET:WAIT_ERROR_OFFSET + 4].cpu()
+    return int(word.view(torch.int32).item())
+
+
+def linear_forward(layer: SalrLayer, X, Y=None, ws=None, stream=None, check: bool = False):
     """Y = X W_s^T + (X A_cat) B_cat on the GPU (asynchronous on `stream`).
-    X bf16 [M][K]; returns Y bf16 [M][N]."""
+    X bf16 [M][K]; returns Y bf16 [M][N].  With check=True the call
+    synchronizes the stream and raises WaitTimeout if the workspace's
+    wait-error word is set."""
     import torch
 
     X = _as_bf16_bits(X, "X")
@@ -308,6 +338,8 @@ def linear_forward(layer: SalrLayer, X, Y=None, ws=None, stream=None):
     st = _lib().salr_linear_forward(C.byref(desc), C.c_void_p(_dev_ptr(X, "X")), M, C.c_void_p(_dev_ptr(Y, "Y")),
                                     C.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), _stream_ptr(stream))
     _check(st, "salr_linear_forward")
+    if check and wait_error(ws, stream):
+        raise WaitTimeout("salr_linear_forward: a bounded wait timed out (workspace error word set)")
     return Y
 
 
@@ -329,3 +361,21 @@ def fuse(layers, stream=None) -> SalrLayer:
     _check(st, "salr_fuse_layers")
     out.parts = tuple((od.part_rows[p], od.part_ranks[p]) for p in range(od.n_parts))
     return out
+
+
+def probe_stream_read(src, sink, workgroups: int, stream=None):
+    """Read all of the device tensor `src` once (include/salr_probe.h);
+    `sink` is a device tensor of at least `workgroups` int32."""
+    nbytes = src.numel() * src.element_size()
+    _check(_lib().salr_probe_stream_read(C.c_void_p(_dev_ptr(src, "src")), nbytes,
+                                         C.c_void_p(_dev_ptr(sink, "sink")), workgroups, _stream_ptr(stream)),
+           "salr_probe_stream_read")
+    return nbytes
+
+
+def probe_mfma(out, workgroups: int, iters: int, shape: int, stream=None):
+    """Matrix-core peak loop (include/salr_probe.h); returns its flop count.
+    `out` is a device float tensor of at least `workgroups` entries."""
+    _check(_lib().salr_probe_mfma(C.c_void_p(_dev_ptr(out, "out")), workgroups, iters, shape, _stream_ptr(stream)),
+           "salr_probe_mfma")
+    return workgroups * 4 * iters * 131072

@@ -1020,7 +1020,11 @@ size_t encode_ws_bytes(int64_t N, int64_t K, int32_t r_svd, int32_t oversample) 
     if ((x) != hipSuccess) return SALR_ERR_HIP; \
   } while (0)
 
-int encode_run(const EncodeParams& p) {
+namespace {
+// The encode steps.  `ev` and `hflags` receive asynchronous device-to-host
+// copies; encode_run owns them and synchronizes the stream before any
+// return, so no copy can land after they are gone.
+int encode_steps(const EncodeParams& p, std::vector<double>& ev, uint32_t (&hflags)[4]) {
   hipStream_t s = p.stream;
   const EncodeLayout E = encode_layout(p.N, p.K, p.r_svd, p.oversample);
   if (p.ws_bytes < E.total) return SALR_ERR_WORKSPACE;
@@ -1047,7 +1051,7 @@ int encode_run(const EncodeParams& p) {
   // 2. residual truncated SVD
   const int r = p.r_svd;
   const int l = E.l;
-  std::vector<double> ev(std::max(l, 1), 0.0);
+  ev.assign(std::max(l, 1), 0.0);
   if (r > 0) {
     const int64_t N = p.N, K = p.K;
     float* Y = at<float>(ws, E.Y);
@@ -1103,7 +1107,6 @@ int encode_run(const EncodeParams& p) {
   }
   if (hipGetLastError() != hipSuccess) return SALR_ERR_HIP;
 
-  uint32_t hflags[4] = {0, 0, 0, 0};
   if (hipMemcpyAsync(hflags, flags, sizeof(hflags), hipMemcpyDeviceToHost, s) != hipSuccess) return SALR_ERR_HIP;
   if (hipStreamSynchronize(s) != hipSuccess) return SALR_ERR_HIP;
   if (hflags[0]) return SALR_ERR_NONFINITE;
@@ -1112,6 +1115,16 @@ int encode_run(const EncodeParams& p) {
     if (p.sigma) p.sigma[i] = ev[i] > 0 ? std::sqrt(ev[i]) : 0.0;
   }
   return SALR_OK;
+}
+}  // namespace
+
+int encode_run(const EncodeParams& p) {
+  std::vector<double> ev;
+  uint32_t hflags[4] = {0, 0, 0, 0};
+  const int st = encode_steps(p, ev, hflags);
+  // (on an error return, copies into ev / hflags may still be queued)
+  if (st != SALR_OK) (void)hipStreamSynchronize(p.stream);
+  return st;
 }
 
 }  // namespace salr

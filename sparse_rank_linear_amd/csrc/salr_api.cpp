@@ -306,6 +306,10 @@ int salr_encode(const uint16_t* W, int64_t N, int64_t K, int32_t n_keep, int32_t
     return SALR_ERR_INVALID_ARG;
   if (!ws || !aligned16(ws)) return SALR_ERR_WORKSPACE;
   if (ws_bytes < salr::encode_ws_bytes(N, K, r_svd, p.oversample)) return SALR_ERR_WORKSPACE;
+  // an encoded layer is one part: a stale record from an earlier fusion
+  // into this descriptor would make the forward skip adapter ranks
+  out->n_parts = 0;
+  for (int e = 0; e < SALR_MAX_PARTS; ++e) out->part_rows[e] = out->part_ranks[e] = 0;
   p.W = W;
   p.N = N;
   p.K = K;

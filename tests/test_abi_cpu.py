@@ -16,9 +16,14 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _header_functions():
-    text = open(os.path.join(ROOT, "include", "salr.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(salr_[a-z_]+)\s*\(", text)))
+    """Every function declared in include/*.h."""
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for fn in sorted(os.listdir(inc)):
+        if fn.endswith(".h"):
+            text = re.sub(r"/\*.*?\*/", "", open(os.path.join(inc, fn)).read(), flags=re.S)
+            names.update(re.findall(r"\b(salr_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
@@ -27,6 +32,23 @@ def test_library_exports_every_declared_function():
     assert set(declared) == set(B.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
+
+
+def test_probe_validation_paths():
+    lib = srl.lib()
+    buf = C.create_string_buffer(64)
+    p = C.cast(buf, C.c_void_p)
+    # null, misaligned, zero or ragged sizes, bad grid / shape / iteration count
+    assert lib.salr_probe_stream_read(None, 16, p, 1, None) == -1
+    assert lib.salr_probe_stream_read(p, 0, p, 1, None) == -1
+    assert lib.salr_probe_stream_read(p, 24, p, 1, None) == -1
+    assert lib.salr_probe_stream_read(p, 16, None, 1, None) == -1
+    assert lib.salr_probe_stream_read(p, 16, p, 0, None) == -1
+    assert lib.salr_probe_stream_read(p, 16, p, 65537, None) == -1
+    assert lib.salr_probe_mfma(None, 1, 1, 0, None) == -1
+    assert lib.salr_probe_mfma(p, 0, 1, 0, None) == -1
+    assert lib.salr_probe_mfma(p, 1, 0, 0, None) == -1
+    assert lib.salr_probe_mfma(p, 1, 1, 2, None) == -1
 
 
 def test_status_strings_and_version():

@@ -88,6 +88,56 @@ def test_encode_matches_oracle(case):
     assert rel.max() <= 1e-2
 
 
+def _signed_zero_subnormal_weight(N, K, seed):
+    """Rows of +0.0, -0.0, subnormal and small normal bf16 patterns (about
+    40% / 40% / 20%): at a high n_keep the kept set holds every normal and
+    subnormal entry plus the lowest-column zeros of both signs."""
+    rng = np.random.default_rng(seed)
+    u = rng.random((N, K))
+    sign = rng.integers(0, 2, size=(N, K)).astype(np.uint16) << 15
+    sub = rng.integers(1, 0x80, size=(N, K)).astype(np.uint16)        # exponent 0, fraction != 0
+    normal = rng.integers(0x0080, 0x3C00, size=(N, K)).astype(np.uint16)
+    W = np.where(u < 0.4, np.uint16(0), np.where(u < 0.8, sub, normal)) | sign
+    return W.astype(np.uint16)
+
+
+@pytest.mark.parametrize("n_keep", [900, 1000])
+def test_encode_keeps_signed_zeros_and_subnormals(n_keep):
+    """A kept -0.0 still sets its bit and is stored as 0x8000, kept
+    subnormals keep their patterns, and +0/-0 tie (lower column kept)."""
+    N, K = 48, 1024
+    say(f"encode signed zeros / subnormals N={N} K={K} n_keep={n_keep}")
+    W = _signed_zero_subnormal_weight(N, K, seed=n_keep)
+    enc = osl.encode(W, n_keep, 0)
+    kept = enc.values
+    assert np.any(kept == 0x8000) and np.any(kept == 0x0000), "case must keep zeros of both signs"
+    assert np.any(((kept & 0x7F80) == 0) & ((kept & 0x7F) != 0)), "case must keep subnormals"
+    layer, _ = _gpu_encode(W, n_keep, 0, [], [])
+    got = layer.to_numpy()
+    assert np.array_equal(got["masks"], enc.masks)
+    assert np.array_equal(got["values"], enc.values)
+    assert np.array_equal(got["offsets"], enc.offsets)
+
+
+def test_encode_zero_residual_with_residual_rank():
+    """Nothing pruned (n_keep = K) with a residual rank requested: the
+    residual is zero, so its singular values and the adapter block are zero
+    (oracle: S = 0)."""
+    N, K, r_svd = 64, 512, 4
+    W = synth.make_w(N, K, seed=3)
+    As, Bs = _loras(N, K, (8,), seed=3)
+    enc = osl.encode(W, K, r_svd, As, Bs)
+    assert enc.R_energy == 0.0 and np.all(enc.S == 0)
+    layer, sigma = _gpu_encode(W, K, r_svd, As, Bs)
+    got = layer.to_numpy()
+    assert np.array_equal(got["masks"], enc.masks) and np.array_equal(got["values"], enc.values)
+    assert np.all(sigma == 0.0)
+    A1 = ob.bits_to_f64(got["a_cat"][:r_svd])
+    B1 = ob.bits_to_f64(got["b_cat"][:, :r_svd])
+    assert np.all(B1 @ A1 == 0.0)
+    assert np.array_equal(got["a_cat"][r_svd:], enc.A_cat[:, r_svd:].T)
+
+
 def test_encode_rejects_nonfinite():
     import sparse_rank_linear_amd as srl
 

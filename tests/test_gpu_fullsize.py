@@ -14,9 +14,12 @@ Encode (salr_encode on the whole weight):
     top singular values within 1e-2, at least 99% of the optimal error
     reduction, and the per-entry MSE bound of the pages.
 Forward (salr_linear_forward on the encoded bitmap and values with seeded
-adapters of the workload's total rank): sampled output columns, for every
-token up to 256 tokens and 256 sampled tokens beyond, against the oracle's
-float64 forward of the same rows from its own encoding."""
+adapters of the workload's total rank), against the oracle's float64 forward
+from its own encoding of the whole weight:
+  * every output column for one token in every 256-token block (every token
+    up to 16), so that every output tile of the full-size launch is checked;
+  * sampled output columns for every token up to 256 tokens and 256 sampled
+    tokens beyond."""
 
 import json
 import os
@@ -54,6 +57,8 @@ TOKEN_SAMPLES = 256
 
 _inputs = {}
 _encoded = {}
+_oracle_enc = {}
+ORACLE_ROW_CHUNK = 4096
 
 
 def _inputs_for(name):
@@ -189,6 +194,33 @@ def test_fullsize_encode(name):
     assert e_err / (N * K) <= (1 - r_svd / min(N, K)) * e_r / (N * K) + 1e-30
 
 
+def _oracle_encoding(name):
+    """The oracle's bitmap and packed values of the whole weight, selected
+    and packed in row chunks (cached for the workload's token counts)."""
+    if name not in _oracle_enc:
+        _oracle_enc.clear()
+        wl = synth.WORKLOADS[name]
+        W = _inputs_for(name).W
+        masks = np.empty((wl.N, -(-wl.K // 64)), dtype=np.uint64)
+        values = np.empty((wl.N, wl.n_keep), dtype=np.uint16)
+        for r0 in range(0, wl.N, ORACLE_ROW_CHUNK):
+            r1 = min(wl.N, r0 + ORACLE_ROW_CHUNK)
+            keep = osl.select_keep(W[r0:r1], wl.n_keep)
+            masks[r0:r1] = osl.pack_masks(keep)
+            values[r0:r1] = osl.pack_values(W[r0:r1], keep, wl.n_keep)
+        say(f"  oracle encoding of all {wl.N} rows ready")
+        _oracle_enc[name] = (masks, values)
+    return _oracle_enc[name]
+
+
+def _block_tokens(M):
+    """Every token up to 16; else one token in every 256-token block, at a
+    different offset within each block."""
+    if M <= 16:
+        return np.arange(M)
+    return np.array(sorted({min(M - 1, 256 * b + (97 * b + 13) % 256) for b in range(-(-M // 256))}))
+
+
 @pytest.mark.parametrize("name", list(FULL))
 def test_fullsize_forward(name):
     import torch
@@ -212,8 +244,8 @@ def test_fullsize_forward(name):
     layer.b_cat.view(torch.int16).copy_(torch.from_numpy(np.ascontiguousarray(b_cat).view(np.int16)))
 
     rows = _rows(N)
-    keep = osl.select_keep(inp.W[rows], n_keep)
-    m_o, v_o = osl.pack_masks(keep), osl.pack_values(inp.W[rows], keep, n_keep)
+    m_all, v_all = _oracle_encoding(name)
+    m_o, v_o = m_all[rows], v_all[rows]
     for M in FULL[name]:
         X = synth.make_x(K, M, seed=wl.seed + 7 + M)
         say(f"forward {name}: M={M} N={N} K={K} r_cat={wl.r_cat}")
@@ -227,5 +259,15 @@ def test_fullsize_forward(name):
         Yref = osl.forward(X[tok], m_o, v_o, K, a_cat.T, b_cat[rows].T)
         mr, nw = errors(Yg, Yref)
         say(f"  {len(tok)} tokens x {len(rows)} rows: max_rel={mr:.3e} normwise={nw:.3e}")
+        assert mr <= TOL_MAX_REL and nw <= TOL_NORMWISE
+        # every output column for one token per 256-token block
+        tb = _block_tokens(M)
+        Yg = to_host_bits(Y[torch.from_numpy(tb).cuda()])
+        Yref = np.empty((len(tb), N))
+        for r0 in range(0, N, ORACLE_ROW_CHUNK):
+            r1 = min(N, r0 + ORACLE_ROW_CHUNK)
+            Yref[:, r0:r1] = osl.forward(X[tb], m_all[r0:r1], v_all[r0:r1], K, a_cat.T, b_cat[r0:r1].T)
+        mr, nw = errors(Yg, Yref)
+        say(f"  {len(tb)} tokens (one per 256-token block) x all {N} rows: max_rel={mr:.3e} normwise={nw:.3e}")
         assert mr <= TOL_MAX_REL and nw <= TOL_NORMWISE
         del Y, ws

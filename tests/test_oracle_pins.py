@@ -251,6 +251,87 @@ def test_mse_bound_from_the_pages(N, K, n_keep, r, dist):
         assert after <= enc.tail_energy / (N * K) * (1 + 1e-3)
 
 
+def _known_residual_weight(seed):
+    """A bf16 weight whose pruned residual has a spectrum known in closed
+    form.  Every row holds n_keep entries of magnitude 1.0 (the kept set,
+    strictly larger than everything else), and the other columns hold a
+    row- and column-permuted block diagonal of 2x2 blocks [[a, b], [b, a]]
+    (singular values |a + b| and |a - b|) and 1x1 blocks [d] (singular value
+    |d|), all exact in bf16.  Returns W bits, n_keep and the residual's
+    singular values (descending, zeros included)."""
+    rng = np.random.default_rng(seed)
+    pairs = [(0.375, 0.125), (-0.25, 0.1875), (0.09375, -0.03125)]
+    singles = [0.4375, -0.15625, 0.0078125]
+    N = 2 * len(pairs) + len(singles)                 # 9 rows
+    K_res, n_keep = N + 3, 7                          # 3 residual columns stay zero
+    block = np.zeros((N, K_res))
+    spec = []
+    i = 0
+    for a, b in pairs:
+        block[i:i + 2, i:i + 2] = [[a, b], [b, a]]
+        spec += [abs(a + b), abs(a - b)]
+        i += 2
+    for d in singles:
+        block[i, i] = d
+        spec.append(abs(d))
+        i += 1
+    block = block[rng.permutation(N)][:, rng.permutation(K_res)]
+    K = K_res + n_keep
+    W = np.zeros((N, K))
+    big_cols = np.sort(rng.choice(K, n_keep, replace=False))
+    W[:, big_cols] = rng.choice([-1.0, 1.0], size=(N, n_keep))
+    W[:, np.setdiff1d(np.arange(K), big_cols)] = block
+    spec = np.sort(np.array(spec))[::-1]
+    return ob.f64_to_bits(W), n_keep, spec
+
+
+def _tail_pin_holds(enc, spec, r):
+    """R_energy is the sum of all sigma^2 and tail_energy the sum of the
+    sigma^2 beyond rank r (Eckart-Young: the optimal rank-r error)."""
+    return (np.isclose(enc.R_energy, float(np.sum(spec ** 2)), rtol=1e-12, atol=0)
+            and np.isclose(enc.tail_energy, float(np.sum(spec[r:] ** 2)), rtol=1e-10, atol=1e-300))
+
+
+@pytest.mark.parametrize("r", [0, 1, 3, 8, 9])
+def test_tail_energy_closed_form(r):
+    """[summary] Methodology 2: the rank-r truncation of the residual leaves
+    exactly the discarded part of its spectrum.  Pinned two-sided on a
+    residual whose singular values are known by construction."""
+    W, n_keep, spec = _known_residual_weight(seed=r + 3)
+    enc = osl.encode(W, n_keep, r)
+    assert np.all(enc.keep == (np.abs(ob.bits_to_f64(W)) == 1.0))
+    assert _tail_pin_holds(enc, spec, r)
+    if r == spec.size:
+        assert enc.tail_energy == 0.0
+
+
+def test_tail_energy_nothing_pruned_and_tiny_layer():
+    # n_keep = K: empty residual, no energy on either side of the cut
+    rng = np.random.default_rng(21)
+    W = _rand_bits(rng, (12, 40))
+    enc = osl.encode(W, 40, 5)
+    assert enc.R_energy == 0.0 and enc.tail_energy == 0.0
+    # the small workload: tail and total against the values-only spectrum of
+    # the residual (LAPACK without vectors) at several ranks
+    wl = synth.WORKLOADS["tiny_512"]
+    W = synth.make_inputs(wl, with_x=False).W
+    S_all = osl.singular_values(osl.residual(W, osl.select_keep(W, wl.n_keep)))
+    for r in (0, 1, wl.r_svd, 100):
+        enc = osl.encode(W, wl.n_keep, r)
+        assert np.isclose(enc.R_energy, float(np.sum(S_all ** 2)), rtol=1e-12)
+        assert np.isclose(enc.tail_energy, float(np.sum(S_all[r:] ** 2)), rtol=1e-9)
+
+
+def test_planted_undiscounted_tail_is_caught():
+    """A tail that forgets to subtract the captured spectrum (tail = total
+    residual energy) must fail the closed-form pin."""
+    W, n_keep, spec = _known_residual_weight(seed=5)
+    enc = osl.encode(W, n_keep, 3)
+    assert _tail_pin_holds(enc, spec, 3)
+    planted = osl.Encoded(**{**enc.__dict__, "tail_energy": enc.R_energy})
+    assert not _tail_pin_holds(planted, spec, 3)
+
+
 def test_zero_sparsity_special_case():
     rng = np.random.default_rng(5)
     W = _rand_bits(rng, (6, 70))
