@@ -196,6 +196,34 @@ int salr_linear_forward(const salr_layer_t* L, const uint16_t* X, int64_t M,
                         uint16_t* Y, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * salr_linear_forward_noalloc - salr_linear_forward without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * The workspace is a fixed device array inside the library,
+ * SALR_NOALLOC_SCRATCH_BYTES per GPU, which each GPU the library runs on
+ * holds until the process ends.  The first call on a device (with that
+ * device current) looks the array up and zero-fills it on `stream`,
+ * waiting for the fill; that first call must not be under graph capture
+ * (SALR_ERR_UNSUPPORTED).  Later calls allocate nothing, call no hipMalloc /
+ * hipFree / allocating routine and may be captured.  Every call on a GPU
+ * shares that GPU's array: calls that overlap on one GPU (different streams
+ * or threads without ordering) race and give wrong results.
+ *
+ * L, X, M, Y, stream: as for salr_linear_forward (same kernels, same
+ * results).  wait_err: device pointer to a uint32 (4-byte aligned) that a
+ * timed-out bounded wait sets nonzero (the caller clears it; Y is then
+ * unreliable, and so are later calls on this GPU), or NULL to not report
+ * timeouts.  Errors: those of salr_linear_forward; SALR_ERR_WORKSPACE when
+ * the layer and M need more workspace than the array holds (the bytes
+ * salr_query_sizes reports as forward_ws_bytes for M_max = M); SALR_ERR_HIP
+ * when the array cannot be set up.
+ */
+#define SALR_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int salr_linear_forward_noalloc(const salr_layer_t* L, const uint16_t* X, int64_t M, uint16_t* Y,
+                                uint32_t* wait_err, void* stream);
+
+/*
  * salr_fuse_layers - one encoded layer from n_parts encoded layers that read
  * the same input (q/k/v, or gate/up): a single forward call on the result
  * computes every part.  This applies the pages' single low-rank product on

@@ -12,6 +12,7 @@ arguments (binding.py) and draws synthetic inputs (synth.py).
 from .binding import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
+    NOALLOC_SCRATCH_BYTES,
     SalrError,
     SalrLayer,
     WaitTimeout,
@@ -20,6 +21,7 @@ from .binding import (  # noqa: F401
     fuse,
     lib,
     linear_forward,
+    linear_forward_noalloc,
     probe_mfma,
     probe_stream_read,
     query_sizes,
@@ -28,7 +30,7 @@ from .binding import (  # noqa: F401
 )
 
 __all__ = [
-    "EXPORTS", "LIB_PATH", "SalrError", "SalrLayer", "WaitTimeout", "encode", "forward_workspace", "fuse", "lib",
-    "linear_forward", "probe_mfma", "probe_stream_read",
+    "EXPORTS", "LIB_PATH", "NOALLOC_SCRATCH_BYTES", "SalrError", "SalrLayer", "WaitTimeout", "encode", "forward_workspace", "fuse", "lib",
+    "linear_forward", "linear_forward_noalloc", "probe_mfma", "probe_stream_read",
     "query_sizes", "wait_error", "workspace",
 ]

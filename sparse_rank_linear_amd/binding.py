@@ -30,6 +30,7 @@ EXPORTS = (
     "salr_query_sizes",
     "salr_encode",
     "salr_linear_forward",
+    "salr_linear_forward_noalloc",
     "salr_fuse_layers",
     "salr_status_string",
     "salr_version",
@@ -99,6 +100,9 @@ def _lib():
         lib.salr_linear_forward.argtypes = [C.POINTER(salr_layer_t), C.c_void_p, C.c_int64, C.c_void_p,
                                             C.c_void_p, C.c_size_t, C.c_void_p]
         lib.salr_linear_forward.restype = C.c_int
+        lib.salr_linear_forward_noalloc.argtypes = [C.POINTER(salr_layer_t), C.c_void_p, C.c_int64, C.c_void_p,
+                                                    C.c_void_p, C.c_void_p]
+        lib.salr_linear_forward_noalloc.restype = C.c_int
         lib.salr_fuse_layers.argtypes = [C.POINTER(C.POINTER(salr_layer_t)), C.c_int32, C.POINTER(salr_layer_t),
                                          C.c_void_p]
         lib.salr_fuse_layers.restype = C.c_int
@@ -340,6 +344,28 @@ def linear_forward(layer: SalrLayer, X, Y=None, ws=None, stream=None, check: boo
     _check(st, "salr_linear_forward")
     if check and wait_error(ws, stream):
         raise WaitTimeout("salr_linear_forward: a bounded wait timed out (workspace error word set)")
+    return Y
+
+
+# Bytes of the library's fixed forward array (SALR_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def linear_forward_noalloc(layer: SalrLayer, X, Y, wait_err=None, stream=None):
+    """salr_linear_forward_noalloc: the forward with the library's fixed
+    per-GPU workspace (nothing allocated by the call).  Y bf16 [M][N] must
+    be given; wait_err is an optional device int32 tensor of one element
+    that a timed-out wait sets nonzero."""
+    X = _as_bf16_bits(X, "X")
+    Y = _as_bf16_bits(Y, "Y")
+    M = X.shape[0]
+    if X.dim() != 2 or X.shape[1] != layer.K or tuple(Y.shape) != (M, layer.N):
+        raise ValueError("X must be [M][K] and Y [M][N]")
+    desc = layer.descriptor()
+    err = C.c_void_p(_dev_ptr(wait_err, "wait_err")) if wait_err is not None else None
+    st = _lib().salr_linear_forward_noalloc(C.byref(desc), C.c_void_p(_dev_ptr(X, "X")), M,
+                                            C.c_void_p(_dev_ptr(Y, "Y")), err, _stream_ptr(stream))
+    _check(st, "salr_linear_forward_noalloc")
     return Y
 
 

@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstring>
 
+#include "salr_api_internal.hpp"
 #include "salr_encode.hpp"
 #include "salr_kernels.hpp"
 
@@ -334,6 +335,17 @@ int salr_encode(const uint16_t* W, int64_t N, int64_t K, int32_t n_keep, int32_t
 
 int salr_linear_forward(const salr_layer_t* L, const uint16_t* X, int64_t M, uint16_t* Y, void* ws, size_t ws_bytes,
                         void* stream) {
+  // (a null ws is rejected by forward_impl before the error word is used)
+  return salr::forward_impl(L, X, M, Y, ws, ws_bytes, ws ? at<uint32_t>(ws, kCounterSync + 8) : nullptr,
+                            static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+// The forward behind both entry points: `ws` is the workspace (caller's, or
+// the library's fixed array), `err` the word a timed-out wait sets.
+int salr::forward_impl(const salr_layer_t* L, const uint16_t* X, int64_t M, uint16_t* Y, void* ws, size_t ws_bytes,
+                       uint32_t* err_word, hipStream_t s) {
   if (!L) return SALR_ERR_INVALID_ARG;
   if (!dims_ok(L->N, L->K, L->n_keep, L->r_cat)) return SALR_ERR_INVALID_ARG;
   if (M < 0 || M > (int64_t(1) << 31) - 1) return SALR_ERR_INVALID_ARG;
@@ -345,7 +357,6 @@ int salr_linear_forward(const salr_layer_t* L, const uint16_t* X, int64_t M, uin
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return SALR_ERR_INVALID_ARG;
   if (static_cast<const void*>(X) == static_cast<const void*>(Y)) return SALR_ERR_INVALID_ARG;
-  if (!ws || !aligned16(ws)) return SALR_ERR_WORKSPACE;
   // A fused layer's parts: each row tile multiplies only its part's block
   // of ranks when every part has whole row tiles and 8-aligned ranks.
   if (L->n_parts < 0 || L->n_parts > SALR_MAX_PARTS) return SALR_ERR_INVALID_ARG;
@@ -364,9 +375,10 @@ int salr_linear_forward(const salr_layer_t* L, const uint16_t* X, int64_t M, uin
     if (rows != L->N || ranks != L->r_cat) return SALR_ERR_INVALID_ARG;
     if (windows) r_win = widest;
   }
+  // (every argument check above comes before the workspace's)
+  if (!ws || !aligned16(ws)) return SALR_ERR_WORKSPACE;
   const FwdLayout W = fwd_layout(L->N, L->K, L->n_keep, L->r_cat, M, r_win);
   if (ws_bytes < W.total) return SALR_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
 
   hipError_t err;
   if (M <= kSmallM && W.stream) {
@@ -396,7 +408,7 @@ int salr_linear_forward(const salr_layer_t* L, const uint16_t* X, int64_t M, uin
     a.t_pieces = W.t_pieces;
     a.t_chunks = W.t_chunks;
     a.tickets = at<uint64_t>(ws, kCounterTickets);
-    a.err = at<uint32_t>(ws, kCounterSync + 8);
+    a.err = err_word;
     err = salr::launch_fwd_stream(a, s);
   } else if (M <= kSmallM) {
     SmallFwdArgs a{};
@@ -444,7 +456,7 @@ int salr_linear_forward(const salr_layer_t* L, const uint16_t* X, int64_t M, uin
       a.nparts = L->n_parts;
     }
     a.tickets = at<uint64_t>(ws, kCounterTickets);
-    a.err = at<uint32_t>(ws, kCounterSync + 8);
+    a.err = err_word;
     a.ycount = at<uint32_t>(ws, kCounterY);
     a.ypart = at<uint64_t>(ws, W.ypart);
     err = salr::launch_fwd_small(a, s);
@@ -510,5 +522,3 @@ int salr_linear_forward(const salr_layer_t* L, const uint16_t* X, int64_t M, uin
   }
   return err == hipSuccess ? SALR_OK : SALR_ERR_HIP;
 }
-
-}  // extern "C"

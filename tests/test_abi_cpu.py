@@ -157,6 +157,27 @@ def _enc(W=0x50000000, N=64, K=64, n_keep=32, r_svd=4, out=None, ws=0x60000000, 
         C.byref(out) if out is not None else None, None, C.c_void_p(ws), ws_bytes, None)
 
 
+def _fwd_noalloc(d, X=0x20000000, M=4, Y=0x30000000, err=None):
+    return srl.lib().salr_linear_forward_noalloc(C.byref(d) if d is not None else None, C.c_void_p(X), M,
+                                                 C.c_void_p(Y), C.c_void_p(err) if err else None, None)
+
+
+def test_forward_noalloc_validation_paths():
+    # Argument errors are reported before the device (and the library's
+    # fixed array) is touched, so these run without a GPU.
+    assert _fwd_noalloc(_layer(), M=0) == 0
+    assert _fwd_noalloc(None) == -1
+    assert _fwd_noalloc(_layer(), M=-1) == -1
+    assert _fwd_noalloc(_layer(), X=0) == -1
+    assert _fwd_noalloc(_layer(), X=0x20000008) == -1
+    assert _fwd_noalloc(_layer(), X=0x30000000, Y=0x30000000) == -1
+    assert _fwd_noalloc(_layer(K=60)) == -1
+    d = _layer(N=64, r_cat=16)
+    d.n_parts = 9
+    assert _fwd_noalloc(d) == -1
+    assert _fwd_noalloc(_layer(), err=0x50000002) == -1   # misaligned wait-error word
+
+
 def test_encode_validation_paths():
     assert _enc(W=0) == -1
     d = _layer(64, 64, 32, 4, base=0x70000000)
