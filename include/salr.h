@@ -96,7 +96,15 @@ typedef struct salr_layer {
                      * N and their ranks to r_cat (else INVALID_ARG)        */
   int32_t part_rows[8];
   int32_t part_ranks[8];
+  /* Value format (QSALR): SALR_VALUES_BF16 (0: `values` holds the kept
+   * values) or SALR_VALUES_NF4 (1: `codes` and `scales` hold them, see
+   * salr_quantize_nf4; `values` is not read by the forward).              */
+  int32_t value_format;
+  uint8_t* codes;   /* NF4: uint8 [N][32 * ceil(n_keep/64)] (+ padding)      */
+  uint16_t* scales; /* NF4: bf16 [N][ceil(n_keep/64)] (+ padding)            */
 } salr_layer_t;
+#define SALR_VALUES_BF16 0
+#define SALR_VALUES_NF4 1
 #define SALR_MAX_PARTS 8
 
 /* Byte sizes of every caller-allocated buffer. */
@@ -108,6 +116,9 @@ typedef struct salr_sizes {
   size_t b_cat_bytes;
   size_t encode_ws_bytes;  /* workspace of salr_encode                      */
   size_t forward_ws_bytes; /* workspace of salr_linear_forward for M<=M_max */
+  size_t codes_bytes;      /* NF4 codes (includes tail padding)             */
+  size_t scales_bytes;     /* NF4 scales (includes tail padding)            */
+  size_t forward_ws_nf4_bytes; /* forward workspace of the NF4 layer        */
 } salr_sizes_t;
 
 /* Options of the residual truncated SVD inside salr_encode (NULL = the
@@ -172,6 +183,36 @@ int salr_encode(const uint16_t* W, int64_t N, int64_t K, int32_t n_keep,
                 double* sigma, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * salr_nf4_levels - the 16 levels of the NF4 value codec (QSALR: summary,
+ * Experimental Results, Ablation Studies, "Quantization"), ascending, as
+ * float32: the NormalFloat definition of QLoRA (Dettmers et al. 2023) -- 8
+ * positive normal quantiles at probabilities evenly spaced from 1 - d down
+ * to 1/2 (exclusive), 7 negative ones mirrored likewise, and 0, with
+ * d = (1/30 + 1/32) / 2, divided by the largest.  `out` is a host pointer.
+ * Pure host arithmetic.  Errors: INVALID_ARG (null).
+ */
+int salr_nf4_levels(float* out);
+
+/*
+ * salr_quantize_nf4 - QSALR value codec: code the kept values of an encoded
+ * layer (L->values, bf16) as NF4, in blocks of 64 consecutive values of a
+ * row (a row's last block may be shorter): the block's scale is its largest
+ * |value| (bf16, exact); each value's code is the index of the level nearest
+ * to value / scale in float32 (the lower level on a tie; a zero block codes
+ * 0.0, level 7); codes are nibble-packed, value 2b in the low nibble of byte
+ * b of the row, rows of 32 bytes per block.  Decoded values are
+ * bf16(level * scale) computed in float32.
+ *
+ * L   host pointer; L->values, L->codes (codes_bytes) and L->scales
+ *     (scales_bytes from salr_query_sizes) must be set; on success
+ *     L->value_format becomes SALR_VALUES_NF4.  The bitmap, lookup table and
+ *     adapters are not touched (the forward then reads codes and scales).
+ * Asynchronous on `stream`.  Errors: INVALID_ARG (nulls, alignment,
+ * dimensions, a layer already in NF4), HIP.
+ */
+int salr_quantize_nf4(salr_layer_t* L, void* stream);
+
+/*
  * salr_linear_forward - Y = X W_s^T + (X A_cat) B_cat for one encoded layer
  * (summary, Methodology 3 and 4: bitmap decode feeding matrix-core tiles,
  * one concatenated low-rank product).
@@ -188,7 +229,9 @@ int salr_encode(const uint16_t* W, int64_t N, int64_t K, int32_t n_keep,
  *     offset 8 of ws becomes nonzero (and Y is unreliable); the library
  *     never clears it.
  * Products accumulate in fp32; X*A_cat is rounded to bf16 before it meets
- * B_cat; Y is rounded to bf16 (nearest-even).
+ * B_cat; Y is rounded to bf16 (nearest-even).  An NF4 layer
+ * (value_format == SALR_VALUES_NF4) computes the same with every kept value
+ * replaced by its decoded value; its workspace is forward_ws_nf4_bytes.
  * Asynchronous on `stream`: returns after queueing.  Errors: INVALID_ARG,
  * WORKSPACE, UNSUPPORTED, HIP (launch failure).
  */

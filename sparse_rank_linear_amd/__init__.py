@@ -22,8 +22,10 @@ from .binding import (  # noqa: F401
     lib,
     linear_forward,
     linear_forward_noalloc,
+    nf4_levels,
     probe_mfma,
     probe_stream_read,
+    quantize_nf4,
     query_sizes,
     wait_error,
     workspace,
@@ -31,6 +33,6 @@ from .binding import (  # noqa: F401
 
 __all__ = [
     "EXPORTS", "LIB_PATH", "NOALLOC_SCRATCH_BYTES", "SalrError", "SalrLayer", "WaitTimeout", "encode", "forward_workspace", "fuse", "lib",
-    "linear_forward", "linear_forward_noalloc", "probe_mfma", "probe_stream_read",
-    "query_sizes", "wait_error", "workspace",
+    "linear_forward", "linear_forward_noalloc", "nf4_levels", "probe_mfma", "probe_stream_read",
+    "quantize_nf4", "query_sizes", "wait_error", "workspace",
 ]

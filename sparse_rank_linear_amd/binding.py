@@ -34,6 +34,8 @@ EXPORTS = (
     "salr_fuse_layers",
     "salr_status_string",
     "salr_version",
+    "salr_nf4_levels",
+    "salr_quantize_nf4",
     # include/salr_probe.h
     "salr_probe_stream_read",
     "salr_probe_mfma",
@@ -61,7 +63,13 @@ class salr_layer_t(C.Structure):
         ("n_parts", C.c_int32),
         ("part_rows", C.c_int32 * 8),
         ("part_ranks", C.c_int32 * 8),
+        ("value_format", C.c_int32),
+        ("codes", C.c_void_p),
+        ("scales", C.c_void_p),
     ]
+
+VALUES_BF16 = 0
+VALUES_NF4 = 1
 
 
 class salr_sizes_t(C.Structure):
@@ -73,6 +81,9 @@ class salr_sizes_t(C.Structure):
         ("b_cat_bytes", C.c_size_t),
         ("encode_ws_bytes", C.c_size_t),
         ("forward_ws_bytes", C.c_size_t),
+        ("codes_bytes", C.c_size_t),
+        ("scales_bytes", C.c_size_t),
+        ("forward_ws_nf4_bytes", C.c_size_t),
     ]
 
 
@@ -110,6 +121,10 @@ def _lib():
         lib.salr_status_string.restype = C.c_char_p
         lib.salr_version.argtypes = []
         lib.salr_version.restype = C.c_int
+        lib.salr_nf4_levels.argtypes = [C.POINTER(C.c_float)]
+        lib.salr_nf4_levels.restype = C.c_int
+        lib.salr_quantize_nf4.argtypes = [C.POINTER(salr_layer_t), C.c_void_p]
+        lib.salr_quantize_nf4.restype = C.c_int
         lib.salr_probe_stream_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int32, C.c_void_p]
         lib.salr_probe_stream_read.restype = C.c_int
         lib.salr_probe_mfma.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p]
@@ -179,6 +194,9 @@ class SalrLayer:
     a_cat: object
     b_cat: object
     parts: tuple = ()  # ((rows, ranks), ...) of a fused layer (salr_fuse_layers)
+    value_format: int = VALUES_BF16
+    codes: object = None   # NF4: uint8 [N][32 * ceil(n_keep/64)] (+ padding)
+    scales: object = None  # NF4: bf16 [N][ceil(n_keep/64)] (+ padding)
 
     @classmethod
     def empty(cls, N, K, n_keep, r_svd, r_cat, device="cuda"):
@@ -228,6 +246,9 @@ class SalrLayer:
         d.n_parts = len(self.parts)
         for p, (rows, ranks) in enumerate(self.parts):
             d.part_rows[p], d.part_ranks[p] = rows, ranks
+        d.value_format = self.value_format
+        d.codes = self.codes.data_ptr() if self.codes is not None else None
+        d.scales = self.scales.data_ptr() if self.scales is not None else None
         return d
 
     def clone(self) -> "SalrLayer":
@@ -235,6 +256,9 @@ class SalrLayer:
         c.parts = self.parts
         for name in ("masks", "values", "offsets", "a_cat", "b_cat"):
             getattr(c, name).copy_(getattr(self, name))
+        if self.codes is not None:
+            c.codes, c.scales = self.codes.clone(), self.scales.clone()
+            c.value_format = self.value_format
         return c
 
     def to_numpy(self) -> dict:
@@ -251,10 +275,15 @@ class SalrLayer:
         }
 
     def compressed_bytes(self) -> int:
-        """Bytes of the encoding (masks + values + offsets + a_cat + b_cat),
-        without the values buffer's tail padding."""
+        """Bytes of the encoding (masks + values, or NF4 codes + scales, +
+        offsets + a_cat + b_cat), without tail padding."""
         kw, ng = -(-self.K // 64), -(-self.K // 1024)
-        return (self.N * kw * 8 + self.N * self.n_keep * 2 + self.N * ng * 4
+        if self.value_format == VALUES_NF4:
+            nblk = -(-self.n_keep // 64)
+            vbytes = self.N * nblk * 32 + self.N * nblk * 2
+        else:
+            vbytes = self.N * self.n_keep * 2
+        return (self.N * kw * 8 + vbytes + self.N * ng * 4
                 + 2 * self.r_cat * self.K + 2 * self.N * self.r_cat)
 
 
@@ -299,7 +328,32 @@ def encode(W, n_keep: int, r_svd: int, lora_A=(), lora_B=(), oversample: int | N
 
 def forward_workspace(layer: SalrLayer, M_max: int, device="cuda"):
     sz = query_sizes(layer.N, layer.K, layer.n_keep, layer.r_svd, layer.r_cat, M_max)
-    return workspace(sz["forward_ws_bytes"], device)
+    key = "forward_ws_nf4_bytes" if layer.value_format == VALUES_NF4 else "forward_ws_bytes"
+    return workspace(sz[key], device)
+
+
+def nf4_levels():
+    """The 16 NF4 levels of the library (salr_nf4_levels), as floats."""
+    out = (C.c_float * 16)()
+    _check(_lib().salr_nf4_levels(out), "salr_nf4_levels")
+    return [out[i] for i in range(16)]
+
+
+def quantize_nf4(layer: SalrLayer, stream=None) -> SalrLayer:
+    """QSALR: code the layer's kept values as NF4 on the GPU
+    (salr_quantize_nf4).  Allocates the codes and scales and switches the
+    layer to them; the bf16 values stay allocated (the forward does not read
+    them)."""
+    import torch
+
+    sz = query_sizes(layer.N, layer.K, layer.n_keep, layer.r_svd, layer.r_cat, 0)
+    dev = layer.masks.device
+    layer.codes = torch.zeros(sz["codes_bytes"], dtype=torch.uint8, device=dev)
+    layer.scales = torch.zeros(sz["scales_bytes"] // 2, dtype=torch.int16, device=dev)
+    d = layer.descriptor()
+    _check(_lib().salr_quantize_nf4(C.byref(d), _stream_ptr(stream)), "salr_quantize_nf4")
+    layer.value_format = d.value_format
+    return layer
 
 
 # Byte offset of the forward workspace's wait-error word (include/salr.h).

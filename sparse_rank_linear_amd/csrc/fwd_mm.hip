@@ -1,0 +1,514 @@
+// SALR forward for many input rows (M > 16): bitmap decode in producer
+// waves, double-buffered against bf16 matrix-core tiles in consumer waves,
+// with the concatenated low-rank product folded in as extra K tiles.
+//
+// Method: gist.science summary of "Sparsity-Aware Low-Rank Representation
+// ...", Methodology 4 (two-stage pipeline: stage 1 rebuilds dense sub-blocks
+// of W_s from the bitmap and the packed values, stage 2 feeds them to
+// matrix-core GEMM tiles, the stages decoupled so decode does not stall the
+// multiply) and Methodology 3 (one GEMM for all stacked adapters).
+//
+// One workgroup: BM = 256 tokens x BN = 128 outputs, 8 waves, K walked in
+// 64-column tiles (one bitmap word per W row).  The two stages run in
+// different waves that share each SIMD:
+//   * waves 0-3 (consumers) each own 128 tokens x 64 outputs (8 x 4 MFMA
+//     16x16 tiles, 32 accumulators) and do nothing but read operands from
+//     LDS and issue v_mfma_f32_16x16x32_bf16;
+//   * waves 4-7 (producers) decode the W tile of the next phase into LDS,
+//     store the X tile of the next phase (loaded into registers a phase
+//     earlier) and keep the packed values two tiles ahead in registers.
+// (X goes through registers rather than direct-to-LDS loads: with such a
+// load in flight the compiler makes every LDS access of the wave wait for
+// it, which would serialize the producers' loads with their decode.)
+// One LDS barrier per phase.  Because the decode and the multiply are in
+// different waves, a SIMD issues the producer's vector instructions while
+// its consumer's matrix instructions run.
+//
+// The product is computed as Y^T = W_s X^T: a consumer lane's accumulator
+// rows are four consecutive outputs of one token (8-byte stores).  W rows
+// are streams of packed values: a row's running kept count gives the first
+// value of each tile, so K is walked from the split's first column on.
+#include <algorithm>
+
+#include "salr_device.hpp"
+#include "salr_kernels.hpp"
+
+namespace salr {
+namespace {
+
+constexpr int kDies = 8;             // XCDs of the GPU, each with its own L2
+constexpr int64_t kFillItems = 256;  // work items wanted to occupy the CUs
+constexpr int BM = 256;              // tokens per workgroup
+constexpr int BN = 128;              // outputs (W rows) per workgroup
+constexpr int kThreads = 512;
+constexpr int kCons = 256;           // consumer threads (waves 0-3)
+constexpr int kVRow = 40;            // words per row of staged values (10 chunks)
+constexpr int kVLoads = 5;           // 16-byte value chunks per producer thread per tile
+constexpr int kXLoads = BM * 8 / 256;  // X chunks per producer thread per tile
+
+// A 64-column bf16 tile row is 8 chunks of 16 bytes at chunk slot
+// (c ^ (row & 7)): a 16-row MFMA operand read (one chunk per row) hits every
+// bank once per pass, and a whole-wave direct-to-LDS load (64 lanes x 16
+// bytes, contiguous) fills 8 rows by choosing which chunk each lane fetches.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+
+__global__ __launch_bounds__(kThreads) void fwd_mm_kernel(LargeFwdArgs a) {
+  __shared__ u32x4_t xl0[BM * 8], xl1[BM * 8];  // X tiles (or bf16 T for the low-rank tiles)
+  __shared__ u32x4_t wl0[BN * 8], wl1[BN * 8];  // decoded W tiles (or B_cat^T slices)
+  __shared__ uint32_t vl[BN * kVRow];     // packed values of the tile being decoded
+  __shared__ u32x2_t luts[4][16];  // the nibble selectors, one copy per producer wave
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int i = lane & 15, g = lane >> 4;
+
+  // Tile of this workgroup.  Workgroups are dealt to the 8 dies in turn
+  // (id % 8); tiles are numbered token-block-major and each die gets a
+  // contiguous run of them, so the workgroups on one die share an X slab in
+  // that die's L2.  With K splits, consecutive work items of a die take the
+  // same split of neighbouring tiles.
+  const int nb = (int)((a.N + BN - 1) / BN);
+  const int total = nb * ((a.M + BM - 1) / BM);
+  const int items = total * a.ksplit;
+  const int per_die = (items + kDies - 1) / kDies;
+  const int id = (int)blockIdx.x;
+  const int item = (id % kDies) * per_die + id / kDies;
+  if (item >= items) return;
+  const int tile = item % total, split = item / total;
+  const int64_t n0 = (int64_t)(tile % nb) * BN;
+  const int m0 = (tile / nb) * BM;
+  const int kt0 = split * a.kt_per;
+  const int nk = min((a.K + 63) / 64, kt0 + a.kt_per);
+  const int n_main = nk - kt0;
+
+  // Low-rank tiles (split 0 only): ranks [rlo, rhi) in 64-rank tiles; a
+  // fused layer's row block takes only its part's ranks (b_cat is zero
+  // outside them; every part holds whole 256-row blocks).
+  // (static indices: a runtime index into the argument's arrays would move
+  // the whole argument block to private memory)
+  int rlo = 0, rhi = a.r_cat;
+  bool found = false;
+#pragma unroll
+  for (int p = 0; p < 8; ++p)
+    if (!found && p < a.nparts && n0 < a.part_row_end[p]) {
+      rlo = a.part_rank0[p];
+      rhi = rlo + a.part_nrank[p];
+      found = true;
+    }
+  const int n_lr = (split == 0 && rhi > rlo) ? (rhi - rlo + 63) / 64 : 0;
+  const int phases = n_main + n_lr;
+
+  if (wave < 4) {
+    // ------------------------------------------------------------ consumer
+    const int wm = wave >> 1, wn = wave & 1;  // 128-token half, 64-output half
+    f32x4_t acc[4][8];
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 8; ++y) acc[x][y] = zero4();
+    lds_barrier();  // (prologue: tile 0 staged by the producers)
+    for (int p = 0; p < phases; ++p) {
+      const u32x4_t* xt = (p & 1) ? xl1 : xl0;
+      const u32x4_t* wt = (p & 1) ? wl1 : wl0;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        u32x4_t av[4], bv[8];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) av[t] = wt[swz(wn * 64 + t * 16 + i, ks * 4 + g)];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) bv[t] = xt[swz(wm * 128 + t * 16 + i, ks * 4 + g)];
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+          for (int tm = 0; tm < 8; ++tm) acc[tn][tm] = mfma_16x16x32(av[tn], bv[tm], acc[tn][tm]);
+      }
+      lds_barrier();
+    }
+
+    // epilogue: lane holds Y[m][n .. n+3]
+    if (a.ksplit > 1) {
+      float* part = a.ypart + (size_t)split * a.M * a.N;
+#pragma unroll
+      for (int tn = 0; tn < 4; ++tn) {
+        const int64_t n = n0 + wn * 64 + tn * 16 + 4 * g;
+#pragma unroll
+        for (int tm = 0; tm < 8; ++tm) {
+          const int m = m0 + wm * 128 + tm * 16 + i;
+          if (m >= a.M) continue;
+          float* dst = part + (size_t)m * a.N + n;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float v = acc[tn][tm][e];
+            if (n + e < a.N) dst[e] = v;
+          }
+        }
+      }
+      return;
+    }
+#pragma unroll
+    for (int tn = 0; tn < 4; ++tn) {
+      const int64_t n = n0 + wn * 64 + tn * 16 + 4 * g;
+#pragma unroll
+      for (int tm = 0; tm < 8; ++tm) {
+        const int m = m0 + wm * 128 + tm * 16 + i;
+        if (m >= a.M) continue;
+        uint16_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = f32_to_bf16(acc[tn][tm][e]);
+        uint16_t* dst = a.Y + (size_t)m * a.N + n;
+        if ((a.N & 3) == 0 && n + 3 < a.N) {
+          *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{(uint32_t)h[0] | ((uint32_t)h[1] << 16),
+                                                     (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < a.N) dst[e] = h[e];
+        }
+      }
+    }
+    return;
+  }
+
+  // -------------------------------------------------------------- producer
+  const int ptid = tid - kCons;          // 0..255
+  const int pwave = ptid >> 6;           // 0..3
+  // (this wave's own copy: its decode starts before the first barrier, and
+  // a wave's LDS operations complete in order)
+  u32x2_t* const lut = luts[pwave];
+  if (lane < 16) lut[lane] = nibble_selectors(lane);
+  const int prow = ptid >> 1, phalf = ptid & 1;  // W row of the tile, column half
+  const int64_t grow = n0 + prow;
+  const bool row_ok = grow < a.N;
+  const int64_t row_base = row_ok ? grow * a.n_keep : 0;
+  const uint64_t* mrow = a.masks + (row_ok ? grow * a.kw : 0);
+  // (raw word of a clamped, unconditional load; bounds applied at use)
+  auto mask_raw = [&](int kt) __attribute__((always_inline)) -> uint64_t { return mrow[min(kt, a.kw - 1)]; };
+  auto mask_ok = [&](uint64_t w, int kt) __attribute__((always_inline)) -> uint64_t { return (row_ok && kt < nk) ? w : 0ull; };
+
+  // X tile loads: this thread carries chunk xch of tile rows xrow0 + 32 u
+  // (8 neighbouring threads read one row's 128 bytes).  Rows past M and
+  // columns past K read clamped (in-bounds) addresses: such rows reach
+  // outputs that are never stored, such columns meet zero weights.
+  const int xrow0 = ptid >> 3, xch = ptid & 7;
+  const int nk_all = (a.K + 63) / 64;
+  // byte offsets of the rows (used when M * K * 2 < 2^32)
+  uint32_t xoff[kXLoads];
+#pragma unroll
+  for (int u = 0; u < kXLoads; ++u)
+    xoff[u] = (uint32_t)min(m0 + xrow0 + 32 * u, a.M - 1) * (uint32_t)a.K * 2u;
+  u32x4_t xr[kXLoads];
+  auto load_x = [&](int kt) __attribute__((always_inline)) {
+    const int k = min(min(kt, nk_all - 1) * 64 + 8 * xch, a.K - 8);
+    if (a.x_off32) {
+      const char* const xb = reinterpret_cast<const char*>(a.X + k);
+#pragma unroll
+      for (int u = 0; u < kXLoads; ++u) xr[u] = load16(xb + xoff[u]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < kXLoads; ++u)
+        xr[u] = load16(a.X + (size_t)min(m0 + xrow0 + 32 * u, a.M - 1) * a.K + k);
+    }
+  };
+  auto store_x = [&](u32x4_t* xt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kXLoads; ++u) xt[swz(xrow0 + 32 * u, xch)] = xr[u];
+  };
+  // The packed values of one tile of this row: the 10 chunks from the one
+  // holding its first value (value index row_base + run) cover up to 64
+  // values and the decode window's overrun; this thread loads every other
+  // one.  Unconditional: the first chunk starts at most at the end of the
+  // values, and 10 chunks from there stay inside the buffer's 256-byte tail
+  // padding.
+  auto load_v = [&](u32x4_t (&r)[kVLoads], uint32_t run) __attribute__((always_inline)) {
+    const uint16_t* const vq = a.values + ((row_base + run) >> 3) * 8;
+#pragma unroll
+    for (int u = 0; u < kVLoads; ++u) r[u] = load16(vq + (phalf + 2 * u) * 8);
+  };
+  auto store_v = [&](const u32x4_t (&r)[kVLoads]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kVLoads; ++u) *reinterpret_cast<u32x4_t*>(&vl[prow * kVRow + (phalf + 2 * u) * 4]) = r[u];
+  };
+  // Decode this thread's 32 columns of the row's tile into dense bf16 (the
+  // row's staged values come from this thread and its neighbour lane, whose
+  // LDS stores precede these reads in the wave's order).
+  auto decode = [&](u32x4_t* wt, uint32_t run, uint64_t mk) __attribute__((always_inline)) {
+    const uint16_t* rowbuf = reinterpret_cast<const uint16_t*>(&vl[prow * kVRow]);
+    uint32_t idx = (uint32_t)((row_base + run) & 7) + (phalf ? (uint32_t)__popc((uint32_t)mk) : 0u);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t byte = (uint32_t)(mk >> (32 * phalf + 8 * b)) & 0xFFu;
+      wt[swz(prow, 4 * phalf + b)] = expand_byte(rowbuf, idx, byte, lut);
+      idx += __popc(byte);
+    }
+  };
+  // Low-rank tile j into buffers xt (bf16 T = sum of the K-split partials of
+  // X A_cat written by the previous launch) and wt (B_cat^T slices).
+  // (T is the bf16 sum of the K-split partials of X A_cat, made by the
+  // previous launch; ranks at or past rhi meet zero B_cat columns below)
+  auto stage_lowrank = [&](int j, u32x4_t* xt, u32x4_t* wt) __attribute__((always_inline)) {
+    const int r0 = rlo + 64 * j;
+    u32x4_t tv[BM * 8 / 256];
+#pragma unroll
+    for (int u = 0; u < BM * 8 / 256; ++u) {
+      const int c = ptid + 256 * u;
+      const int row = c >> 3, ch = c & 7;
+      const int m = m0 + row, k = r0 + 8 * ch;
+      tv[u] = (m < a.M && k < rhi) ? load16(a.t16 + (size_t)m * a.r_pad + k) : zero_u4();
+    }
+#pragma unroll
+    for (int u = 0; u < BM * 8 / 256; ++u) {
+      const int c = ptid + 256 * u;
+      xt[swz(c >> 3, c & 7)] = tv[u];
+    }
+    // B_cat^T row grow, ranks [r0 + 32 phalf, + 32): 16-byte loads when the
+    // chunk lies inside [rlo, rhi) and is 16-byte aligned
+    const uint16_t* brow = a.b_cat + (row_ok ? grow * a.r_cat : 0);
+#pragma unroll
+    for (int c8 = 0; c8 < 4; ++c8) {
+      const int ra = r0 + 32 * phalf + 8 * c8;
+      u32x4_t v = zero_u4();
+      if (row_ok && ra < rhi) {
+        if (ra + 8 <= rhi && (((size_t)grow * a.r_cat + ra) & 7) == 0) {
+          v = load16(brow + ra);
+        } else {
+          uint32_t w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t lo = ra + 2 * e < rhi ? brow[ra + 2 * e] : 0u;
+            const uint32_t hi = ra + 2 * e + 1 < rhi ? brow[ra + 2 * e + 1] : 0u;
+            w[e] = lo | (hi << 16);
+          }
+          v = u32x4_t{w[0], w[1], w[2], w[3]};
+        }
+      }
+      wt[swz(prow, 4 * phalf + c8)] = v;
+    }
+  };
+
+  // kept values of the row before this split: the lookup table entry at the
+  // last 1024-column boundary, plus the bitmap words after it
+  uint32_t run0 = 0;
+  if (kt0 > 0) {
+    const int w0 = kt0 & ~15;
+    uint64_t wd[15];
+#pragma unroll
+    for (int u = 0; u < 15; ++u) wd[u] = mrow[min(w0 + u, a.kw - 1)];
+    const uint32_t base = a.offsets[(row_ok ? grow : 0) * a.ng + (kt0 >> 4)];
+    uint32_t sum = 0;
+#pragma unroll
+    for (int u = 0; u < 15; ++u) sum += (w0 + u < kt0) ? (uint32_t)__popcll(wd[u]) : 0u;
+    run0 = row_ok ? base + sum : 0u;
+  }
+
+  // ---- prologue: tile kt0 decoded and its X in LDS; X of kt0+1 and the
+  // values of kt0+1, kt0+2 on their way
+  const uint64_t mk0 = mask_ok(mask_raw(kt0), kt0);
+  uint64_t mk1 = mask_ok(mask_raw(kt0 + 1), kt0 + 1);
+  uint64_t mk2 = mask_ok(mask_raw(kt0 + 2), kt0 + 2);
+  uint64_t mk3raw = mask_raw(kt0 + 3);
+  uint32_t run1 = run0 + (uint32_t)__popcll(mk0);   // first value of tile kt+1
+  uint32_t run2 = run1 + (uint32_t)__popcll(mk1);   // of tile kt+2
+  u32x4_t va[kVLoads], vb[kVLoads];
+  if (n_main > 0) {
+    load_x(kt0);
+    load_v(va, run0);
+    store_x(xl0);
+    load_x(kt0 + 1);
+    load_v(vb, run1);
+    store_v(va);
+    decode(wl0, run0, mk0);
+    load_v(va, run2);
+  } else {
+    stage_lowrank(0, xl0, wl0);
+  }
+  lds_barrier();
+
+  // ---- phases: the consumers multiply the tile of phase p (kt = kt0 + p,
+  // buffers of parity p) while this wave prepares the tile of phase p + 1
+  // and issues the loads of later tiles.  Main phases are unrolled by two so
+  // that the buffers and the two value register sets are named.
+  auto main_phase = [&](int p, u32x4_t(&vnext)[kVLoads], u32x4_t* xnext, u32x4_t* wnext)
+                        __attribute__((always_inline)) {
+    const int kt = kt0 + p;
+    // tile kt+1: X (loaded a phase ago) to LDS, X of kt+2 requested; its
+    // values (loaded two phases ago) to LDS, decoded; the values of kt+3
+    // requested into the set just stored, and the bitmap word of kt+4
+    store_x(xnext);
+    load_x(kt + 2);
+    store_v(vnext);
+    decode(wnext, run1, mk1);
+    const uint64_t mk3 = mask_ok(mk3raw, kt + 3);
+    const uint32_t run3 = run2 + (uint32_t)__popcll(mk2);
+    load_v(vnext, run3);
+    mk3raw = mask_raw(kt + 4);
+    mk1 = mk2;
+    mk2 = mk3;
+    run1 = run2;
+    run2 = run3;
+    lds_barrier();
+  };
+  int p = 0;
+  for (; p + 2 < n_main; p += 2) {
+    main_phase(p, vb, xl1, wl1);
+    main_phase(p + 1, va, xl0, wl0);
+  }
+  if (p + 1 < n_main) main_phase(p++, vb, xl1, wl1);
+  // the last main phase and the low-rank phases: stage the next low-rank tile
+  for (; p < phases; ++p) {
+    if (p + 1 < phases) stage_lowrank(p + 1 - n_main, ((p + 1) & 1) ? xl1 : xl0, ((p + 1) & 1) ? wl1 : wl0);
+    lds_barrier();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Partial T = X * A_cat over one K range per workgroup, fp32, written to
+// tpart[split][M][r_pad] (columns >= r_cat are zero).  A workgroup owns 64
+// tokens (one 16-token MFMA tile per wave); the A_cat slice of each
+// 64-column tile is shared through LDS.  The splits are summed by the
+// consumer (the next launch), so no workgroup waits for another.
+// ---------------------------------------------------------------------------
+constexpr int kTThreads = 256;
+constexpr int kMaxRTiles = 16;   // r_pad <= 256
+constexpr int kLdsRow = 36;      // words per 64-column bf16 row (+16 B pad)
+
+__global__ __launch_bounds__(kTThreads) void lowrank_t_kernel(LowRankTArgs a) {
+  __shared__ uint32_t al[kMaxRTiles * 16 * kLdsRow];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int mb = blockIdx.x, ks = blockIdx.y;
+  const int token = mb * 64 + wave * 16 + i;
+  const int rt = a.r_pad / 16;
+  const int k0 = ks * a.k_chunk, k1 = min(a.K, k0 + a.k_chunk);
+
+  f32x4_t acc[kMaxRTiles];
+#pragma unroll
+  for (int j = 0; j < kMaxRTiles; ++j) acc[j] = zero4();
+
+  for (int kt = k0; kt < k1; kt += 64) {
+    // stage A_cat[0..r_pad)[kt .. kt+64)
+    for (int c = tid; c < a.r_pad * 8; c += kTThreads) {
+      const int r = c >> 3, k = kt + 8 * (c & 7);
+      const u32x4_t v = (r < a.r_cat && k < k1) ? load16(a.a_cat + (size_t)r * a.K + k) : zero_u4();
+      *reinterpret_cast<u32x4_t*>(&al[r * kLdsRow + (c & 7) * 4]) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int k = kt + 32 * s + 8 * g;
+      const u32x4_t xv = (token < a.M && k < k1) ? load16(a.X + (size_t)token * a.K + k) : zero_u4();
+#pragma unroll
+      for (int j = 0; j < kMaxRTiles; ++j)
+        if (j < rt) {
+          const u32x4_t av = *reinterpret_cast<const u32x4_t*>(&al[(16 * j + i) * kLdsRow + s * 16 + g * 4]);
+          acc[j] = mfma_16x16x32(av, xv, acc[j]);
+        }
+    }
+    __syncthreads();
+  }
+
+  // lane holds T[token][16j + 4g + e]
+  if (token < a.M) {
+    float* dst = a.tpart + ((size_t)ks * a.M + token) * a.r_pad;
+#pragma unroll
+    for (int j = 0; j < kMaxRTiles; ++j)
+      if (j < rt) *reinterpret_cast<f32x4_t*>(&dst[16 * j + 4 * g]) = acc[j];
+  }
+}
+
+// T = bf16(sum of the K-split partials of X A_cat, in split order), [M][r_pad]
+// with r_pad a multiple of 16: 8 ranks a thread.
+__global__ __launch_bounds__(256) void reduce_t_kernel(const float* tpart, int splits, int64_t MR, uint16_t* t16) {
+  const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (e0 >= MR) return;
+  f32x4_t lo = zero4(), hi = zero4();
+  for (int sp = 0; sp < splits; ++sp) {
+    const float* src = tpart + (size_t)sp * MR + e0;
+    lo += *reinterpret_cast<const f32x4_t*>(src);
+    hi += *reinterpret_cast<const f32x4_t*>(src + 4);
+  }
+  *reinterpret_cast<u32x4_t*>(t16 + e0) =
+      u32x4_t{(uint32_t)f32_to_bf16(lo[0]) | ((uint32_t)f32_to_bf16(lo[1]) << 16),
+              (uint32_t)f32_to_bf16(lo[2]) | ((uint32_t)f32_to_bf16(lo[3]) << 16),
+              (uint32_t)f32_to_bf16(hi[0]) | ((uint32_t)f32_to_bf16(hi[1]) << 16),
+              (uint32_t)f32_to_bf16(hi[2]) | ((uint32_t)f32_to_bf16(hi[3]) << 16)};
+}
+
+// Y = bf16(sum of the K-split partials, in split order): 8 outputs a thread
+// (16-byte loads and store when MN is a multiple of 8, as it is whenever N is).
+__global__ __launch_bounds__(256) void sum_splits_kernel(const float* part, uint16_t* Y, int64_t MN, int ksplit) {
+  const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (e0 >= MN) return;
+  if ((MN & 7) == 0) {
+    f32x4_t lo = zero4(), hi = zero4();
+    for (int s = 0; s < ksplit; ++s) {
+      const float* src = part + (size_t)s * MN + e0;
+      lo += *reinterpret_cast<const f32x4_t*>(src);
+      hi += *reinterpret_cast<const f32x4_t*>(src + 4);
+    }
+    *reinterpret_cast<u32x4_t*>(Y + e0) =
+        u32x4_t{(uint32_t)f32_to_bf16(lo[0]) | ((uint32_t)f32_to_bf16(lo[1]) << 16),
+                (uint32_t)f32_to_bf16(lo[2]) | ((uint32_t)f32_to_bf16(lo[3]) << 16),
+                (uint32_t)f32_to_bf16(hi[0]) | ((uint32_t)f32_to_bf16(hi[1]) << 16),
+                (uint32_t)f32_to_bf16(hi[2]) | ((uint32_t)f32_to_bf16(hi[3]) << 16)};
+    return;
+  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int n = (int)min<int64_t>(8, MN - e0);
+  for (int s = 0; s < ksplit; ++s) {
+    const float* src = part + (size_t)s * MN + e0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (e < n) acc[e] += src[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (e < n) Y[e0 + e] = f32_to_bf16(acc[e]);
+}
+
+}  // namespace
+
+hipError_t launch_lowrank_t(const LowRankTArgs& a, hipStream_t s) {
+  dim3 grid((a.M + 63) / 64, a.splits);
+  hipLaunchKernelGGL(lowrank_t_kernel, grid, dim3(kTThreads), 0, s, a);
+  const int64_t mr = (int64_t)a.M * a.r_pad;  // (r_pad % 16 == 0)
+  hipLaunchKernelGGL(reduce_t_kernel, dim3((unsigned)((mr + 2047) / 2048)), dim3(256), 0, s, a.tpart, a.splits, mr,
+                     a.t16);
+  return hipGetLastError();
+}
+
+int64_t fwd_large_tiles(int64_t N, int64_t M) { return ((N + BN - 1) / BN) * ((M + BM - 1) / BM); }
+
+int fwd_large_ksplit(int64_t N, int64_t K, int64_t M) {
+  // enough work items for every CU, each split at least 8 K tiles, at most 8
+  const int64_t tiles = fwd_large_tiles(N, M), nk = (K + 63) / 64;
+  int64_t s = std::min<int64_t>({kFillItems / std::max<int64_t>(tiles, 1), nk / 8, 8});
+  return (int)std::max<int64_t>(s, 1);
+}
+
+size_t fwd_large_part_bytes(int64_t N, int64_t K, int64_t M_max) {
+  // ksplit * tiles <= kFillItems, so the partials never exceed kFillItems
+  // whole tiles; nothing when no M <= M_max splits
+  size_t most = 0;
+  for (int64_t M = BM; M - BM < M_max; M += BM) {
+    const int s = fwd_large_ksplit(N, K, std::min<int64_t>(M, M_max));
+    if (s > 1) most = std::max(most, (size_t)s * std::min<int64_t>(M, M_max) * N * 4);
+    if (fwd_large_tiles(N, M) >= kFillItems) break;
+  }
+  return most;
+}
+
+hipError_t launch_fwd_large(const LargeFwdArgs& a, hipStream_t s) {
+  // (ceil(work items / 8) workgroups per die: see the tile mapping)
+  const int64_t items = fwd_large_tiles(a.N, a.M) * a.ksplit;
+  const dim3 grid((unsigned)((items + kDies - 1) / kDies * kDies));
+  hipLaunchKernelGGL(fwd_mm_kernel, grid, dim3(kThreads), 0, s, a);
+  if (a.ksplit > 1) {
+    const int64_t mn = a.N * (int64_t)a.M;
+    hipLaunchKernelGGL(sum_splits_kernel, dim3((unsigned)((mn + 2047) / 2048)), dim3(256), 0, s, a.ypart, a.Y, mn,
+                       a.ksplit);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace salr

@@ -60,6 +60,7 @@ constexpr int kBatch = 4;  // decode steps whose LDS reads are issued together
 // LDS carve-up (dynamic shared memory): a fixed part, then the values area.
 struct alignas(16) Lds {
   u32x2_t lut[16];
+  float levels[16];        // NF4 levels (NF4 layers)
   uint32_t seg[kRows][2];  // per-row range of kept-value indices (within the row)
   int64_t vorg[kRows];     // global value index = LDS value slot + vorg (per row)
   uint64_t masks[kRows * kMaskRowWords];
@@ -153,11 +154,83 @@ __device__ __forceinline__ void copy_chunks_to_lds(const uint32_t* src, uint32_t
   }
 }
 
+// NF4 dequantization pass (kNF4 instances): the row segments' codes and
+// scales were loaded to the end of each row's LDS area; 32 threads per row
+// each read the codes and scales of up to kNf4Groups groups of 8 values
+// (value group g of a row is LDS chunk g of its area, as in the bf16 layout),
+// and after a barrier write their bf16 values, level[code] * scale rounded
+// in float32, over the same area.
+__device__ __forceinline__ void nf4_dequantize(const SmallFwdArgs& a, const Lds& L, uint32_t* vals, int64_t row0,
+                                               int rows_here, int tid) {
+  const int r = tid >> 5, p = tid & 31;
+  const uint32_t lo = L.seg[r][0], hi = L.seg[r][1];
+  const bool live = r < rows_here && hi > lo;
+  const int64_t rowv = (row0 + r) * a.n_keep;  // global index of the row's value 0
+  const int64_t q0 = (rowv + lo) >> 3;          // first 8-value group (global)
+  const int nch = live ? (int)(((rowv + hi + 7) >> 3) - q0) : 0;
+  const int64_t cbyte0 = (((row0 + r) * a.cb_row + (lo >> 1)) >> 4) * 16;              // first loaded code byte
+  const int64_t sbyte0 = ((((row0 + r) * a.nblk + (lo >> 6)) * 2) >> 4) * 16;         // first loaded scale byte
+  const unsigned char* cl = reinterpret_cast<const unsigned char*>(vals + ((size_t)r * a.vcap + a.cofs) * 4);
+  const unsigned char* sl = reinterpret_cast<const unsigned char*>(vals + ((size_t)r * a.vcap + a.sofs) * 4);
+  const int64_t blo = lo >> 6, bhi = hi > 0 ? (int64_t)(hi - 1) >> 6 : 0;
+  uint32_t cw[kNf4Groups];
+  uint32_t sc[kNf4Groups];  // the two bf16 scales of the group (first | second << 16)
+  // values of a group from this index on take the second scale
+  const auto split_of = [&](int64_t j0) {
+    int64_t b0 = (j0 > (int64_t)lo ? j0 : (int64_t)lo) >> 6, b1 = (j0 + 7) >> 6;
+    b0 = b0 < blo ? blo : (b0 > bhi ? bhi : b0);
+    b1 = b1 < blo ? blo : (b1 > bhi ? bhi : b1);
+    return b1 != b0 ? (int)(64 * b1 - j0) : 8;
+  };
+#pragma unroll
+  for (int q = 0; q < kNf4Groups; ++q) {
+    const int g = p + 32 * q;
+    cw[q] = 0u;
+    sc[q] = 0u;
+    if (g < nch) {
+      // the group's 8 codes from row-local value j0 on (values before the
+      // segment, never selected, read as code 0)
+      const int64_t j0 = (q0 + g) * 8 - rowv;
+      const int64_t jc = j0 > (int64_t)(lo & ~1u) ? j0 : (int64_t)(lo & ~1u);
+      const int64_t byte = (row0 + r) * a.cb_row + (jc >> 1) - cbyte0;
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(cl + (byte & ~3ll));
+      const uint32_t c = __builtin_amdgcn_alignbit(w[1], w[0], (uint32_t)((byte & 3) * 8 + (jc & 1) * 4));
+      cw[q] = c << (4 * (uint32_t)(jc - j0));
+      // scales of the group's first and last value (clamped to the segment)
+      int64_t b0 = (j0 > (int64_t)lo ? j0 : (int64_t)lo) >> 6;
+      int64_t b1 = (j0 + 7) >> 6;
+      b0 = b0 < blo ? blo : (b0 > bhi ? bhi : b0);
+      b1 = b1 < blo ? blo : (b1 > bhi ? bhi : b1);
+      const uint16_t* sp = reinterpret_cast<const uint16_t*>(sl);
+      sc[q] = (uint32_t)sp[((row0 + r) * a.nblk + b0) - sbyte0 / 2] |
+              ((uint32_t)sp[((row0 + r) * a.nblk + b1) - sbyte0 / 2] << 16);
+    }
+  }
+  lds_barrier();  // every thread has its codes and scales: the area is free
+#pragma unroll
+  for (int q = 0; q < kNf4Groups; ++q) {
+    const int g = p + 32 * q;
+    if (g < nch) {
+      const int split = split_of((q0 + g) * 8 - rowv);
+      const float s0 = __uint_as_float(sc[q] << 16), s1 = __uint_as_float(sc[q] & 0xFFFF0000u);
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float f0 = L.levels[(cw[q] >> (4 * e)) & 15u] * (e < split ? s0 : s1);
+        const float f1 = L.levels[(cw[q] >> (4 * e + 4)) & 15u] * (e + 1 < split ? s0 : s1);
+        w[e / 2] = (uint32_t)f32_to_bf16(f0) | ((uint32_t)f32_to_bf16(f1) << 16);
+      }
+      reinterpret_cast<u32x4_t*>(vals)[(size_t)r * a.vcap + g] = u32x4_t{w[0], w[1], w[2], w[3]};
+    }
+  }
+}
+
 // kOneRound: every weight workgroup is resident at once, so the T producers
 // sit on CUs beside some of them (see the producer section).
 // kWin: a fused layer's parts bound each row tile's adapter ranks (a.nparts
 // > 0); the plain instance keeps the whole-r_cat code.
-template <bool kOneRound, bool kWin>
+// kNF4: the kept values are NF4 codes (QSALR), dequantized in LDS.
+template <bool kOneRound, bool kWin, bool kNF4>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void fwd_small_kernel(SmallFwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -232,6 +305,7 @@ void fwd_small_kernel(SmallFwdArgs a) {
     if (kOneRound) __builtin_amdgcn_s_setprio(3);
     load_x_frags();
     if (tid < 16) L.lut[tid] = nibble_selectors(tid);
+    if (kNF4 && tid >= 64 && tid < 80) L.levels[tid - 64] = a.levels[tid - 64];
     const int lw = wave, lws = kWaves;
     // Bitmap words of the range, per row 2*nwords dwords direct to LDS; rows
     // past N read as zero.
@@ -270,11 +344,28 @@ void fwd_small_kernel(SmallFwdArgs a) {
       if (r < kRows) {
         const int64_t va = (row0 + r) * a.n_keep + seg_lo[k], vb = (row0 + r) * a.n_keep + seg_hi[k];
         const int64_t q0 = va >> 3, nch = (r < rows_here && vb > va) ? ((vb + 7) >> 3) - q0 : 0;
-        copy_chunks_to_lds(reinterpret_cast<const uint32_t*>(a.values) + q0 * 4, vals + (size_t)r * a.vcap * 4, nch,
-                           0, 1, lane);
+        if (kNF4) {
+          // the segment's codes (+ 8 bytes for the last group's window) and
+          // the scales of its blocks, to the end of the row's area
+          const bool seg_live = r < rows_here && seg_hi[k] > seg_lo[k];
+          const int64_t cb0 = (row0 + r) * a.cb_row + (seg_lo[k] >> 1);
+          const int64_t cb1 = (row0 + r) * a.cb_row + ((seg_hi[k] + 1) >> 1) + 8;
+          const int64_t ncc = seg_live ? ((cb1 + 15) >> 4) - (cb0 >> 4) : 0;
+          copy_chunks_to_lds(reinterpret_cast<const uint32_t*>(a.codes) + (cb0 >> 4) * 4,
+                             vals + ((size_t)r * a.vcap + a.cofs) * 4, ncc, 0, 1, lane);
+          const int64_t sb0 = ((row0 + r) * a.nblk + (seg_lo[k] >> 6)) * 2;
+          const int64_t sb1 = ((row0 + r) * a.nblk + (seg_live ? ((seg_hi[k] - 1) >> 6) + 1 : 0)) * 2;
+          const int64_t nsc = seg_live ? ((sb1 + 15) >> 4) - (sb0 >> 4) : 0;
+          copy_chunks_to_lds(reinterpret_cast<const uint32_t*>(a.scales) + (sb0 >> 4) * 4,
+                             vals + ((size_t)r * a.vcap + a.sofs) * 4, nsc, 0, 1, lane);
+        } else {
+          copy_chunks_to_lds(reinterpret_cast<const uint32_t*>(a.values) + q0 * 4, vals + (size_t)r * a.vcap * 4,
+                             nch, 0, 1, lane);
+        }
         if (lane == 0) {
           L.vorg[r] = q0 * 8 - (int64_t)r * a.vcap * 8;
           L.seg[r][0] = seg_lo[k];
+          L.seg[r][1] = seg_hi[k];
         }
       }
     }
@@ -384,6 +475,10 @@ void fwd_small_kernel(SmallFwdArgs a) {
 
   __builtin_amdgcn_s_waitcnt(0);  // every load of this wave has landed
   lds_barrier();
+  if (kNF4) {
+    nf4_dequantize(a, L, vals, row0, rows_here, tid);
+    lds_barrier();
+  }
 
   // This workgroup's share of the low-rank term: the 32-rank chunks rng,
   // rng + splits, ...; wave k reads chunk k's T operand after the decode.
@@ -557,21 +652,32 @@ size_t fwd_small_lds_bytes(int vcap, int bl_bytes) {
   return sizeof(Lds) + fwd_small_vals_bytes(vcap) + (size_t)bl_bytes;
 }
 
+template <bool kNF4>
+void launch_small(const SmallFwdArgs& a, int grid, size_t lds, bool one_round, hipStream_t s) {
+  if (a.nparts > 0) {
+    if (one_round)
+      hipLaunchKernelGGL((fwd_small_kernel<true, true, kNF4>), dim3(grid), dim3(kThreads), lds, s, a);
+    else
+      hipLaunchKernelGGL((fwd_small_kernel<false, true, kNF4>), dim3(grid), dim3(kThreads), lds, s, a);
+  } else if (one_round) {
+    hipLaunchKernelGGL((fwd_small_kernel<true, false, kNF4>), dim3(grid), dim3(kThreads), lds, s, a);
+  } else {
+    hipLaunchKernelGGL((fwd_small_kernel<false, false, kNF4>), dim3(grid), dim3(kThreads), lds, s, a);
+  }
+}
+
 hipError_t launch_fwd_small(const SmallFwdArgs& a, hipStream_t s) {
   const int grid = a.n_tiles * a.splits + a.r_tiles * a.t_pieces;
   if (a.tl_bytes > 8 * 1024) return hipErrorInvalidValue;  // (r_cat <= 256)
   const size_t lds = fwd_small_lds_bytes(a.vcap, a.bl_bytes);
   // one weight workgroup per CU at most: all resident in one round
   const bool one_round = (int64_t)a.n_tiles * a.splits <= kCus;
-  if (a.nparts > 0) {
-    if (one_round)
-      hipLaunchKernelGGL((fwd_small_kernel<true, true>), dim3(grid), dim3(kThreads), lds, s, a);
-    else
-      hipLaunchKernelGGL((fwd_small_kernel<false, true>), dim3(grid), dim3(kThreads), lds, s, a);
-  } else if (one_round) {
-    hipLaunchKernelGGL((fwd_small_kernel<true, false>), dim3(grid), dim3(kThreads), lds, s, a);
+  if (a.nf4) {
+    SmallFwdArgs b = a;
+    nf4_levels(b.levels);
+    launch_small<true>(b, grid, lds, one_round, s);
   } else {
-    hipLaunchKernelGGL((fwd_small_kernel<false, false>), dim3(grid), dim3(kThreads), lds, s, a);
+    launch_small<false>(a, grid, lds, one_round, s);
   }
   return hipGetLastError();
 }

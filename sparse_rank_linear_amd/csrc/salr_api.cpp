@@ -71,6 +71,7 @@ int t_splits_large(int64_t M, int64_t K) {
 struct FwdLayout {
   // few-row path
   int n_tiles, splits, range, vcap, r_tiles, r_pad_small, t_pieces, t_chunks;
+  int nf4_cofs, nf4_sofs;  // NF4: LDS chunk offsets of the codes and scales in a row's area
   int vals_bytes, tl_bytes, bl_bytes;
   // few-row streaming path (layers with more than one round of 16-row work)
   bool stream;
@@ -79,12 +80,23 @@ struct FwdLayout {
   int64_t m_max;
   int r_pad_large;
   // offsets (bytes)
-  size_t tsum, tfinal, ypart, T, ltpart, ylarge, total;
+  size_t tsum, tfinal, ypart, T, ltpart, t16, ylarge, dq, total;
 };
+
+// NF4 layers: the few-row kernel's dequantization pass gives each of 32
+// threads per row at most kNf4Groups groups of 8 values, so a row segment
+// holds at most this many kept values.
+constexpr int64_t kNf4MaxSeg = 2048;
+static_assert(kNf4MaxSeg / 8 + 1 <= 32 * salr::kNf4Groups, "NF4 segment too long for the dequantization pass");
 
 // r_win: the most adapter ranks one row tile multiplies (r_cat, or a fused
 // layer's largest part block); it sizes the few-row B_cat rows in LDS.
-FwdLayout fwd_layout(int64_t N, int64_t K, int32_t n_keep, int32_t r_cat, int64_t M_max, int32_t r_win = -1) {
+// nf4: the layer's values are NF4 codes (QSALR): few-row segments of at most
+// kNf4MaxSeg values with room for codes and scales at the end of each row's
+// LDS area, no streaming kernel, and (M_max > 16) a workspace region for the
+// dequantized values of the many-row kernel.
+FwdLayout fwd_layout(int64_t N, int64_t K, int32_t n_keep, int32_t r_cat, int64_t M_max, int32_t r_win = -1,
+                     bool nf4 = false) {
   if (r_win < 0) r_win = r_cat;
   FwdLayout L{};
   L.n_tiles = (int)cdiv(N, 16);
@@ -96,15 +108,27 @@ FwdLayout fwd_layout(int64_t N, int64_t K, int32_t n_keep, int32_t r_cat, int64_
   // trip), else the widest range that fits; narrower ranges while there are
   // too few workgroups to occupy the GPU.
   // (whole rows start on a chunk when n_keep is a multiple of 8)
+  // (NF4: codes of cap values + a window's 8 bytes, and the scales of its
+  // blocks, in whole chunks behind the values)
+  const auto nf4_code_chunks = [](int64_t cap) { return (int)((cap / 2 + 1 + 8 + 15) / 16 + 1); };
+  const auto nf4_scale_chunks = [](int64_t cap) { return (int)((((cap + 63) / 64 + 1) * 2 + 15) / 16 + 1); };
   const auto vcap_for = [&](int64_t range) {
-    return salr::fwd_small_vcap(std::min<int64_t>(range, n_keep), range >= K && n_keep % 8 == 0);
+    const int64_t cap = std::min<int64_t>(range, n_keep);
+    int v = salr::fwd_small_vcap(cap, range >= K && n_keep % 8 == 0);
+    if (nf4) {
+      const int need = nf4_code_chunks(cap) + nf4_scale_chunks(cap) + 1;
+      while (v < need) v += 8;  // (stride stays 1 mod 8 chunks)
+    }
+    return v;
   };
   const auto lds_for = [&](int64_t range) { return salr::fwd_small_lds_bytes(vcap_for(range), L.bl_bytes); };
   L.range = 0;
-  if (K <= salr::kMaxRangeCols && lds_for(K) <= kSmallLdsBudget && (L.n_tiles >= kFillWgs || K <= 1024)) {
+  const int max_range = nf4 ? (int)kNf4MaxSeg : salr::kMaxRangeCols;
+  if (K <= salr::kMaxRangeCols && lds_for(K) <= kSmallLdsBudget && (L.n_tiles >= kFillWgs || K <= 1024) &&
+      (!nf4 || n_keep <= kNf4MaxSeg)) {
     L.range = (int)K;
   } else {
-    for (int range = salr::kMaxRangeCols; range >= 1024; range /= 2) {
+    for (int range = max_range; range >= 1024; range /= 2) {
       if (lds_for(range) > kSmallLdsBudget) continue;
       L.range = range;
       if ((int64_t)L.n_tiles * cdiv(K, range) >= kFillWgs) break;
@@ -114,6 +138,11 @@ FwdLayout fwd_layout(int64_t N, int64_t K, int32_t n_keep, int32_t r_cat, int64_
   }
   L.splits = (int)cdiv(K, L.range);
   L.vcap = vcap_for(L.range);
+  if (nf4) {
+    const int64_t cap = std::min<int64_t>(L.range, n_keep);
+    L.nf4_sofs = L.vcap - nf4_scale_chunks(cap);
+    L.nf4_cofs = L.nf4_sofs - nf4_code_chunks(cap);
+  }
   L.vals_bytes = (int)salr::fwd_small_vals_bytes(L.vcap);
   // Few-row T pieces: 16 ranks x t_chunks 1024-column chunks, at most 8
   // pieces per rank tile (bounds the work of the workgroup that sums them);
@@ -137,7 +166,7 @@ FwdLayout fwd_layout(int64_t N, int64_t K, int32_t n_keep, int32_t r_cat, int64_
     const int64_t n_wg = cdiv(L.n_tiles, L.tiles_per_wg);
     L.svcap = std::max(salr::fwd_small_vcap(std::min<int64_t>(salr::kChunk, n_keep), false), 65);
     const bool fills = (int64_t)L.n_tiles * 100 >= (int64_t)L.tiles_per_wg * kFillWgs * 85;
-    L.stream = L.splits > 1 && fills && (int64_t)L.n_tiles * L.splits > kFillWgs && cdiv(K, 1024) <= 64 &&
+    L.stream = !nf4 && L.splits > 1 && fills && (int64_t)L.n_tiles * L.splits > kFillWgs && cdiv(K, 1024) <= 64 &&
                (int64_t)L.r_tiles * L.t_pieces <= n_wg && salr::fwd_stream_lds_bytes(L.svcap) <= 160 * 1024;
   }
   // The one-round few-row kernel (every weight workgroup resident at once)
@@ -155,16 +184,23 @@ FwdLayout fwd_layout(int64_t N, int64_t K, int32_t n_keep, int32_t r_cat, int64_
   L.tsum = off;    off = align_up(off + (size_t)L.r_tiles * L.t_pieces * 256 * 8, 256);
   L.tfinal = off;  off = align_up(off + (size_t)L.r_tiles * 128 * 8, 256);
   L.ypart = off;   off = align_up(off + (L.splits > 1 ? (size_t)L.n_tiles * L.splits * 256 * 8 : 0), 256);
-  // many-row path: fp32 split-K partials of T = X A_cat
+  // many-row path: fp32 split-K partials of T = X A_cat, then their bf16 sum
   L.T = L.ltpart = off;
+  L.t16 = off;
   if (L.m_max > kSmallM && r_cat > 0) {
     // splits * M <= 64 * max(256, ceil(M/64)) for every M <= m_max
     const size_t rows = (size_t)std::max<int64_t>(64 * 256, cdiv(L.m_max, 64) * 64);
     off = align_up(off + rows * L.r_pad_large * 4, 256);
+    L.t16 = off;
+    off = align_up(off + (size_t)L.m_max * L.r_pad_large * 2, 256);
   }
   // many-row path: fp32 K-split partials of Y (few output tiles only)
   L.ylarge = off;
   if (L.m_max > kSmallM) off = align_up(off + salr::fwd_large_part_bytes(N, K, L.m_max), 256);
+  // NF4, many-row path: the dequantized values (the bf16 layout, with its
+  // tail padding)
+  L.dq = off;
+  if (nf4 && L.m_max > kSmallM) off = align_up(off + align_up((size_t)N * n_keep * 2, 256) + kValuesPad, 256);
   L.total = off;
   return L;
 }
@@ -186,6 +222,7 @@ int salr_fuse_layers(const salr_layer_t* const* parts, int32_t n_parts, salr_lay
     const salr_layer_t* L = parts[p];
     if (!L || !dims_ok(L->N, L->K, L->n_keep, L->r_cat)) return SALR_ERR_INVALID_ARG;
     if (L->K != out->K || L->n_keep != out->n_keep) return SALR_ERR_INVALID_ARG;
+    if (L->value_format != SALR_VALUES_BF16) return SALR_ERR_INVALID_ARG;  // (fusion copies bf16 values)
     if (!L->masks || !L->offsets || (L->n_keep > 0 && !L->values)) return SALR_ERR_INVALID_ARG;
     if (L->r_cat > 0 && (!L->a_cat || !L->b_cat)) return SALR_ERR_INVALID_ARG;
     const void* ptrs[] = {L->masks, L->values, L->offsets, L->a_cat, L->b_cat};
@@ -274,6 +311,10 @@ int salr_query_sizes(int64_t N, int64_t K, int32_t n_keep, int32_t r_svd, int32_
   out->b_cat_bytes = align_up((size_t)N * r_cat * 2, 256) + kValuesPad;
   out->encode_ws_bytes = salr::encode_ws_bytes(N, K, r_svd, kMaxOversample);
   out->forward_ws_bytes = fwd_layout(N, K, n_keep, r_cat, M_max).total;
+  const int64_t nblk = cdiv(n_keep, 64);
+  out->codes_bytes = (size_t)N * nblk * 32 + kValuesPad;
+  out->scales_bytes = align_up((size_t)N * nblk * 2, 256) + kValuesPad;
+  out->forward_ws_nf4_bytes = fwd_layout(N, K, n_keep, r_cat, M_max, -1, true).total;
   return SALR_OK;
 }
 
@@ -308,8 +349,10 @@ int salr_encode(const uint16_t* W, int64_t N, int64_t K, int32_t n_keep, int32_t
   if (!ws || !aligned16(ws)) return SALR_ERR_WORKSPACE;
   if (ws_bytes < salr::encode_ws_bytes(N, K, r_svd, p.oversample)) return SALR_ERR_WORKSPACE;
   // an encoded layer is one part: a stale record from an earlier fusion
-  // into this descriptor would make the forward skip adapter ranks
+  // into this descriptor would make the forward skip adapter ranks; its
+  // values are bf16
   out->n_parts = 0;
+  out->value_format = SALR_VALUES_BF16;
   for (int e = 0; e < SALR_MAX_PARTS; ++e) out->part_rows[e] = out->part_ranks[e] = 0;
   p.W = W;
   p.N = N;
@@ -333,6 +376,25 @@ int salr_encode(const uint16_t* W, int64_t N, int64_t K, int32_t n_keep, int32_t
   return salr::encode_run(p);
 }
 
+int salr_nf4_levels(float* out) {
+  if (!out) return SALR_ERR_INVALID_ARG;
+  salr::nf4_levels(out);
+  return SALR_OK;
+}
+
+int salr_quantize_nf4(salr_layer_t* L, void* stream) {
+  if (!L || !dims_ok(L->N, L->K, L->n_keep, L->r_cat)) return SALR_ERR_INVALID_ARG;
+  if (L->value_format != SALR_VALUES_BF16) return SALR_ERR_INVALID_ARG;
+  if ((L->n_keep > 0 && !L->values) || !L->codes || !L->scales) return SALR_ERR_INVALID_ARG;
+  if ((L->values && !aligned16(L->values)) || !aligned16(L->codes) || !aligned16(L->scales))
+    return SALR_ERR_INVALID_ARG;
+  if (salr::launch_quantize_nf4(L->values, L->N, L->n_keep, L->codes, L->scales, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return SALR_ERR_HIP;
+  L->value_format = SALR_VALUES_NF4;
+  return SALR_OK;
+}
+
 int salr_linear_forward(const salr_layer_t* L, const uint16_t* X, int64_t M, uint16_t* Y, void* ws, size_t ws_bytes,
                         void* stream) {
   // (a null ws is rejected by forward_impl before the error word is used)
@@ -351,9 +413,13 @@ int salr::forward_impl(const salr_layer_t* L, const uint16_t* X, int64_t M, uint
   if (M < 0 || M > (int64_t(1) << 31) - 1) return SALR_ERR_INVALID_ARG;
   if (M == 0) return SALR_OK;
   if (!X || !Y || !L->masks || !L->offsets) return SALR_ERR_INVALID_ARG;
-  if (L->n_keep > 0 && !L->values) return SALR_ERR_INVALID_ARG;
+  if (L->value_format != SALR_VALUES_BF16 && L->value_format != SALR_VALUES_NF4) return SALR_ERR_INVALID_ARG;
+  const bool nf4 = L->value_format == SALR_VALUES_NF4;
+  if (!nf4 && L->n_keep > 0 && !L->values) return SALR_ERR_INVALID_ARG;
+  if (nf4 && L->n_keep > 0 && (!L->codes || !L->scales)) return SALR_ERR_INVALID_ARG;
   if (L->r_cat > 0 && (!L->a_cat || !L->b_cat)) return SALR_ERR_INVALID_ARG;
-  const void* ptrs[] = {X, Y, L->masks, L->values, L->offsets, L->a_cat, L->b_cat};
+  const void* ptrs[] = {X, Y, L->masks, nf4 ? nullptr : L->values, L->offsets, L->a_cat, L->b_cat,
+                        nf4 ? L->codes : nullptr, nf4 ? L->scales : nullptr};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return SALR_ERR_INVALID_ARG;
   if (static_cast<const void*>(X) == static_cast<const void*>(Y)) return SALR_ERR_INVALID_ARG;
@@ -377,8 +443,9 @@ int salr::forward_impl(const salr_layer_t* L, const uint16_t* X, int64_t M, uint
   }
   // (every argument check above comes before the workspace's)
   if (!ws || !aligned16(ws)) return SALR_ERR_WORKSPACE;
-  const FwdLayout W = fwd_layout(L->N, L->K, L->n_keep, L->r_cat, M, r_win);
+  const FwdLayout W = fwd_layout(L->N, L->K, L->n_keep, L->r_cat, M, r_win, nf4);
   if (ws_bytes < W.total) return SALR_ERR_WORKSPACE;
+  const int32_t nblk = (int32_t)cdiv(L->n_keep, 64);
 
   hipError_t err;
   if (M <= kSmallM && W.stream) {
@@ -459,6 +526,15 @@ int salr::forward_impl(const salr_layer_t* L, const uint16_t* X, int64_t M, uint
     a.err = err_word;
     a.ycount = at<uint32_t>(ws, kCounterY);
     a.ypart = at<uint64_t>(ws, W.ypart);
+    if (nf4) {
+      a.nf4 = 1;
+      a.codes = L->codes;
+      a.scales = L->scales;
+      a.cb_row = nblk * 32;
+      a.nblk = nblk;
+      a.cofs = W.nf4_cofs;
+      a.sofs = W.nf4_sofs;
+    }
     err = salr::launch_fwd_small(a, s);
   } else {
     int t_splits = 0;
@@ -467,6 +543,7 @@ int salr::forward_impl(const salr_layer_t* L, const uint16_t* X, int64_t M, uint
       t.X = X;
       t.a_cat = L->a_cat;
       t.tpart = at<float>(ws, W.ltpart);
+      t.t16 = at<uint16_t>(ws, W.t16);
       t.M = (int32_t)M;
       t.K = (int32_t)L->K;
       t.r_cat = L->r_cat;
@@ -478,12 +555,21 @@ int salr::forward_impl(const salr_layer_t* L, const uint16_t* X, int64_t M, uint
       err = salr::launch_lowrank_t(t, s);
       if (err != hipSuccess) return SALR_ERR_HIP;
     }
+    // NF4: the values decoded to bf16 first (the many-row kernel is bound by
+    // its matrix cores, not by the bytes of the values)
+    const uint16_t* values = L->values;
+    if (nf4) {
+      uint16_t* dq = at<uint16_t>(ws, W.dq);
+      if (salr::launch_dequantize_nf4(L->codes, L->scales, L->N, L->n_keep, dq, s) != hipSuccess) return SALR_ERR_HIP;
+      values = dq;
+    }
     LargeFwdArgs a{};
     a.masks = L->masks;
-    a.values = L->values;
+    a.values = values;
     a.b_cat = L->b_cat;
     a.X = X;
     a.tpart = L->r_cat > 0 ? at<float>(ws, W.ltpart) : nullptr;
+    a.t16 = L->r_cat > 0 ? at<uint16_t>(ws, W.t16) : nullptr;
     a.t_splits = t_splits;
     a.Y = Y;
     a.N = L->N;

@@ -6,6 +6,8 @@
 
 namespace salr {
 
+void nf4_levels(float out[16]);  // (QSALR value codec, see below)
+
 constexpr int kMaxRangeCols = 4096;  // columns per few-row workgroup
 // Launch-tag ticket words in the forward workspace (see salr_device.hpp).
 constexpr uint32_t kTicketGroups = 16;
@@ -51,7 +53,18 @@ struct SmallFwdArgs {
   uint32_t* err;           // set nonzero when a wait times out
   uint32_t* ycount;        // [n_tiles]
   uint64_t* ypart;         // [n_tiles][splits][256] tagged fp32
+  // NF4 values (nf4 != 0): codes and scales go to the end of each row's LDS
+  // area (chunk offsets cofs and sofs) and are dequantized into the bf16
+  // stream the decode reads
+  int32_t nf4;
+  const uint8_t* codes;    // [N][cb_row]
+  const uint16_t* scales;  // [N][nblk]
+  int32_t cb_row, nblk, cofs, sofs;
+  float levels[16];        // the NF4 levels (set by launch_fwd_small)
 };
+// Groups of 8 values per thread of the few-row dequantization pass (32
+// threads per row).
+constexpr int kNf4Groups = 9;
 hipError_t launch_fwd_small(const SmallFwdArgs& a, hipStream_t s);
 size_t fwd_small_vals_bytes(int vcap);
 // Dynamic LDS bytes of one few-row workgroup.
@@ -109,6 +122,7 @@ struct LowRankTArgs {
   const uint16_t* X;       // [M][K]
   const uint16_t* a_cat;   // [r_cat][K]
   float* tpart;            // [splits][M][r_pad] fp32 partial sums of X A_cat
+  uint16_t* t16;           // [M][r_pad] bf16 T (their sum, written after them)
   int32_t M, K, r_cat, r_pad;
   int32_t splits, k_chunk; // K-splits, columns per split (multiple of 64)
 };
@@ -120,6 +134,7 @@ struct LargeFwdArgs {
   const uint16_t* b_cat;   // [N][r_cat]
   const uint16_t* X;       // [M][K]
   const float* tpart;      // [t_splits][M][r_pad] partial T, null when r_cat == 0
+  const uint16_t* t16;     // [M][r_pad] bf16 T (sum of the partials), null when r_cat == 0
   uint16_t* Y;             // [M][N]
   int64_t N;
   int32_t K, n_keep, r_cat, r_pad, M;
@@ -154,6 +169,20 @@ size_t fwd_large_part_bytes(int64_t N, int64_t K, int64_t M_max);
 // zeros elsewhere.
 hipError_t launch_fuse_b(const uint16_t* src, int64_t rows, int r_src, uint16_t* dst, int r_dst, int col0,
                          hipStream_t s);
+
+// ----------------------------------------------------------------------------
+// QSALR value codec (NF4): 16 levels, 64-value blocks with a bf16 absmax
+// scale, codes nibble-packed (value 2b low, 2b + 1 high nibble of byte b),
+// rows of 32 bytes per block.
+struct Nf4Levels {
+  float v[16];
+};
+constexpr uint32_t kNf4ZeroCode = 7;  // the level 0.0
+void nf4_levels(float out[16]);
+hipError_t launch_quantize_nf4(const uint16_t* values, int64_t N, int32_t n_keep, uint8_t* codes, uint16_t* scales,
+                               hipStream_t s);
+hipError_t launch_dequantize_nf4(const uint8_t* codes, const uint16_t* scales, int64_t N, int32_t n_keep,
+                                 uint16_t* values, hipStream_t s);
 
 // ----------------------------------------------------------------------------
 // Encode kernels.

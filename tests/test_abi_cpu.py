@@ -51,6 +51,36 @@ def test_probe_validation_paths():
     assert lib.salr_probe_mfma(p, 1, 1, 2, None) == -1
 
 
+def test_nf4_levels_equal_the_oracle():
+    """The library's level table (normal quantiles by bisection on erfc)
+    equals the oracle's (scipy quantiles), bit for bit."""
+    import numpy as np
+    from oracle import nf4
+
+    got = np.array(srl.nf4_levels(), dtype=np.float32)
+    assert np.array_equal(got.view(np.uint32), nf4.nf4_levels().view(np.uint32))
+    assert srl.lib().salr_nf4_levels(None) == -1
+
+
+def test_nf4_sizes_and_quantize_validation():
+    sz = srl.query_sizes(100, 520, 260, 4, 12, 300)
+    assert sz["codes_bytes"] >= 100 * 5 * 32 and sz["scales_bytes"] >= 100 * 5 * 2
+    assert sz["forward_ws_nf4_bytes"] >= sz["forward_ws_bytes"] + 100 * 260 * 2   # dequantized values
+    lib = srl.lib()
+    assert lib.salr_quantize_nf4(None, None) == -1
+    d = _layer()
+    assert lib.salr_quantize_nf4(C.byref(d), None) == -1          # no codes / scales
+    d.codes, d.scales = 0x50000000, 0x60000008                   # misaligned scales
+    assert lib.salr_quantize_nf4(C.byref(d), None) == -1
+    d.scales, d.value_format = 0x60000000, 1                      # already NF4
+    assert lib.salr_quantize_nf4(C.byref(d), None) == -1
+    d = _layer()
+    d.value_format = 2                                            # unknown format
+    assert _fwd(d) == -1
+    d.value_format = 1                                            # NF4 without codes
+    assert _fwd(d) == -1
+
+
 def test_status_strings_and_version():
     lib = srl.lib()
     for code in B.STATUS_NAMES:
