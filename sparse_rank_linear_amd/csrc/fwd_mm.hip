@@ -14,12 +14,13 @@
 //   * waves 0-3 (consumers) each own 128 tokens x 64 outputs (8 x 4 MFMA
 //     16x16 tiles, 32 accumulators) and do nothing but read operands from
 //     LDS and issue v_mfma_f32_16x16x32_bf16;
-//   * waves 4-7 (producers) decode the W tile of the next phase into LDS,
-//     store the X tile of the next phase (loaded into registers a phase
-//     earlier) and keep the packed values two tiles ahead in registers.
-// (X goes through registers rather than direct-to-LDS loads: with such a
-// load in flight the compiler makes every LDS access of the wave wait for
-// it, which would serialize the producers' loads with their decode.)
+//     Each phase they also send the X tile two phases ahead straight to LDS
+//     (global_load_lds, a ring of three buffers), issued after their operand
+//     reads: with such a load in flight the compiler makes every later LDS
+//     access of the wave wait for it, and a consumer has none left in the
+//     phase;
+//   * waves 4-7 (producers) decode the W tile of the next phase into LDS and
+//     keep the packed values two tiles ahead in registers.
 // One LDS barrier per phase.  Because the decode and the multiply are in
 // different waves, a SIMD issues the producer's vector instructions while
 // its consumer's matrix instructions run.
@@ -44,7 +45,7 @@ constexpr int kThreads = 512;
 constexpr int kCons = 256;           // consumer threads (waves 0-3)
 constexpr int kVRow = 40;            // words per row of staged values (10 chunks)
 constexpr int kVLoads = 5;           // 16-byte value chunks per producer thread per tile
-constexpr int kXLoads = BM * 8 / 256;  // X chunks per producer thread per tile
+constexpr int kXLoads = BM * 8 / 256;  // X chunks (direct-to-LDS loads) per consumer thread per tile
 
 // A 64-column bf16 tile row is 8 chunks of 16 bytes at chunk slot
 // (c ^ (row & 7)): a 16-row MFMA operand read (one chunk per row) hits every
@@ -52,8 +53,19 @@ constexpr int kXLoads = BM * 8 / 256;  // X chunks per producer thread per tile
 // bytes, contiguous) fills 8 rows by choosing which chunk each lane fetches.
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
 
+// s_waitcnt with vmcnt = n (n < 64), expcnt and lgkmcnt not waited on
+// (gfx9 encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14); the
+// compiler fences keep every memory operation on its side of the wait.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 __global__ __launch_bounds__(kThreads) void fwd_mm_kernel(LargeFwdArgs a) {
-  __shared__ u32x4_t xl0[BM * 8], xl1[BM * 8];  // X tiles (or bf16 T for the low-rank tiles)
+  __shared__ u32x4_t xl0[BM * 8], xl1[BM * 8], xl2[BM * 8];  // X ring (or bf16 T for the low-rank tiles)
   __shared__ u32x4_t wl0[BN * 8], wl1[BN * 8];  // decoded W tiles (or B_cat^T slices)
   __shared__ uint32_t vl[BN * kVRow];     // packed values of the tile being decoded
   __shared__ u32x2_t luts[4][16];  // the nibble selectors, one copy per producer wave
@@ -98,18 +110,63 @@ __global__ __launch_bounds__(kThreads) void fwd_mm_kernel(LargeFwdArgs a) {
   const int n_lr = (split == 0 && rhi > rlo) ? (rhi - rlo + 63) / 64 : 0;
   const int phases = n_main + n_lr;
 
+  // X buffer of phase p (a ring of three) and W buffer (two)
+  const auto xbuf = [&](int p) __attribute__((always_inline)) -> u32x4_t* {
+    const int b = p % 3;
+    return b == 0 ? xl0 : (b == 1 ? xl1 : xl2);
+  };
+
   if (wave < 4) {
     // ------------------------------------------------------------ consumer
     const int wm = wave >> 1, wn = wave & 1;  // 128-token half, 64-output half
+    // X tile loads: load j of this wave fills tile rows 8 (8 wave + j) ..
+    // +7, lane l fetching chunk (l & 7) ^ (row & 7) of row 8 (8 wave + j) +
+    // l / 8 (the swizzled layout), from byte offsets formed once (used when
+    // M * K * 2 < 2^32).  Rows past M and columns past K read clamped
+    // (in-bounds) addresses: such rows reach outputs that are never stored,
+    // such columns meet zero weights.
+    const int nk_all = (a.K + 63) / 64;
+    uint32_t xoff[kXLoads];
+#pragma unroll
+    for (int j = 0; j < kXLoads; ++j) {
+      const int row = 8 * (kXLoads * wave + j) + (lane >> 3);
+      const int chunk = (lane & 7) ^ (row & 7);
+      xoff[j] = ((uint32_t)min(m0 + row, a.M - 1) * (uint32_t)a.K + 8u * (uint32_t)chunk) * 2u;
+    }
+    const auto dma_x = [&](u32x4_t* xt, int kt) __attribute__((always_inline)) {
+      kt = min(kt, nk_all - 1);
+      const int k0 = kt * 64;
+      if (a.x_off32 && k0 + 64 <= a.K) {
+        const char* const xb = reinterpret_cast<const char*>(a.X + k0);
+#pragma unroll
+        for (int j = 0; j < kXLoads; ++j)
+          __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(xb + xoff[j]),
+                                           reinterpret_cast<uint32_t*>(xt + (kXLoads * wave + j) * 64), 16, 0, 0);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kXLoads; ++j) {
+          const int row = 8 * (kXLoads * wave + j) + (lane >> 3);
+          const int chunk = (lane & 7) ^ (row & 7);
+          const int m = min(m0 + row, a.M - 1), k = min(k0 + 8 * chunk, a.K - 8);
+          __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint32_t*>(a.X + (size_t)m * a.K + k),
+                                           reinterpret_cast<uint32_t*>(xt + (kXLoads * wave + j) * 64), 16, 0, 0);
+        }
+      }
+    };
     f32x4_t acc[4][8];
 #pragma unroll
     for (int x = 0; x < 4; ++x)
 #pragma unroll
       for (int y = 0; y < 8; ++y) acc[x][y] = zero4();
-    lds_barrier();  // (prologue: tile 0 staged by the producers)
+    // prologue: X of the first two tiles
+    if (n_main > 0) dma_x(xl0, kt0);
+    if (n_main > 1) dma_x(xl1, kt0 + 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();  // (and tile 0's W staged by the producers)
     for (int p = 0; p < phases; ++p) {
-      const u32x4_t* xt = (p & 1) ? xl1 : xl0;
+      const u32x4_t* xt = xbuf(p);
       const u32x4_t* wt = (p & 1) ? wl1 : wl0;
+      const bool more = p + 2 < n_main;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         u32x4_t av[4], bv[8];
@@ -117,11 +174,21 @@ __global__ __launch_bounds__(kThreads) void fwd_mm_kernel(LargeFwdArgs a) {
         for (int t = 0; t < 4; ++t) av[t] = wt[swz(wn * 64 + t * 16 + i, ks * 4 + g)];
 #pragma unroll
         for (int t = 0; t < 8; ++t) bv[t] = xt[swz(wm * 128 + t * 16 + i, ks * 4 + g)];
+        // after the phase's last operand reads: X two tiles ahead into the
+        // buffer freed a phase ago (every wave's reads of it ended at the
+        // last barrier)
+        if (ks == 1 && more) dma_x(xbuf(p + 2), kt0 + p + 2);
 #pragma unroll
         for (int tn = 0; tn < 4; ++tn)
 #pragma unroll
           for (int tm = 0; tm < 8; ++tm) acc[tn][tm] = mfma_16x16x32(av[tn], bv[tm], acc[tn][tm]);
       }
+      // X of the next phase (issued a phase ago) has landed once at most
+      // this phase's loads are outstanding
+      if (more)
+        wait_vmcnt<kXLoads>();
+      else
+        __builtin_amdgcn_s_waitcnt(0);
       lds_barrier();
     }
 
@@ -185,34 +252,6 @@ __global__ __launch_bounds__(kThreads) void fwd_mm_kernel(LargeFwdArgs a) {
   auto mask_raw = [&](int kt) __attribute__((always_inline)) -> uint64_t { return mrow[min(kt, a.kw - 1)]; };
   auto mask_ok = [&](uint64_t w, int kt) __attribute__((always_inline)) -> uint64_t { return (row_ok && kt < nk) ? w : 0ull; };
 
-  // X tile loads: this thread carries chunk xch of tile rows xrow0 + 32 u
-  // (8 neighbouring threads read one row's 128 bytes).  Rows past M and
-  // columns past K read clamped (in-bounds) addresses: such rows reach
-  // outputs that are never stored, such columns meet zero weights.
-  const int xrow0 = ptid >> 3, xch = ptid & 7;
-  const int nk_all = (a.K + 63) / 64;
-  // byte offsets of the rows (used when M * K * 2 < 2^32)
-  uint32_t xoff[kXLoads];
-#pragma unroll
-  for (int u = 0; u < kXLoads; ++u)
-    xoff[u] = (uint32_t)min(m0 + xrow0 + 32 * u, a.M - 1) * (uint32_t)a.K * 2u;
-  u32x4_t xr[kXLoads];
-  auto load_x = [&](int kt) __attribute__((always_inline)) {
-    const int k = min(min(kt, nk_all - 1) * 64 + 8 * xch, a.K - 8);
-    if (a.x_off32) {
-      const char* const xb = reinterpret_cast<const char*>(a.X + k);
-#pragma unroll
-      for (int u = 0; u < kXLoads; ++u) xr[u] = load16(xb + xoff[u]);
-    } else {
-#pragma unroll
-      for (int u = 0; u < kXLoads; ++u)
-        xr[u] = load16(a.X + (size_t)min(m0 + xrow0 + 32 * u, a.M - 1) * a.K + k);
-    }
-  };
-  auto store_x = [&](u32x4_t* xt) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < kXLoads; ++u) xt[swz(xrow0 + 32 * u, xch)] = xr[u];
-  };
   // The packed values of one tile of this row: the 10 chunks from the one
   // holding its first value (value index row_base + run) cover up to 64
   // values and the decode window's overrun; this thread loads every other
@@ -300,8 +339,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mm_kernel(LargeFwdArgs a) {
     run0 = row_ok ? base + sum : 0u;
   }
 
-  // ---- prologue: tile kt0 decoded and its X in LDS; X of kt0+1 and the
-  // values of kt0+1, kt0+2 on their way
+  // ---- prologue: tile kt0 decoded; the values of kt0+1, kt0+2 on their way
   const uint64_t mk0 = mask_ok(mask_raw(kt0), kt0);
   uint64_t mk1 = mask_ok(mask_raw(kt0 + 1), kt0 + 1);
   uint64_t mk2 = mask_ok(mask_raw(kt0 + 2), kt0 + 2);
@@ -310,10 +348,7 @@ __global__ __launch_bounds__(kThreads) void fwd_mm_kernel(LargeFwdArgs a) {
   uint32_t run2 = run1 + (uint32_t)__popcll(mk1);   // of tile kt+2
   u32x4_t va[kVLoads], vb[kVLoads];
   if (n_main > 0) {
-    load_x(kt0);
     load_v(va, run0);
-    store_x(xl0);
-    load_x(kt0 + 1);
     load_v(vb, run1);
     store_v(va);
     decode(wl0, run0, mk0);
@@ -323,18 +358,15 @@ __global__ __launch_bounds__(kThreads) void fwd_mm_kernel(LargeFwdArgs a) {
   }
   lds_barrier();
 
-  // ---- phases: the consumers multiply the tile of phase p (kt = kt0 + p,
-  // buffers of parity p) while this wave prepares the tile of phase p + 1
-  // and issues the loads of later tiles.  Main phases are unrolled by two so
-  // that the buffers and the two value register sets are named.
-  auto main_phase = [&](int p, u32x4_t(&vnext)[kVLoads], u32x4_t* xnext, u32x4_t* wnext)
-                        __attribute__((always_inline)) {
+  // ---- phases: the consumers multiply the tile of phase p (kt = kt0 + p)
+  // while this wave prepares the W tile of phase p + 1 and issues the loads
+  // of later tiles.  Main phases are unrolled by two so that the W buffers
+  // and the two value register sets are named.
+  auto main_phase = [&](int p, u32x4_t(&vnext)[kVLoads], u32x4_t* wnext) __attribute__((always_inline)) {
     const int kt = kt0 + p;
-    // tile kt+1: X (loaded a phase ago) to LDS, X of kt+2 requested; its
-    // values (loaded two phases ago) to LDS, decoded; the values of kt+3
-    // requested into the set just stored, and the bitmap word of kt+4
-    store_x(xnext);
-    load_x(kt + 2);
+    // tile kt+1: its values (loaded two phases ago) to LDS, decoded; the
+    // values of kt+3 requested into the set just stored, and the bitmap
+    // word of kt+4
     store_v(vnext);
     decode(wnext, run1, mk1);
     const uint64_t mk3 = mask_ok(mk3raw, kt + 3);
@@ -349,13 +381,15 @@ __global__ __launch_bounds__(kThreads) void fwd_mm_kernel(LargeFwdArgs a) {
   };
   int p = 0;
   for (; p + 2 < n_main; p += 2) {
-    main_phase(p, vb, xl1, wl1);
-    main_phase(p + 1, va, xl0, wl0);
+    main_phase(p, vb, wl1);
+    main_phase(p + 1, va, wl0);
   }
-  if (p + 1 < n_main) main_phase(p++, vb, xl1, wl1);
-  // the last main phase and the low-rank phases: stage the next low-rank tile
+  if (p + 1 < n_main) main_phase(p++, vb, wl1);
+  // the last main phase and the low-rank phases: stage the next low-rank
+  // tile (its X buffer got no direct-to-LDS load: the consumers load X only
+  // for main tiles)
   for (; p < phases; ++p) {
-    if (p + 1 < phases) stage_lowrank(p + 1 - n_main, ((p + 1) & 1) ? xl1 : xl0, ((p + 1) & 1) ? wl1 : wl0);
+    if (p + 1 < phases) stage_lowrank(p + 1 - n_main, xbuf(p + 1), ((p + 1) & 1) ? wl1 : wl0);
     lds_barrier();
   }
 }
