@@ -204,6 +204,27 @@ def encode(W_bits, n_keep: int, r_svd: int, lora_A=(), lora_B=()) -> Encoded:
 # [summary] Methodology 3: one concatenated low-rank product.
 # ---------------------------------------------------------------------------
 
+def decode_keep(masks: np.ndarray, K: int) -> np.ndarray:
+    """The kept set, bool [N x K], from the bitmap words."""
+    masks = np.asarray(masks, dtype=np.uint64)
+    N, nw = masks.shape
+    bits = (masks[:, :, None] >> np.arange(WORD, dtype=np.uint64)) & np.uint64(1)
+    return bits.reshape(N, nw * WORD)[:, :K].astype(bool)
+
+
+def decode_dense_bits(masks: np.ndarray, values: np.ndarray, K: int) -> np.ndarray:
+    """Stage-1 decode keeping bit patterns: uint16 [N x K], row n's values at
+    the set bits of its bitmap in ascending column order, 0 elsewhere."""
+    keep = decode_keep(masks, K)
+    N = keep.shape[0]
+    out = np.zeros((N, K), dtype=np.uint16)
+    values = np.asarray(values, dtype=np.uint16)
+    for n in range(N):
+        c = int(keep[n].sum())
+        out[n, keep[n]] = values[n, :c]
+    return out
+
+
 def decode_dense(masks: np.ndarray, values: np.ndarray, K: int) -> np.ndarray:
     """Stage-1 decode to a dense float64 W_s [N x K]: row n's values are
     placed, in ascending column order, at the set bits of its bitmap."""
