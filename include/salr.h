@@ -297,6 +297,94 @@ int salr_linear_forward_noalloc(const salr_layer_t* L, const uint16_t* X, int64_
 int salr_fuse_layers(const salr_layer_t* const* parts, int32_t n_parts,
                      salr_layer_t* out, void* stream);
 
+/*
+ * Backward pass, for fine-tuning the adapters while the base weight stays
+ * frozen (summary, Methodology 2: the SVD residual adapter is trained
+ * together with the LoRA adapters; Methodology 1: the mask belongs to the
+ * frozen base weight only).  For Y = X W_s^T + (X A_cat) B_cat and the
+ * upstream gradient dY = dL/dY:
+ *     dX     = dY W_s + (dY B_cat^T) A_cat^T
+ *     dA_cat = X^T (dY B_cat^T)          dB_cat = (X A_cat)^T dY
+ * W_s itself gets no gradient.  dX is a forward of the TRANSPOSED layer:
+ * W_s^T (K rows of N columns) in the encoded-layer layout, with adapters
+ * B_cat^T and A_cat^T.  Its encoding is built once per frozen weight by
+ * salr_transpose_layer; a row of it (a column of W_s) may keep fewer than
+ * n_keep columns: its kept values come first, +0.0 fills the rest of the
+ * row, and the forward kernels accept such rows.  Limits: the layer's own,
+ * plus N % 8 == 0 and N <= 2^20 (W_s^T's column limits), else
+ * SALR_ERR_UNSUPPORTED.
+ */
+
+/* Workspace bytes of salr_transpose_count / salr_transpose_layer for an
+ * N x K layer (`out` host).  Errors: INVALID_ARG. */
+int salr_transpose_ws_bytes(int64_t N, int64_t K, size_t* out);
+
+/*
+ * salr_transpose_count - the largest number of kept entries in one column of
+ * W_s (host `*n_keep_t`), which is the n_keep of the transposed layer: size
+ * its buffers with salr_query_sizes(K, N, n_keep_t, 0, r_cat, M_max, ...).
+ * Reads L->masks only.  ws: device, salr_transpose_ws_bytes long (contents
+ * on entry do not matter).  SYNCHRONOUS (waits for `stream`).
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
+ */
+int salr_transpose_count(const salr_layer_t* L, int32_t* n_keep_t, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/*
+ * salr_transpose_layer - the encoding of W_s^T from that of W_s (a bf16
+ * layer).  LT: host pointer; the caller fills N = L->K, K = L->N,
+ * n_keep >= the count from salr_transpose_count, and the masks, values and
+ * offsets buffers (sizes from salr_query_sizes as above; not overlapping
+ * L's).  Written: LT->masks (bit n of word w of row k set iff W_s keeps
+ * (64w + n, k)), LT->values (row k: column k's kept values in ascending row
+ * order, bit-exact, then +0.0 up to n_keep), LT->offsets (kept rows of
+ * column k before every 1024th row), and the fields r_cat = L->r_cat,
+ * n_parts = 0, value_format = SALR_VALUES_BF16, codes = scales = NULL.
+ * LT->a_cat and LT->b_cat are neither read nor written (the backward supplies
+ * the transposed adapters).  ws as for salr_transpose_count.  SYNCHRONOUS.
+ * Errors: INVALID_ARG (shapes, nulls, alignment, LT->n_keep below the
+ * largest column count), UNSUPPORTED (limits, an NF4 layer), WORKSPACE, HIP.
+ */
+int salr_transpose_layer(const salr_layer_t* L, salr_layer_t* LT, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* Workspace bytes of salr_linear_backward for an N x K layer whose
+ * transposed layer keeps n_keep_t per row, adapter rank r_cat, at most M_max
+ * tokens per call (`out` host).  Errors: INVALID_ARG, UNSUPPORTED. */
+int salr_backward_ws_bytes(int64_t N, int64_t K, int32_t n_keep_t,
+                           int32_t r_cat, int64_t M_max, size_t* out);
+
+/*
+ * salr_linear_backward - dX, dA_cat and dB_cat of one layer for M tokens.
+ *
+ * L    host pointer to the layer (its a_cat and b_cat are read; any value
+ *      format, the base weight is read through LT).
+ * LT   host pointer to its transposed layer from salr_transpose_layer.
+ * X    device bf16 [M][K] (the forward's input); dY device bf16 [M][N].
+ * dX   device bf16 [M][K], or NULL to skip it (a first layer).  Computed
+ *      exactly as salr_linear_forward computes Y for LT and input dY: fp32
+ *      accumulation, dY B_cat^T rounded to bf16 before it meets A_cat^T, dX
+ *      rounded to bf16.  May not alias dY.
+ * dA   device float [r_cat][K]: the gradient of a_cat AS STORED
+ *      (dA[j][k] = sum_m G[m][j] X[m][k], G = bf16(dY B_cat^T)).
+ * dB   device float [N][r_cat]: the gradient of b_cat as stored
+ *      (dB[n][j] = sum_m dY[m][n] T[m][j], T = bf16(X A_cat)).  For a fused
+ *      layer it covers b_cat's zero blocks too (keep them at zero).
+ *      dA and dB are required when r_cat > 0; they are overwritten (not
+ *      accumulated into), fp32 accumulation over the tokens; M == 0 writes
+ *      zeros.
+ * ws   device workspace of at least salr_backward_ws_bytes for some
+ *      M_max >= M; zero-filled before its first use, then left ready by
+ *      every completed call; calls that share it must be ordered.  As for
+ *      the forward, a timed-out bounded wait sets the uint32 at byte 8.
+ * Asynchronous on `stream`.  Errors: INVALID_ARG (shapes, nulls, alignment,
+ * LT not matching L), UNSUPPORTED, WORKSPACE, HIP.
+ */
+int salr_linear_backward(const salr_layer_t* L, const salr_layer_t* LT,
+                         const uint16_t* X, const uint16_t* dY, int64_t M,
+                         uint16_t* dX, float* dA, float* dB, void* ws,
+                         size_t ws_bytes, void* stream);
+
 /* Static English text for a status code (never NULL). */
 const char* salr_status_string(int status);
 

@@ -4,7 +4,7 @@ SALR (Sparsity-Aware Low-Rank Representation) serves a linear layer as
 Y = X W_s^T + (X A_cat) B_cat: W_s is the frozen weight after a static
 per-row magnitude prune, stored as a bitmap plus packed bf16 values, and
 A_cat / B_cat stack the truncated-SVD residual adapter with the LoRA
-adapters.  Encode and forward run in hand-written gfx950 HIP kernels behind
+adapters.  Encode, forward and the adapter backward run in hand-written gfx950 HIP kernels behind
 the C ABI of include/salr.h (libsalr.so); this package only marshals
 arguments (binding.py) and draws synthetic inputs (synth.py).
 """
@@ -16,10 +16,13 @@ from .binding import (  # noqa: F401
     SalrError,
     SalrLayer,
     WaitTimeout,
+    backward_workspace,
+    backward_ws_bytes,
     encode,
     forward_workspace,
     fuse,
     lib,
+    linear_backward,
     linear_forward,
     linear_forward_noalloc,
     nf4_levels,
@@ -27,12 +30,16 @@ from .binding import (  # noqa: F401
     probe_stream_read,
     quantize_nf4,
     query_sizes,
+    transpose_count,
+    transpose_layer,
+    transpose_ws_bytes,
     wait_error,
     workspace,
 )
 
 __all__ = [
-    "EXPORTS", "LIB_PATH", "NOALLOC_SCRATCH_BYTES", "SalrError", "SalrLayer", "WaitTimeout", "encode", "forward_workspace", "fuse", "lib",
-    "linear_forward", "linear_forward_noalloc", "nf4_levels", "probe_mfma", "probe_stream_read",
-    "quantize_nf4", "query_sizes", "wait_error", "workspace",
+    "EXPORTS", "LIB_PATH", "NOALLOC_SCRATCH_BYTES", "SalrError", "SalrLayer", "WaitTimeout", "backward_workspace",
+    "backward_ws_bytes", "encode", "forward_workspace", "fuse", "lib", "linear_backward", "linear_forward",
+    "linear_forward_noalloc", "nf4_levels", "probe_mfma", "probe_stream_read", "quantize_nf4", "query_sizes",
+    "transpose_count", "transpose_layer", "transpose_ws_bytes", "wait_error", "workspace",
 ]

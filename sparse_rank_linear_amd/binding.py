@@ -36,6 +36,11 @@ EXPORTS = (
     "salr_version",
     "salr_nf4_levels",
     "salr_quantize_nf4",
+    "salr_transpose_ws_bytes",
+    "salr_transpose_count",
+    "salr_transpose_layer",
+    "salr_backward_ws_bytes",
+    "salr_linear_backward",
     # include/salr_probe.h
     "salr_probe_stream_read",
     "salr_probe_mfma",
@@ -125,6 +130,21 @@ def _lib():
         lib.salr_nf4_levels.restype = C.c_int
         lib.salr_quantize_nf4.argtypes = [C.POINTER(salr_layer_t), C.c_void_p]
         lib.salr_quantize_nf4.restype = C.c_int
+        lib.salr_transpose_ws_bytes.argtypes = [C.c_int64, C.c_int64, C.POINTER(C.c_size_t)]
+        lib.salr_transpose_ws_bytes.restype = C.c_int
+        lib.salr_transpose_count.argtypes = [C.POINTER(salr_layer_t), C.POINTER(C.c_int32), C.c_void_p, C.c_size_t,
+                                             C.c_void_p]
+        lib.salr_transpose_count.restype = C.c_int
+        lib.salr_transpose_layer.argtypes = [C.POINTER(salr_layer_t), C.POINTER(salr_layer_t), C.c_void_p,
+                                             C.c_size_t, C.c_void_p]
+        lib.salr_transpose_layer.restype = C.c_int
+        lib.salr_backward_ws_bytes.argtypes = [C.c_int64, C.c_int64, C.c_int32, C.c_int32, C.c_int64,
+                                               C.POINTER(C.c_size_t)]
+        lib.salr_backward_ws_bytes.restype = C.c_int
+        lib.salr_linear_backward.argtypes = [C.POINTER(salr_layer_t), C.POINTER(salr_layer_t), C.c_void_p,
+                                             C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p,
+                                             C.c_void_p, C.c_size_t, C.c_void_p]
+        lib.salr_linear_backward.restype = C.c_int
         lib.salr_probe_stream_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int32, C.c_void_p]
         lib.salr_probe_stream_read.restype = C.c_int
         lib.salr_probe_mfma.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p]
@@ -441,6 +461,92 @@ def fuse(layers, stream=None) -> SalrLayer:
     _check(st, "salr_fuse_layers")
     out.parts = tuple((od.part_rows[p], od.part_ranks[p]) for p in range(od.n_parts))
     return out
+
+
+def transpose_ws_bytes(N: int, K: int) -> int:
+    out = C.c_size_t()
+    _check(_lib().salr_transpose_ws_bytes(N, K, C.byref(out)), "salr_transpose_ws_bytes")
+    return out.value
+
+
+def transpose_count(layer: SalrLayer, ws=None, stream=None) -> int:
+    """The largest number of kept entries in one column of W_s (the n_keep
+    of the transposed layer).  Synchronous."""
+    if ws is None:
+        ws = workspace(transpose_ws_bytes(layer.N, layer.K), layer.masks.device)
+    out = C.c_int32()
+    desc = layer.descriptor()
+    st = _lib().salr_transpose_count(C.byref(desc), C.byref(out), C.c_void_p(ws.data_ptr()),
+                                     ws.numel() * ws.element_size(), _stream_ptr(stream))
+    _check(st, "salr_transpose_count")
+    return out.value
+
+
+def transpose_layer(layer: SalrLayer, n_keep: int | None = None, ws=None, stream=None) -> SalrLayer:
+    """The encoding of W_s^T (K rows of N columns) built on the GPU, for
+    the backward pass; n_keep defaults to the largest column count.
+    Synchronous.  Its adapters are not allocated (the backward supplies the
+    transposed adapters)."""
+    dev = layer.masks.device
+    if ws is None:
+        ws = workspace(transpose_ws_bytes(layer.N, layer.K), dev)
+    if n_keep is None:
+        n_keep = transpose_count(layer, ws, stream)
+    lt = SalrLayer.empty(layer.K, layer.N, n_keep, 0, 0, dev)
+    lt.r_cat = layer.r_cat
+    desc = layer.descriptor()
+    tdesc = lt.descriptor()
+    tdesc.a_cat = tdesc.b_cat = None
+    st = _lib().salr_transpose_layer(C.byref(desc), C.byref(tdesc), C.c_void_p(ws.data_ptr()),
+                                     ws.numel() * ws.element_size(), _stream_ptr(stream))
+    _check(st, "salr_transpose_layer")
+    return lt
+
+
+def backward_ws_bytes(N: int, K: int, n_keep_t: int, r_cat: int, M_max: int) -> int:
+    out = C.c_size_t()
+    _check(_lib().salr_backward_ws_bytes(N, K, n_keep_t, r_cat, M_max, C.byref(out)), "salr_backward_ws_bytes")
+    return out.value
+
+
+def backward_workspace(layer: SalrLayer, lt: SalrLayer, M_max: int, device="cuda"):
+    return workspace(backward_ws_bytes(layer.N, layer.K, lt.n_keep, layer.r_cat, M_max), device)
+
+
+def linear_backward(layer: SalrLayer, lt: SalrLayer, X, dY, dX=None, dA=None, dB=None, ws=None,
+                    need_dx: bool = True, stream=None, check: bool = False):
+    """dX = dY W_s + (dY B_cat^T) A_cat^T (bf16 [M][K], or None when
+    need_dx is False), dA = grad of a_cat as stored (float [r_cat][K]) and
+    dB = grad of b_cat as stored (float [N][r_cat]) on the GPU
+    (asynchronous on `stream`).  lt is transpose_layer(layer)."""
+    import torch
+
+    X = _as_bf16_bits(X, "X")
+    dY = _as_bf16_bits(dY, "dY")
+    M = X.shape[0]
+    if X.dim() != 2 or X.shape[1] != layer.K or tuple(dY.shape) != (M, layer.N):
+        raise ValueError("X must be [M][K] and dY [M][N]")
+    dev = X.device
+    if need_dx and dX is None:
+        dX = torch.empty((M, layer.K), dtype=torch.bfloat16, device=dev)
+    r = layer.r_cat
+    if dA is None:
+        dA = torch.empty((r, layer.K), dtype=torch.float32, device=dev)
+    if dB is None:
+        dB = torch.empty((layer.N, r), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = backward_workspace(layer, lt, M, dev)
+    desc = layer.descriptor()
+    tdesc = lt.descriptor()
+    tdesc.a_cat = tdesc.b_cat = None
+    ptr = lambda t, n: C.c_void_p(_dev_ptr(t, n)) if (t is not None and t.numel()) else None
+    st = _lib().salr_linear_backward(C.byref(desc), C.byref(tdesc), ptr(X, "X"), ptr(dY, "dY"), M,
+                                     ptr(dX, "dX") if need_dx else None, ptr(dA, "dA"), ptr(dB, "dB"),
+                                     C.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), _stream_ptr(stream))
+    _check(st, "salr_linear_backward")
+    if check and wait_error(ws, stream):
+        raise WaitTimeout("salr_linear_backward: a bounded wait timed out (workspace error word set)")
+    return (dX if need_dx else None), dA, dB
 
 
 def probe_stream_read(src, sink, workgroups: int, stream=None):

@@ -1,0 +1,238 @@
+// Backward pass of the SALR layer for fine-tuning the adapters with the base
+// weight frozen (gist.science summary of "Sparsity-Aware Low-Rank
+// Representation ...", Methodology 2: the SVD residual adapter is trained
+// together with the LoRA adapters; Methodology 1: the mask applies to the
+// frozen base weight only).  For Y = X W_s^T + (X A_cat) B_cat and dY:
+//   dX = dY W_s + (dY B_cat^T) A_cat^T,  dA_cat = X^T (dY B_cat^T),
+//   dB_cat = (X A_cat)^T dY.
+// dX is a forward of the transposed layer (W_s^T with adapters B_cat^T,
+// A_cat^T), run by the forward kernels on a column-major copy of W_s's
+// encoding built here once; the adapter gradients contract over the tokens.
+//
+// Transposed encoding (W_s^T, K rows of N columns), built tile-parallel:
+//   1. rowpre[n][w]: kept values of row n before bitmap word w;
+//   2. per 64-row block b and word w, one wave transposes the 64 x 64 bit
+//      tile with 64 ballots (ballot k collects bit k of the 64 rows' words,
+//      i.e. column k's word for the block) and counts each column's bits;
+//   3. colpre[b][k]: kept rows of column k before block b (a scan over b),
+//      the column counts, their maximum and the lookup table of W_s^T;
+//   4. the same waves scatter the values: column k's kept rows in block b
+//      land at colpre[b][k] onward, in row order.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "salr_device.hpp"
+#include "salr_kernels.hpp"
+
+namespace salr {
+namespace {
+
+// 1. one thread per row: exclusive running counts of the row's words
+__global__ __launch_bounds__(256) void row_prefix_kernel(const uint64_t* masks, int64_t N, int32_t kw,
+                                                         uint32_t* rowpre) {
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  uint32_t run = 0;
+  for (int w = 0; w < kw; ++w) {
+    rowpre[n * kw + w] = run;
+    run += (uint32_t)__popcll(masks[n * kw + w]);
+  }
+}
+
+// 2. wave per (block b, word w): column counts of the tile (and, with
+// masks_t, the transposed bitmap words)
+__device__ __forceinline__ uint64_t tile_column_word(uint64_t rw, int lane) {
+  uint64_t mine = 0;
+#pragma unroll 8
+  for (int k = 0; k < 64; ++k) {
+    const uint64_t b = __ballot((rw >> k) & 1ull);
+    if (lane == k) mine = b;
+  }
+  return mine;
+}
+
+__global__ __launch_bounds__(256) void tile_counts_kernel(const uint64_t* masks, int64_t N, int32_t K, int32_t kw,
+                                                          int32_t nb, uint32_t* cnt) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // tile id = b * kw + w
+  if (t >= (int64_t)nb * kw) return;
+  const int b = (int)(t / kw), w = (int)(t % kw);
+  const int64_t n = (int64_t)b * 64 + lane;
+  const uint64_t rw = n < N ? masks[n * kw + w] : 0ull;
+  const uint64_t mine = tile_column_word(rw, lane);
+  const int k = w * 64 + lane;
+  if (k < K) cnt[(size_t)b * K + k] = (uint32_t)__popcll(mine);
+}
+
+// 3. thread per column: exclusive scan of the block counts (in place), the
+// column's total, the lookup table of W_s^T and the largest count
+__global__ __launch_bounds__(256) void column_scan_kernel(uint32_t* cnt, int32_t nb, int32_t K, uint32_t* offsets_t,
+                                                          int32_t ng_t, uint32_t* maxcount) {
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  if (k >= K) return;
+  uint32_t run = 0;
+  for (int b = 0; b < nb; ++b) {
+    // (entry g of the table: kept rows before row 1024 g = 16 blocks of 64)
+    if (offsets_t && (b & 15) == 0) offsets_t[(size_t)k * ng_t + (b >> 4)] = run;
+    const uint32_t c = cnt[(size_t)b * K + k];
+    cnt[(size_t)b * K + k] = run;
+    run += c;
+  }
+  atomicMax(maxcount, run);
+}
+
+// 4. wave per (block b, word w): transposed bitmap word and value scatter
+__global__ __launch_bounds__(256) void transpose_scatter_kernel(const uint64_t* masks, const uint16_t* values,
+                                                                const uint32_t* rowpre, const uint32_t* colpre,
+                                                                int64_t N, int32_t K, int32_t kw, int32_t n_keep,
+                                                                int32_t nb, int32_t kw_t, int32_t n_keep_t,
+                                                                uint64_t* masks_t, uint16_t* values_t) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= (int64_t)nb * kw) return;
+  const int b = (int)(t / kw), w = (int)(t % kw);
+  const int64_t n = (int64_t)b * 64 + lane;
+  const uint64_t rw = n < N ? masks[n * kw + w] : 0ull;
+  const uint32_t rp = n < N ? rowpre[n * kw + w] : 0u;
+  const uint64_t mine = tile_column_word(rw, lane);  // column (w, lane)'s bits over the block's rows
+  const int k = w * 64 + lane;
+  const bool live = k < K;
+  if (live) masks_t[(size_t)k * kw_t + b] = mine;
+  uint32_t pos = live ? colpre[(size_t)b * K + k] : 0u;
+  const uint64_t below = (1ull << lane) - 1ull;
+  // rows of the block in order (all lanes active: row j's word and running
+  // count are read from lane j); a lane whose column row j keeps copies that
+  // value to the next slot of its column
+  for (int j = 0; j < 64; ++j) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)rw, j);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(rw >> 32), j);
+    const uint64_t wj = ((uint64_t)hi << 32) | lo;
+    if (wj == 0ull) continue;
+    const uint32_t rpj = (uint32_t)__builtin_amdgcn_readlane((int)rp, j);
+    if (live && ((wj >> lane) & 1ull)) {
+      values_t[(size_t)k * n_keep_t + pos] = values[((int64_t)b * 64 + j) * n_keep + rpj + __popcll(wj & below)];
+      ++pos;
+    }
+  }
+}
+
+// bf16 [R][C] -> [C][ld_dst] transpose through LDS, 64 x 64 tiles; the
+// destination row stride is ld_dst (>= R; the columns past R are zero).
+__global__ __launch_bounds__(256) void transpose_bf16_tiles(const uint16_t* src, int64_t R, int64_t C, int64_t ld_src,
+                                                            uint16_t* dst, int64_t ld_dst) {
+  __shared__ uint16_t tile[64][65];
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int y = ty; y < 64; y += 4) {
+    const int64_t r = r0 + y, c = c0 + tx;
+    tile[y][tx] = (r < R && c < C) ? src[r * ld_src + c] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int y = ty; y < 64; y += 4) {
+    const int64_t c = c0 + y, r = r0 + tx;
+    if (c < C && r < ld_dst) dst[c * ld_dst + r] = tile[tx][y];
+  }
+}
+
+// C[p][q] += sum over k in split s of A[p][k] B[q][k] (bf16, k contiguous,
+// row strides lda / ldb, k range padded with zeros to a multiple of 8),
+// fp32 partials part[s][P][Q].  Workgroup: 64 x 64 outputs, 4 waves of
+// 32 x 32 (2 x 2 MFMA tiles), operands loaded straight into MFMA layout.
+__global__ __launch_bounds__(256) void gemm_nt_kernel(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                                                      int64_t P, int64_t Q, int64_t Kc, int64_t k_split,
+                                                      float* part) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int64_t p0 = (int64_t)blockIdx.y * 64 + (wave >> 1) * 32;
+  const int64_t q0 = (int64_t)blockIdx.x * 64 + (wave & 1) * 32;
+  const int64_t kb = (int64_t)blockIdx.z * k_split, ke = min(Kc, kb + k_split);
+  f32x4_t acc[2][2] = {{zero4(), zero4()}, {zero4(), zero4()}};
+  for (int64_t k = kb; k < ke; k += 32) {
+    const int64_t kk = k + 8 * g;
+    u32x4_t a[2], b[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int64_t p = p0 + 16 * t + i, q = q0 + 16 * t + i;
+      a[t] = (p < P && kk < ke) ? load16(A + p * lda + kk) : zero_u4();
+      b[t] = (q < Q && kk < ke) ? load16(B + q * ldb + kk) : zero_u4();
+    }
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y) acc[x][y] = mfma_16x16x32(a[x], b[y], acc[x][y]);
+  }
+  // lane holds C[p0 + 16x + 4g + e][q0 + 16y + i]
+  float* out = part + (size_t)blockIdx.z * P * Q;
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t p = p0 + 16 * x + 4 * g + e, q = q0 + 16 * y + i;
+        const float v = acc[x][y][e];
+        if (p < P && q < Q) out[p * Q + q] = v;
+      }
+}
+
+__global__ __launch_bounds__(256) void sum_parts_kernel(const float* part, int splits, int64_t n, float* out) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  float s = 0.f;
+  for (int sp = 0; sp < splits; ++sp) s += part[(size_t)sp * n + e];
+  out[e] = s;
+}
+
+}  // namespace
+
+hipError_t launch_transpose_count(const uint64_t* masks, int64_t N, int32_t K, uint32_t* rowpre, uint32_t* cnt,
+                                  uint32_t* maxcount, uint32_t* offsets_t, int32_t ng_t, hipStream_t s) {
+  const int32_t kw = (K + 63) / 64, nb = (int32_t)((N + 63) / 64);
+  hipLaunchKernelGGL(row_prefix_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, masks, N, kw, rowpre);
+  const int64_t tiles = (int64_t)nb * kw;
+  hipLaunchKernelGGL(tile_counts_kernel, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, s, masks, N, K, kw, nb,
+                     cnt);
+  hipLaunchKernelGGL(column_scan_kernel, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, s, cnt, nb, K, offsets_t,
+                     ng_t, maxcount);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_scatter(const uint64_t* masks, const uint16_t* values, const uint32_t* rowpre,
+                                    const uint32_t* colpre, int64_t N, int32_t K, int32_t n_keep, int32_t n_keep_t,
+                                    uint64_t* masks_t, uint16_t* values_t, hipStream_t s) {
+  const int32_t kw = (K + 63) / 64, nb = (int32_t)((N + 63) / 64);
+  const int64_t tiles = (int64_t)nb * kw;
+  hipLaunchKernelGGL(transpose_scatter_kernel, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, s, masks, values,
+                     rowpre, colpre, N, K, kw, n_keep, nb, nb, n_keep_t, masks_t, values_t);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_bf16(const uint16_t* src, int64_t R, int64_t C, int64_t ld_src, uint16_t* dst,
+                                 int64_t ld_dst, hipStream_t s) {
+  if (R == 0 || C == 0) return hipSuccess;
+  const dim3 grid((unsigned)((C + 63) / 64), (unsigned)((std::max<int64_t>(R, ld_dst) + 63) / 64));
+  hipLaunchKernelGGL(transpose_bf16_tiles, grid, dim3(256), 0, s, src, R, C, ld_src, dst, ld_dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t P, int64_t Q,
+                          int64_t Kc, int splits, float* part, float* out, hipStream_t s) {
+  if (P == 0 || Q == 0) return hipSuccess;
+  const int64_t n = P * Q;
+  if (Kc <= 0) {  // (an empty sum: zeros)
+    hipLaunchKernelGGL(sum_parts_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, 0, n, out);
+    return hipGetLastError();
+  }
+  const int64_t k_split = ((Kc + splits - 1) / splits + 31) / 32 * 32;
+  splits = (int)((Kc + k_split - 1) / k_split);
+  if (splits < 1) splits = 1;
+  const dim3 grid((unsigned)((Q + 63) / 64), (unsigned)((P + 63) / 64), (unsigned)splits);
+  // (one split: straight into the output)
+  hipLaunchKernelGGL(gemm_nt_kernel, grid, dim3(256), 0, s, A, lda, B, ldb, P, Q, Kc, k_split, splits == 1 ? out : part);
+  if (splits > 1)
+    hipLaunchKernelGGL(sum_parts_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, splits, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace salr

@@ -404,6 +404,241 @@ int salr_linear_forward(const salr_layer_t* L, const uint16_t* X, int64_t M, uin
 
 }  // extern "C"
 
+// ----------------------------------------------------------------------------
+// Backward: the transposed encoding of W_s and the gradient pass.
+namespace {
+
+// Workspace of the transposed-encoding build: rowpre [N][kw], the block
+// column counts [nb][K], then the largest column count.
+struct TrLayout {
+  size_t rowpre, cnt, maxc, total;
+};
+TrLayout tr_layout(int64_t N, int64_t K) {
+  TrLayout T{};
+  const int64_t kw = cdiv(K, 64), nb = cdiv(N, 64);
+  T.rowpre = 0;
+  T.cnt = align_up((size_t)N * kw * 4, 256);
+  T.maxc = align_up(T.cnt + (size_t)nb * K * 4, 256);
+  T.total = T.maxc + 256;
+  return T;
+}
+
+// Runs the count pass and returns (host) the largest column count.
+int transpose_count_run(const salr_layer_t* L, uint32_t* offsets_t, void* ws, size_t ws_bytes, hipStream_t s,
+                        uint32_t* maxc) {
+  const TrLayout T = tr_layout(L->N, L->K);
+  if (!ws || !aligned16(ws)) return SALR_ERR_WORKSPACE;
+  if (ws_bytes < T.total) return SALR_ERR_WORKSPACE;
+  uint32_t* dmax = at<uint32_t>(ws, T.maxc);
+  if (hipMemsetAsync(dmax, 0, 4, s) != hipSuccess) return SALR_ERR_HIP;
+  if (salr::launch_transpose_count(L->masks, L->N, (int32_t)L->K, at<uint32_t>(ws, T.rowpre), at<uint32_t>(ws, T.cnt),
+                                   dmax, offsets_t, (int32_t)cdiv(L->N, 1024), s) != hipSuccess)
+    return SALR_ERR_HIP;
+  if (hipMemcpyAsync(maxc, dmax, 4, hipMemcpyDeviceToHost, s) != hipSuccess) return SALR_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return SALR_ERR_HIP;
+  return SALR_OK;
+}
+
+// Checks shared by the transposed-encoding calls.
+int transpose_check(const salr_layer_t* L) {
+  if (!L || !dims_ok(L->N, L->K, L->n_keep, L->r_cat)) return SALR_ERR_INVALID_ARG;
+  if (!L->masks || !aligned16(L->masks)) return SALR_ERR_INVALID_ARG;
+  // W_s^T has N columns: the layer limits apply with N and K swapped
+  if (L->N % 8 != 0 || L->N > kMaxK || L->K > kMaxRowTiles * 16) return SALR_ERR_UNSUPPORTED;
+  return SALR_OK;
+}
+
+// Gradient-GEMM K splits over M tokens: about kGemmItems workgroups, each
+// split at least 256 tokens.
+constexpr int64_t kGemmItems = 512;
+int gemm_splits(int64_t P, int64_t Q, int64_t M) {
+  const int64_t tiles = cdiv(P, 64) * cdiv(Q, 64);
+  const int64_t s = std::min<int64_t>(std::max<int64_t>(1, kGemmItems / std::max<int64_t>(tiles, 1)), cdiv(M, 256));
+  return (int)std::max<int64_t>(s, 1);
+}
+
+// Backward workspace: the forward workspace of the transposed layer first
+// (its counter header at offset 0), then the transposed adapters, the
+// low-rank activations and their token-major transposes, and the gradient
+// GEMMs' split partials.  Every region grows with M.
+struct BwdLayout {
+  int r_pad;
+  int64_t m8;
+  int splits_a, splits_b;
+  size_t fwd, bt, at_, tpart, g16, t16, xt, dyt, gt, tt, part, total;
+};
+BwdLayout bwd_layout(int64_t N, int64_t K, int32_t n_keep_t, int32_t r_cat, int64_t M) {
+  BwdLayout B{};
+  B.r_pad = (int)align_up((size_t)r_cat, 16);
+  B.m8 = (int64_t)align_up((size_t)M, 8);
+  B.fwd = fwd_layout(K, N, n_keep_t, r_cat, M).total;
+  size_t off = align_up(B.fwd, 256);
+  B.bt = off;   off = align_up(off + (size_t)r_cat * N * 2, 256);
+  B.at_ = off;  off = align_up(off + (size_t)K * r_cat * 2, 256) + kValuesPad;
+  B.tpart = off;
+  B.g16 = B.t16 = B.xt = B.dyt = B.gt = B.tt = B.part = off;
+  if (r_cat > 0 && M > 0) {
+    const size_t rows = (size_t)std::max<int64_t>(64 * 256, cdiv(M, 64) * 64);
+    off = align_up(off + rows * B.r_pad * 4, 256);
+    B.g16 = off;  off = align_up(off + (size_t)M * B.r_pad * 2, 256);
+    B.t16 = off;  off = align_up(off + (size_t)M * B.r_pad * 2, 256);
+    B.xt = off;   off = align_up(off + (size_t)K * B.m8 * 2, 256);
+    B.dyt = off;  off = align_up(off + (size_t)N * B.m8 * 2, 256);
+    B.gt = off;   off = align_up(off + (size_t)r_cat * B.m8 * 2, 256);
+    B.tt = off;   off = align_up(off + (size_t)r_cat * B.m8 * 2, 256);
+    B.splits_a = gemm_splits(r_cat, K, M);
+    B.splits_b = gemm_splits(N, r_cat, M);
+    B.part = off;
+    off = align_up(off + std::max((size_t)B.splits_a * r_cat * K, (size_t)B.splits_b * N * r_cat) * 4, 256);
+  }
+  B.total = off;
+  return B;
+}
+
+}  // namespace
+
+extern "C" {
+
+int salr_transpose_ws_bytes(int64_t N, int64_t K, size_t* out) {
+  if (!out || !dims_ok(N, K, 0, 0)) return SALR_ERR_INVALID_ARG;
+  *out = tr_layout(N, K).total;
+  return SALR_OK;
+}
+
+int salr_transpose_count(const salr_layer_t* L, int32_t* n_keep_t, void* ws, size_t ws_bytes, void* stream) {
+  if (!n_keep_t) return SALR_ERR_INVALID_ARG;
+  const int rc = transpose_check(L);
+  if (rc != SALR_OK) return rc;
+  uint32_t maxc = 0;
+  const int e = transpose_count_run(L, nullptr, ws, ws_bytes, static_cast<hipStream_t>(stream), &maxc);
+  if (e != SALR_OK) return e;
+  *n_keep_t = (int32_t)maxc;
+  return SALR_OK;
+}
+
+int salr_transpose_layer(const salr_layer_t* L, salr_layer_t* LT, void* ws, size_t ws_bytes, void* stream) {
+  const int rc = transpose_check(L);
+  if (rc != SALR_OK) return rc;
+  if (!LT) return SALR_ERR_INVALID_ARG;
+  if (L->value_format != SALR_VALUES_BF16) return SALR_ERR_UNSUPPORTED;
+  if (L->n_keep > 0 && (!L->values || !aligned16(L->values))) return SALR_ERR_INVALID_ARG;
+  if (LT->N != L->K || LT->K != L->N || !dims_ok(LT->N, LT->K, LT->n_keep, L->r_cat)) return SALR_ERR_INVALID_ARG;
+  if (!LT->masks || !LT->offsets || (LT->n_keep > 0 && !LT->values)) return SALR_ERR_INVALID_ARG;
+  const void* ptrs[] = {LT->masks, LT->values, LT->offsets};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return SALR_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t maxc = 0;
+  int e = transpose_count_run(L, LT->offsets, ws, ws_bytes, s, &maxc);
+  if (e != SALR_OK) return e;
+  if ((int64_t)maxc > LT->n_keep) return SALR_ERR_INVALID_ARG;
+  const TrLayout T = tr_layout(L->N, L->K);
+  if (LT->n_keep > 0 && hipMemsetAsync(LT->values, 0, (size_t)LT->N * LT->n_keep * 2, s) != hipSuccess)
+    return SALR_ERR_HIP;
+  if (salr::launch_transpose_scatter(L->masks, L->values, at<uint32_t>(ws, T.rowpre), at<uint32_t>(ws, T.cnt), L->N,
+                                     (int32_t)L->K, L->n_keep, LT->n_keep, LT->masks, LT->values, s) != hipSuccess)
+    return SALR_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return SALR_ERR_HIP;
+  LT->r_cat = L->r_cat;
+  LT->n_parts = 0;
+  for (int q = 0; q < SALR_MAX_PARTS; ++q) LT->part_rows[q] = LT->part_ranks[q] = 0;
+  LT->value_format = SALR_VALUES_BF16;
+  LT->codes = nullptr;
+  LT->scales = nullptr;
+  return SALR_OK;
+}
+
+int salr_backward_ws_bytes(int64_t N, int64_t K, int32_t n_keep_t, int32_t r_cat, int64_t M_max, size_t* out) {
+  if (!out || !dims_ok(N, K, 0, r_cat) || M_max < 0) return SALR_ERR_INVALID_ARG;
+  if (N % 8 != 0 || N > kMaxK || K > kMaxRowTiles * 16) return SALR_ERR_UNSUPPORTED;
+  if (!dims_ok(K, N, n_keep_t, r_cat)) return SALR_ERR_INVALID_ARG;
+  *out = bwd_layout(N, K, n_keep_t, r_cat, M_max).total;
+  return SALR_OK;
+}
+
+int salr_linear_backward(const salr_layer_t* L, const salr_layer_t* LT, const uint16_t* X, const uint16_t* dY,
+                         int64_t M, uint16_t* dX, float* dA, float* dB, void* ws, size_t ws_bytes, void* stream) {
+  if (!L || !LT) return SALR_ERR_INVALID_ARG;
+  if (!dims_ok(L->N, L->K, L->n_keep, L->r_cat)) return SALR_ERR_INVALID_ARG;
+  if (L->N % 8 != 0 || L->N > kMaxK || L->K > kMaxRowTiles * 16) return SALR_ERR_UNSUPPORTED;
+  if (LT->N != L->K || LT->K != L->N || LT->r_cat != L->r_cat || !dims_ok(LT->N, LT->K, LT->n_keep, LT->r_cat))
+    return SALR_ERR_INVALID_ARG;
+  if (LT->value_format != SALR_VALUES_BF16 || LT->n_parts != 0) return SALR_ERR_INVALID_ARG;
+  if (M < 0 || M > (int64_t(1) << 31) - 1) return SALR_ERR_INVALID_ARG;
+  const int32_t r = L->r_cat;
+  if (r > 0 && (!L->a_cat || !L->b_cat)) return SALR_ERR_INVALID_ARG;
+  if (M > 0 && (!X || !dY)) return SALR_ERR_INVALID_ARG;
+  if (dX && (!LT->masks || !LT->offsets || (LT->n_keep > 0 && !LT->values))) return SALR_ERR_INVALID_ARG;
+  if (r > 0 && (!dA || !dB)) return SALR_ERR_INVALID_ARG;
+  const void* ptrs[] = {X, dY, dX, dA, dB, L->a_cat, L->b_cat, LT->masks, LT->values, LT->offsets};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return SALR_ERR_INVALID_ARG;
+  if (dX && (static_cast<const void*>(dX) == static_cast<const void*>(dY))) return SALR_ERR_INVALID_ARG;
+  if (!ws || !aligned16(ws)) return SALR_ERR_WORKSPACE;
+  const BwdLayout B = bwd_layout(L->N, L->K, LT->n_keep, r, M);
+  if (ws_bytes < B.total) return SALR_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t N = L->N, K = L->K;
+  if (M == 0) {
+    // an empty token sum: zero adapter gradients (no dX rows)
+    if (r > 0 && (salr::launch_gemm_nt(nullptr, 0, nullptr, 0, r, K, 0, 1, nullptr, dA, s) != hipSuccess ||
+                  salr::launch_gemm_nt(nullptr, 0, nullptr, 0, N, r, 0, 1, nullptr, dB, s) != hipSuccess))
+      return SALR_ERR_HIP;
+    return SALR_OK;
+  }
+  uint16_t* bt = at<uint16_t>(ws, B.bt);   // B_cat [r][N]: the transposed layer's a_cat
+  uint16_t* att = at<uint16_t>(ws, B.at_); // A_cat [K][r]: the transposed layer's b_cat
+  if (r > 0) {
+    if (salr::launch_transpose_bf16(L->b_cat, N, r, r, bt, N, s) != hipSuccess) return SALR_ERR_HIP;
+    if (salr::launch_transpose_bf16(L->a_cat, r, K, K, att, r, s) != hipSuccess) return SALR_ERR_HIP;
+  }
+  if (dX) {
+    salr_layer_t lt = *LT;
+    lt.a_cat = r > 0 ? bt : nullptr;
+    lt.b_cat = r > 0 ? att : nullptr;
+    const int e = salr::forward_impl(&lt, dY, M, dX, ws, B.fwd, at<uint32_t>(ws, kCounterSync + 8), s);
+    if (e != SALR_OK) return e;
+  }
+  if (r == 0) return SALR_OK;
+  // G = dY B_cat^T and T = X A_cat, each rounded to bf16 [M][r_pad]
+  const auto lowrank = [&](const uint16_t* in, const uint16_t* rows, int64_t Kin, uint16_t* out16) {
+    LowRankTArgs t{};
+    t.X = in;
+    t.a_cat = rows;
+    t.tpart = at<float>(ws, B.tpart);
+    t.t16 = out16;
+    t.M = (int32_t)M;
+    t.K = (int32_t)Kin;
+    t.r_cat = r;
+    t.r_pad = B.r_pad;
+    t.splits = t_splits_large(M, Kin);
+    t.k_chunk = (int32_t)(cdiv(cdiv(Kin, 64), t.splits) * 64);
+    t.splits = (int32_t)cdiv(Kin, t.k_chunk);
+    return salr::launch_lowrank_t(t, s) == hipSuccess;
+  };
+  uint16_t* g16 = at<uint16_t>(ws, B.g16);
+  uint16_t* t16 = at<uint16_t>(ws, B.t16);
+  if (!lowrank(dY, bt, N, g16) || !lowrank(X, L->a_cat, K, t16)) return SALR_ERR_HIP;
+  // token-major operands of the two gradient GEMMs (rows zero-padded to m8)
+  uint16_t* xt = at<uint16_t>(ws, B.xt);
+  uint16_t* dyt = at<uint16_t>(ws, B.dyt);
+  uint16_t* gt = at<uint16_t>(ws, B.gt);
+  uint16_t* tt = at<uint16_t>(ws, B.tt);
+  if (salr::launch_transpose_bf16(X, M, K, K, xt, B.m8, s) != hipSuccess ||
+      salr::launch_transpose_bf16(dY, M, N, N, dyt, B.m8, s) != hipSuccess ||
+      salr::launch_transpose_bf16(g16, M, r, B.r_pad, gt, B.m8, s) != hipSuccess ||
+      salr::launch_transpose_bf16(t16, M, r, B.r_pad, tt, B.m8, s) != hipSuccess)
+    return SALR_ERR_HIP;
+  float* part = at<float>(ws, B.part);
+  // dA_cat (stored [r][K]) [j][k] = sum_m G[m][j] X[m][k]
+  if (salr::launch_gemm_nt(gt, B.m8, xt, B.m8, r, K, M, B.splits_a, part, dA, s) != hipSuccess) return SALR_ERR_HIP;
+  // dB_cat (stored [N][r]) [n][j] = sum_m dY[m][n] T[m][j]
+  if (salr::launch_gemm_nt(dyt, B.m8, tt, B.m8, N, r, M, B.splits_b, part, dB, s) != hipSuccess) return SALR_ERR_HIP;
+  return SALR_OK;
+}
+
+}  // extern "C"
+
 // The forward behind both entry points: `ws` is the workspace (caller's, or
 // the library's fixed array), `err` the word a timed-out wait sets.
 int salr::forward_impl(const salr_layer_t* L, const uint16_t* X, int64_t M, uint16_t* Y, void* ws, size_t ws_bytes,

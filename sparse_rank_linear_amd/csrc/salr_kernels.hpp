@@ -185,6 +185,26 @@ hipError_t launch_dequantize_nf4(const uint8_t* codes, const uint16_t* scales, i
                                  uint16_t* values, hipStream_t s);
 
 // ----------------------------------------------------------------------------
+// Backward: the transposed encoding of W_s and the adapter-gradient GEMMs.
+// Transposed encoding: rowpre [N][kw] (kept before each word), cnt [nb][K]
+// (per 64-row block column counts, scanned in place to the kept rows before
+// each block), maxcount (one word, zeroed by the caller), offsets_t
+// [K][ceil(N/1024)] (or null).
+hipError_t launch_transpose_count(const uint64_t* masks, int64_t N, int32_t K, uint32_t* rowpre, uint32_t* cnt,
+                                  uint32_t* maxcount, uint32_t* offsets_t, int32_t ng_t, hipStream_t s);
+hipError_t launch_transpose_scatter(const uint64_t* masks, const uint16_t* values, const uint32_t* rowpre,
+                                    const uint32_t* colpre, int64_t N, int32_t K, int32_t n_keep, int32_t n_keep_t,
+                                    uint64_t* masks_t, uint16_t* values_t, hipStream_t s);
+// dst[c][r] = src[r][c] (bf16), dst rows of ld_dst >= R entries, zero past R.
+hipError_t launch_transpose_bf16(const uint16_t* src, int64_t R, int64_t C, int64_t ld_src, uint16_t* dst,
+                                 int64_t ld_dst, hipStream_t s);
+// out[p][q] = sum_k A[p][k] B[q][k] (bf16 rows, k contiguous, zero-padded to
+// a multiple of 8), fp32, the k range cut into `splits` partials (part:
+// splits * P * Q floats) summed in order.
+hipError_t launch_gemm_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t P, int64_t Q,
+                          int64_t Kc, int splits, float* part, float* out, hipStream_t s);
+
+// ----------------------------------------------------------------------------
 // Encode kernels.
 // ----------------------------------------------------------------------------
 struct PrunePackArgs {

@@ -265,3 +265,84 @@ def test_python_wrapper_requires_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         B.query_sizes(4, 64, 8, 0, 0, 1)
+
+
+def _bwd(L, LT, X=0x20000000, dY=0x21000000, M=4, dX=0x30000000, dA=0x31000000, dB=0x32000000, ws=0x40000000,
+         ws_bytes=1 << 30):
+    vp = lambda a: C.c_void_p(a) if a else None
+    return srl.lib().salr_linear_backward(C.byref(L) if L is not None else None,
+                                          C.byref(LT) if LT is not None else None, vp(X), vp(dY), M, vp(dX), vp(dA),
+                                          vp(dB), vp(ws), ws_bytes, None)
+
+
+def test_backward_sizes():
+    # the transposed-encoding build: row counts, block column counts, max word
+    assert srl.transpose_ws_bytes(4096, 4096) >= 4096 * 64 * 4 + 64 * 4096 * 4
+    with pytest.raises(srl.SalrError):
+        srl.transpose_ws_bytes(4, 60)
+    # the backward workspace grows with M and holds the transposed forward's
+    a = srl.backward_ws_bytes(4096, 4096, 2100, 80, 16)
+    b = srl.backward_ws_bytes(4096, 4096, 2100, 80, 2048)
+    assert b > a >= srl.query_sizes(4096, 4096, 2100, 0, 80, 16)["forward_ws_bytes"]
+    # operands of the gradient GEMMs at 2048 tokens: X^T, dY^T, G^T, T^T
+    assert b >= 2 * 2048 * (4096 + 4096 + 2 * 80)
+    with pytest.raises(srl.SalrError):
+        srl.backward_ws_bytes(4100, 4096, 2048, 80, 16)    # N % 8: W_s^T's column count
+    with pytest.raises(srl.SalrError):
+        srl.backward_ws_bytes(4096, 4096, 4097, 80, 16)    # n_keep_t > N
+
+
+def test_transpose_validation_paths():
+    # These return before any HIP call, so they run without a GPU.
+    lib = srl.lib()
+    n = C.c_int32()
+    L = _layer(N=64, K=128, n_keep=32)
+    assert lib.salr_transpose_count(None, C.byref(n), C.c_void_p(0x40000000), 1 << 30, None) == -1
+    assert lib.salr_transpose_count(C.byref(L), None, C.c_void_p(0x40000000), 1 << 30, None) == -1
+    assert lib.salr_transpose_count(C.byref(_layer(N=60, K=128)), C.byref(n), C.c_void_p(0x40000000), 1 << 30,
+                                    None) == -2                    # N % 8
+    assert lib.salr_transpose_count(C.byref(L), C.byref(n), None, 1 << 30, None) == -3
+    assert lib.salr_transpose_count(C.byref(L), C.byref(n), C.c_void_p(0x40000000), 64, None) == -3
+    LT = _layer(N=128, K=64, n_keep=40, base=0x11000000)
+    ws = C.c_void_p(0x40000000)
+    assert lib.salr_transpose_layer(C.byref(L), None, ws, 1 << 30, None) == -1
+    bad = _layer(N=120, K=64, n_keep=40, base=0x11000000)
+    assert lib.salr_transpose_layer(C.byref(L), C.byref(bad), ws, 1 << 30, None) == -1   # LT.N != K
+    bad = _layer(N=128, K=64, n_keep=65, base=0x11000000)
+    assert lib.salr_transpose_layer(C.byref(L), C.byref(bad), ws, 1 << 30, None) == -1   # n_keep > N
+    bad = _layer(N=128, K=64, n_keep=40, base=0x11000000)
+    bad.values = 0x11100008
+    assert lib.salr_transpose_layer(C.byref(L), C.byref(bad), ws, 1 << 30, None) == -1   # misaligned
+    q = _layer(N=64, K=128, n_keep=32)
+    q.value_format = B.VALUES_NF4
+    assert lib.salr_transpose_layer(C.byref(q), C.byref(LT), ws, 1 << 30, None) == -2    # NF4 layer
+    assert lib.salr_transpose_layer(C.byref(L), C.byref(LT), ws, 64, None) == -3
+
+
+def test_backward_validation_paths():
+    L = _layer(N=64, K=128, n_keep=32, r_cat=16)
+    LT = _layer(N=128, K=64, n_keep=40, r_cat=16, base=0x11000000)
+    assert _bwd(None, LT) == -1
+    assert _bwd(L, None) == -1
+    assert _bwd(L, _layer(N=120, K=64, n_keep=40, r_cat=16, base=0x11000000)) == -1   # LT.N != K
+    assert _bwd(L, _layer(N=128, K=64, n_keep=40, r_cat=8, base=0x11000000)) == -1    # ranks differ
+    assert _bwd(_layer(N=60, K=128, n_keep=32, r_cat=16),
+                _layer(N=128, K=60, n_keep=30, r_cat=16, base=0x11000000)) == -2       # N % 8
+    t = _layer(N=128, K=64, n_keep=40, r_cat=16, base=0x11000000)
+    t.n_parts = 1
+    assert _bwd(L, t) == -1                                     # a transposed layer has no parts
+    t = _layer(N=128, K=64, n_keep=40, r_cat=16, base=0x11000000)
+    t.value_format = B.VALUES_NF4
+    assert _bwd(L, t) == -1                                     # nor NF4 values
+    assert _bwd(L, LT, M=-1) == -1
+    assert _bwd(L, LT, X=0) == -1
+    assert _bwd(L, LT, dY=0) == -1
+    assert _bwd(L, LT, dA=0) == -1                              # adapters need both gradients
+    assert _bwd(L, LT, dB=0) == -1
+    assert _bwd(L, LT, dY=0x21000008) == -1                     # misaligned
+    assert _bwd(L, LT, dX=0x21000000) == -1                     # dX aliases dY
+    d = _layer(N=64, K=128, n_keep=32, r_cat=16)
+    d.b_cat = None
+    assert _bwd(d, LT) == -1
+    assert _bwd(L, LT, ws=0) == -3
+    assert _bwd(L, LT, ws_bytes=4096) == -3
