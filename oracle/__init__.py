@@ -21,8 +21,21 @@ Parity status of each function (what pins it, see tests/test_oracle_*.py):
                                    ranks), nothing pruned, a planted
                                    undiscounted tail
   salr.forward                     pinned: per-set-bit triple loop, X = I
+  salr.fuse                        pinned: fused forward = the parts', a
+                                   planted misplaced block
+  nf4.nf4_levels / quantize / dequantize / pack_codes
+                                   pinned: normal-CDF spacing of the levels,
+                                   brute-force nearest level, exact round
+                                   trips, the per-block error bound, planted
+                                   mistakes
+  backward.backward                pinned: exact finite differences of the
+                                   forward, a planted missing term
+  backward.transpose_encoding      pinned: the dense transpose, bit for bit
+  moe.grouped_forward              pinned: per-token brute force from the
+                                   original weights, planted boundary shift
+                                   and expert swap
   The pages print no worked example and no intermediate values, so no
   function is pinned to a number printed on the pages.
 """
 
-from . import bf16, salr  # noqa: F401
+from . import backward, bf16, moe, nf4, salr  # noqa: F401
