@@ -385,6 +385,76 @@ int salr_linear_backward(const salr_layer_t* L, const salr_layer_t* LT,
                          uint16_t* dX, float* dA, float* dB, void* ws,
                          size_t ws_bytes, void* stream);
 
+/*
+ * Grouped (mixture-of-experts) layer: E experts of one shape, each its own
+ * encoded layer (summary, Experimental Results: SALR applied to the MoE
+ * models Mixtral-8x7B and DeepSeek-V2-Lite), held in five stacked buffers,
+ * expert e's arrays at fixed element strides (each a multiple of 256 bytes,
+ * reported by salr_moe_query_sizes):
+ *   masks   uint64 [E][masks_stride]    expert e: its [N][ceil(K/64)]
+ *   values  bf16   [E][values_stride]   expert e: its [N][n_keep]
+ *   offsets uint32 [E][offsets_stride]  expert e: its [N][ceil(K/1024)]
+ *   a_cat   bf16   [E][a_cat_stride]    expert e: its [r_cat][K]
+ *   b_cat   bf16   [E][b_cat_stride]    expert e: its [N][r_cat]
+ * (values and b_cat with tail padding: use the *_bytes sizes).  All experts
+ * share N, K, n_keep and r_cat (a smaller LoRA rank pads with zero ranks).
+ */
+typedef struct salr_moe_layer {
+  int32_t E;
+  int64_t N;
+  int64_t K;
+  int32_t n_keep;
+  int32_t r_cat;
+  uint64_t* masks;
+  uint16_t* values;
+  uint32_t* offsets;
+  uint16_t* a_cat;
+  uint16_t* b_cat;
+} salr_moe_layer_t;
+
+typedef struct salr_moe_sizes {
+  size_t masks_bytes, values_bytes, offsets_bytes, a_cat_bytes, b_cat_bytes;
+  size_t masks_stride, values_stride, offsets_stride, a_cat_stride, b_cat_stride;  /* elements */
+  size_t forward_ws_bytes;  /* salr_moe_forward workspace for T_max rows    */
+} salr_moe_sizes_t;
+
+/* Sizes and strides of an E-expert layer (1 <= E <= 4096; the layer limits
+ * above per expert), forward workspace for at most T_max rows (`out` host).
+ * Pure host arithmetic.  Errors: INVALID_ARG. */
+int salr_moe_query_sizes(int32_t E, int64_t N, int64_t K, int32_t n_keep,
+                         int32_t r_cat, int64_t T_max, salr_moe_sizes_t* out);
+
+/* The layer descriptor of expert e (views into the stacked buffers; n_parts
+ * 0, bf16 values): pass it to salr_encode to encode that expert in place,
+ * or to salr_linear_forward to run it alone.  `out` host; host arithmetic.
+ * Errors: INVALID_ARG. */
+int salr_moe_expert(const salr_moe_layer_t* G, int32_t e, salr_layer_t* out);
+
+/*
+ * salr_moe_forward - for every expert e:
+ *   Y[off[e]:off[e+1]] = X[off[e]:off[e+1]] W_s,e^T
+ *                        + (X[off[e]:off[e+1]] A_cat,e) B_cat,e
+ * in one grouped pair of launches.
+ *
+ * G    host pointer to the grouped layer.
+ * X    device bf16 [T][K], rows grouped by expert; Y device bf16 [T][N]
+ *      (may not alias X).
+ * expert_offsets  DEVICE int32 [E + 1], read by the kernels (routing needs
+ *      no host round trip): off[0] = 0, nondecreasing, off[E] = T.  The
+ *      kernels clamp each boundary into [0, T] and never leave X or Y, but
+ *      rows outside every valid group are then not written.
+ * m_cap  the expected most rows of one expert (0: T); it only sizes the
+ *      low-rank grid: any distribution is computed correctly.
+ * ws   device workspace, forward_ws_bytes for some T_max >= T (contents on
+ *      entry do not matter; no zero fill needed).
+ * Numerics as salr_linear_forward (fp32 accumulation, X A_cat rounded to
+ * bf16, Y rounded to bf16).  An expert with no rows reads none of its
+ * weight.  Asynchronous on `stream`.  Errors: INVALID_ARG, WORKSPACE, HIP.
+ */
+int salr_moe_forward(const salr_moe_layer_t* G, const uint16_t* X, int64_t T,
+                     const int32_t* expert_offsets, int64_t m_cap, uint16_t* Y,
+                     void* ws, size_t ws_bytes, void* stream);
+
 /* Static English text for a status code (never NULL). */
 const char* salr_status_string(int status);
 

@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     NOALLOC_SCRATCH_BYTES,
     SalrError,
     SalrLayer,
+    SalrMoE,
     WaitTimeout,
     backward_workspace,
     backward_ws_bytes,
@@ -25,6 +26,9 @@ from .binding import (  # noqa: F401
     linear_backward,
     linear_forward,
     linear_forward_noalloc,
+    moe_forward,
+    moe_query_sizes,
+    moe_workspace,
     nf4_levels,
     probe_mfma,
     probe_stream_read,
@@ -38,8 +42,8 @@ from .binding import (  # noqa: F401
 )
 
 __all__ = [
-    "EXPORTS", "LIB_PATH", "NOALLOC_SCRATCH_BYTES", "SalrError", "SalrLayer", "WaitTimeout", "backward_workspace",
+    "EXPORTS", "LIB_PATH", "NOALLOC_SCRATCH_BYTES", "SalrError", "SalrLayer", "SalrMoE", "WaitTimeout", "backward_workspace",
     "backward_ws_bytes", "encode", "forward_workspace", "fuse", "lib", "linear_backward", "linear_forward",
-    "linear_forward_noalloc", "nf4_levels", "probe_mfma", "probe_stream_read", "quantize_nf4", "query_sizes",
+    "linear_forward_noalloc", "moe_forward", "moe_query_sizes", "moe_workspace", "nf4_levels", "probe_mfma", "probe_stream_read", "quantize_nf4", "query_sizes",
     "transpose_count", "transpose_layer", "transpose_ws_bytes", "wait_error", "workspace",
 ]

@@ -41,6 +41,9 @@ EXPORTS = (
     "salr_transpose_layer",
     "salr_backward_ws_bytes",
     "salr_linear_backward",
+    "salr_moe_query_sizes",
+    "salr_moe_expert",
+    "salr_moe_forward",
     # include/salr_probe.h
     "salr_probe_stream_read",
     "salr_probe_mfma",
@@ -90,6 +93,28 @@ class salr_sizes_t(C.Structure):
         ("scales_bytes", C.c_size_t),
         ("forward_ws_nf4_bytes", C.c_size_t),
     ]
+
+
+class salr_moe_layer_t(C.Structure):
+    _fields_ = [
+        ("E", C.c_int32),
+        ("N", C.c_int64),
+        ("K", C.c_int64),
+        ("n_keep", C.c_int32),
+        ("r_cat", C.c_int32),
+        ("masks", C.c_void_p),
+        ("values", C.c_void_p),
+        ("offsets", C.c_void_p),
+        ("a_cat", C.c_void_p),
+        ("b_cat", C.c_void_p),
+    ]
+
+
+class salr_moe_sizes_t(C.Structure):
+    _fields_ = [(n, C.c_size_t) for n in (
+        "masks_bytes", "values_bytes", "offsets_bytes", "a_cat_bytes", "b_cat_bytes",
+        "masks_stride", "values_stride", "offsets_stride", "a_cat_stride", "b_cat_stride",
+        "forward_ws_bytes")]
 
 
 class salr_encode_opts_t(C.Structure):
@@ -145,6 +170,14 @@ def _lib():
                                              C.c_void_p, C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p,
                                              C.c_void_p, C.c_size_t, C.c_void_p]
         lib.salr_linear_backward.restype = C.c_int
+        lib.salr_moe_query_sizes.argtypes = [C.c_int32, C.c_int64, C.c_int64, C.c_int32, C.c_int32, C.c_int64,
+                                             C.POINTER(salr_moe_sizes_t)]
+        lib.salr_moe_query_sizes.restype = C.c_int
+        lib.salr_moe_expert.argtypes = [C.POINTER(salr_moe_layer_t), C.c_int32, C.POINTER(salr_layer_t)]
+        lib.salr_moe_expert.restype = C.c_int
+        lib.salr_moe_forward.argtypes = [C.POINTER(salr_moe_layer_t), C.c_void_p, C.c_int64, C.c_void_p,
+                                         C.c_int64, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+        lib.salr_moe_forward.restype = C.c_int
         lib.salr_probe_stream_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int32, C.c_void_p]
         lib.salr_probe_stream_read.restype = C.c_int
         lib.salr_probe_mfma.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p]
@@ -547,6 +580,102 @@ def linear_backward(layer: SalrLayer, lt: SalrLayer, X, dY, dX=None, dA=None, dB
     if check and wait_error(ws, stream):
         raise WaitTimeout("salr_linear_backward: a bounded wait timed out (workspace error word set)")
     return (dX if need_dx else None), dA, dB
+
+
+def moe_query_sizes(E: int, N: int, K: int, n_keep: int, r_cat: int, T_max: int) -> dict:
+    out = salr_moe_sizes_t()
+    _check(_lib().salr_moe_query_sizes(E, N, K, n_keep, r_cat, T_max, C.byref(out)), "salr_moe_query_sizes")
+    return {f: getattr(out, f) for f, _ in salr_moe_sizes_t._fields_}
+
+
+@dataclass
+class SalrMoE:
+    """E experts of one shape, each its own encoding, in five stacked device
+    buffers at the library's per-expert strides (include/salr.h,
+    salr_moe_layer_t)."""
+
+    E: int
+    N: int
+    K: int
+    n_keep: int
+    r_cat: int
+    masks: object
+    values: object
+    offsets: object
+    a_cat: object
+    b_cat: object
+
+    @classmethod
+    def empty(cls, E, N, K, n_keep, r_cat, device="cuda"):
+        import torch
+
+        sz = moe_query_sizes(E, N, K, n_keep, r_cat, 0)
+        z = lambda nbytes: torch.zeros(max(int(nbytes), 256) // 2, dtype=torch.int16, device=device)
+        return cls(E, N, K, n_keep, r_cat, masks=z(sz["masks_bytes"]), values=z(sz["values_bytes"]),
+                   offsets=z(sz["offsets_bytes"]), a_cat=z(sz["a_cat_bytes"]), b_cat=z(sz["b_cat_bytes"]))
+
+    def descriptor(self) -> salr_moe_layer_t:
+        d = salr_moe_layer_t()
+        d.E, d.N, d.K, d.n_keep, d.r_cat = self.E, self.N, self.K, self.n_keep, self.r_cat
+        d.masks, d.values, d.offsets = self.masks.data_ptr(), self.values.data_ptr(), self.offsets.data_ptr()
+        d.a_cat = self.a_cat.data_ptr() if self.r_cat else None
+        d.b_cat = self.b_cat.data_ptr() if self.r_cat else None
+        return d
+
+    def expert(self, e: int) -> salr_layer_t:
+        """Expert e's layer descriptor (views into the stacked buffers)."""
+        out = salr_layer_t()
+        d = self.descriptor()
+        _check(_lib().salr_moe_expert(C.byref(d), e, C.byref(out)), "salr_moe_expert")
+        return out
+
+    def set_expert(self, e: int, masks, values, offsets, a_cat, b_cat):
+        """Upload expert e's encoding from numpy arrays in the stored layout
+        (uint64 masks, uint16 values [N][n_keep], uint32 offsets, uint16 a_cat
+        [r_cat][K], b_cat [N][r_cat])."""
+        import numpy as np
+
+        sz = moe_query_sizes(self.E, self.N, self.K, self.n_keep, self.r_cat, 0)
+        for buf, arr, stride, esize in ((self.masks, masks, sz["masks_stride"], 8),
+                                        (self.values, values, sz["values_stride"], 2),
+                                        (self.offsets, offsets, sz["offsets_stride"], 4),
+                                        (self.a_cat, a_cat, sz["a_cat_stride"], 2),
+                                        (self.b_cat, b_cat, sz["b_cat_stride"], 2)):
+            flat = np.ascontiguousarray(arr).reshape(-1).view(np.int16)
+            if flat.size == 0:
+                continue
+            start = e * stride * esize // 2
+            import torch
+            buf[start:start + flat.size].copy_(torch.from_numpy(flat))
+
+
+def moe_workspace(moe: SalrMoE, T_max: int, device="cuda"):
+    return workspace(moe_query_sizes(moe.E, moe.N, moe.K, moe.n_keep, moe.r_cat, T_max)["forward_ws_bytes"], device)
+
+
+def moe_forward(moe: SalrMoE, X, expert_offsets, Y=None, m_cap: int = 0, ws=None, stream=None):
+    """Grouped forward: rows [off[e], off[e+1]) of X (bf16 [T][K]) through
+    expert e; expert_offsets is a device int32 tensor [E + 1].  Returns Y
+    bf16 [T][N] (asynchronous on `stream`)."""
+    import torch
+
+    X = _as_bf16_bits(X, "X")
+    T = X.shape[0]
+    if X.dim() != 2 or X.shape[1] != moe.K:
+        raise ValueError("X must be [T][K]")
+    if expert_offsets.dtype != torch.int32 or expert_offsets.numel() != moe.E + 1:
+        raise ValueError("expert_offsets must be int32 [E + 1]")
+    if Y is None:
+        Y = torch.empty((T, moe.N), dtype=torch.bfloat16, device=X.device)
+    if ws is None:
+        ws = moe_workspace(moe, T, X.device)
+    d = moe.descriptor()
+    st = _lib().salr_moe_forward(C.byref(d), C.c_void_p(_dev_ptr(X, "X")) if T else None, T,
+                                 C.c_void_p(_dev_ptr(expert_offsets, "expert_offsets")), m_cap,
+                                 C.c_void_p(_dev_ptr(Y, "Y")) if T else None, C.c_void_p(ws.data_ptr()),
+                                 ws.numel() * ws.element_size(), _stream_ptr(stream))
+    _check(st, "salr_moe_forward")
+    return Y
 
 
 def probe_stream_read(src, sink, workgroups: int, stream=None):

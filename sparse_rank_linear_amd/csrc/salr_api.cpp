@@ -639,6 +639,132 @@ int salr_linear_backward(const salr_layer_t* L, const salr_layer_t* LT, const ui
 
 }  // extern "C"
 
+// ----------------------------------------------------------------------------
+// Grouped (mixture-of-experts) layers.
+namespace {
+
+constexpr int32_t kMaxExperts = 4096;
+
+struct MoeLayout {
+  size_t ms, vs, os, as, bs;       // per-expert strides (elements)
+  size_t mb, vb, ob, ab, bb;       // buffer bytes
+  int r_pad;
+};
+MoeLayout moe_layout(int32_t E, int64_t N, int64_t K, int32_t n_keep, int32_t r_cat) {
+  MoeLayout G{};
+  G.ms = align_up((size_t)N * cdiv(K, 64), 32);
+  G.vs = align_up((size_t)N * n_keep, 128);
+  G.os = align_up((size_t)N * cdiv(K, 1024), 64);
+  G.as = align_up((size_t)r_cat * K, 128);
+  G.bs = align_up((size_t)N * r_cat, 128);
+  G.mb = G.ms * E * 8;
+  G.vb = G.vs * E * 2 + kValuesPad;
+  G.ob = G.os * E * 4;
+  G.ab = G.as * E * 2;
+  G.bb = G.bs * E * 2 + kValuesPad;
+  G.r_pad = (int)align_up((size_t)r_cat, 32);
+  return G;
+}
+
+bool moe_dims_ok(const salr_moe_layer_t* G) {
+  return G && G->E >= 1 && G->E <= kMaxExperts && dims_ok(G->N, G->K, G->n_keep, G->r_cat) &&
+         G->N <= kMaxNK / G->K / G->E;
+}
+
+}  // namespace
+
+extern "C" {
+
+int salr_moe_query_sizes(int32_t E, int64_t N, int64_t K, int32_t n_keep, int32_t r_cat, int64_t T_max,
+                         salr_moe_sizes_t* out) {
+  salr_moe_layer_t g{};
+  g.E = E;
+  g.N = N;
+  g.K = K;
+  g.n_keep = n_keep;
+  g.r_cat = r_cat;
+  if (!out || !moe_dims_ok(&g) || T_max < 0 || T_max > (int64_t(1) << 31) - 1) return SALR_ERR_INVALID_ARG;
+  const MoeLayout G = moe_layout(E, N, K, n_keep, r_cat);
+  std::memset(out, 0, sizeof(*out));
+  out->masks_bytes = G.mb;
+  out->values_bytes = G.vb;
+  out->offsets_bytes = G.ob;
+  out->a_cat_bytes = G.ab;
+  out->b_cat_bytes = G.bb;
+  out->masks_stride = G.ms;
+  out->values_stride = G.vs;
+  out->offsets_stride = G.os;
+  out->a_cat_stride = G.as;
+  out->b_cat_stride = G.bs;
+  out->forward_ws_bytes = r_cat > 0 ? align_up((size_t)T_max * G.r_pad * 2, 256) + 256 : 256;
+  return SALR_OK;
+}
+
+int salr_moe_expert(const salr_moe_layer_t* G, int32_t e, salr_layer_t* out) {
+  if (!out || !moe_dims_ok(G) || e < 0 || e >= G->E) return SALR_ERR_INVALID_ARG;
+  if (!G->masks || !G->offsets || (G->n_keep > 0 && !G->values)) return SALR_ERR_INVALID_ARG;
+  if (G->r_cat > 0 && (!G->a_cat || !G->b_cat)) return SALR_ERR_INVALID_ARG;
+  const MoeLayout L = moe_layout(G->E, G->N, G->K, G->n_keep, G->r_cat);
+  std::memset(out, 0, sizeof(*out));
+  out->N = G->N;
+  out->K = G->K;
+  out->n_keep = G->n_keep;
+  out->r_cat = G->r_cat;
+  out->masks = G->masks + L.ms * e;
+  out->values = G->values ? G->values + L.vs * e : nullptr;
+  out->offsets = G->offsets + L.os * e;
+  out->a_cat = G->r_cat > 0 ? G->a_cat + L.as * e : nullptr;
+  out->b_cat = G->r_cat > 0 ? G->b_cat + L.bs * e : nullptr;
+  out->value_format = SALR_VALUES_BF16;
+  return SALR_OK;
+}
+
+int salr_moe_forward(const salr_moe_layer_t* G, const uint16_t* X, int64_t T, const int32_t* expert_offsets,
+                     int64_t m_cap, uint16_t* Y, void* ws, size_t ws_bytes, void* stream) {
+  if (!moe_dims_ok(G)) return SALR_ERR_INVALID_ARG;
+  if (T < 0 || T > (int64_t(1) << 31) - 1 || m_cap < 0) return SALR_ERR_INVALID_ARG;
+  if (T == 0) return SALR_OK;
+  if (!X || !Y || !expert_offsets) return SALR_ERR_INVALID_ARG;
+  if (!G->masks || !G->offsets || (G->n_keep > 0 && !G->values)) return SALR_ERR_INVALID_ARG;
+  if (G->r_cat > 0 && (!G->a_cat || !G->b_cat)) return SALR_ERR_INVALID_ARG;
+  const void* ptrs[] = {X, Y, G->masks, G->values, G->offsets, G->a_cat, G->b_cat};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return SALR_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(expert_offsets) & 3u) != 0) return SALR_ERR_INVALID_ARG;
+  if (static_cast<const void*>(X) == static_cast<const void*>(Y)) return SALR_ERR_INVALID_ARG;
+  const MoeLayout L = moe_layout(G->E, G->N, G->K, G->n_keep, G->r_cat);
+  if (!ws || !aligned16(ws)) return SALR_ERR_WORKSPACE;
+  if (G->r_cat > 0 && ws_bytes < (size_t)T * L.r_pad * 2) return SALR_ERR_WORKSPACE;
+  salr::MoeArgs a{};
+  a.masks = G->masks;
+  a.values = G->values;
+  a.offsets = G->offsets;
+  a.a_cat = G->a_cat;
+  a.b_cat = G->b_cat;
+  a.mstride = L.ms;
+  a.vstride = L.vs;
+  a.ostride = L.os;
+  a.astride = L.as;
+  a.bstride = L.bs;
+  a.X = X;
+  a.Y = Y;
+  a.eoff = expert_offsets;
+  a.t16 = static_cast<uint16_t*>(ws);
+  a.N = G->N;
+  a.E = G->E;
+  a.T = (int32_t)T;
+  a.K = (int32_t)G->K;
+  a.n_keep = G->n_keep;
+  a.r_cat = G->r_cat;
+  a.r_pad = G->r_cat > 0 ? L.r_pad : 0;
+  a.kw = (int32_t)cdiv(G->K, 64);
+  a.ng = (int32_t)cdiv(G->K, 1024);
+  const int32_t cap = (int32_t)(m_cap > 0 ? std::min<int64_t>(m_cap, T) : T);
+  return salr::launch_moe_forward(a, cap, static_cast<hipStream_t>(stream)) == hipSuccess ? SALR_OK : SALR_ERR_HIP;
+}
+
+}  // extern "C"
+
 // The forward behind both entry points: `ws` is the workspace (caller's, or
 // the library's fixed array), `err` the word a timed-out wait sets.
 int salr::forward_impl(const salr_layer_t* L, const uint16_t* X, int64_t M, uint16_t* Y, void* ws, size_t ws_bytes,

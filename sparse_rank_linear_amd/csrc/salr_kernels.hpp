@@ -205,6 +205,29 @@ hipError_t launch_gemm_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int
                           int64_t Kc, int splits, float* part, float* out, hipStream_t s);
 
 // ----------------------------------------------------------------------------
+// Grouped (mixture-of-experts) forward: E experts stacked at fixed strides
+// (elements of each array per expert), rows [eoff[e], eoff[e+1]) of X go to
+// expert e; t16 is the bf16 T = X_e A_cat,e scratch [T][r_pad], r_pad a
+// multiple of 32.
+struct MoeArgs {
+  const uint64_t* masks;
+  const uint16_t* values;
+  const uint32_t* offsets;
+  const uint16_t* a_cat;
+  const uint16_t* b_cat;
+  size_t mstride, vstride, ostride, astride, bstride;
+  const uint16_t* X;
+  uint16_t* Y;
+  const int32_t* eoff;
+  uint16_t* t16;
+  int64_t N;
+  int32_t E, T, K, n_keep, r_cat, r_pad, kw, ng;
+};
+// m_cap: the expected most rows of one expert (sets the low-rank grid; any
+// count is computed correctly).
+hipError_t launch_moe_forward(const MoeArgs& a, int32_t m_cap, hipStream_t s);
+
+// ----------------------------------------------------------------------------
 // Encode kernels.
 // ----------------------------------------------------------------------------
 struct PrunePackArgs {

@@ -346,3 +346,71 @@ def test_backward_validation_paths():
     assert _bwd(d, LT) == -1
     assert _bwd(L, LT, ws=0) == -3
     assert _bwd(L, LT, ws_bytes=4096) == -3
+
+
+def _moe(E=4, N=64, K=128, n_keep=64, r_cat=8, base=0x10000000):
+    d = B.salr_moe_layer_t()
+    d.E, d.N, d.K, d.n_keep, d.r_cat = E, N, K, n_keep, r_cat
+    d.masks, d.values, d.offsets = base, base + 0x1000000, base + 0x2000000
+    d.a_cat = base + 0x3000000 if r_cat else None
+    d.b_cat = base + 0x4000000 if r_cat else None
+    return d
+
+
+def test_moe_sizes_and_expert_views():
+    E, N, K, n_keep, r = 8, 14336, 4096, 2048, 80
+    sz = srl.moe_query_sizes(E, N, K, n_keep, r, 32)
+    assert sz["masks_stride"] == N * K // 64 and sz["values_stride"] == N * n_keep
+    assert sz["masks_bytes"] == E * N * K // 8
+    assert sz["values_bytes"] >= E * N * n_keep * 2 + 256          # tail padding
+    assert sz["b_cat_bytes"] >= E * N * r * 2 + 256
+    assert sz["forward_ws_bytes"] >= 32 * 96 * 2                    # bf16 T, ranks padded to 32
+    for name in ("masks", "values", "offsets", "a_cat", "b_cat"):   # 256-byte aligned expert slices
+        esize = {"masks": 8, "values": 2, "offsets": 4, "a_cat": 2, "b_cat": 2}[name]
+        assert (sz[name + "_stride"] * esize) % 256 == 0
+    # ragged shapes keep every slice aligned
+    sz = srl.moe_query_sizes(3, 7, 520, 9, 5, 1)
+    assert sz["values_stride"] % 128 == 0 and sz["masks_stride"] % 32 == 0 and sz["offsets_stride"] % 64 == 0
+    # expert views
+    d = _moe(E=3, N=7, K=520, n_keep=9, r_cat=5)
+    out = B.salr_layer_t()
+    assert srl.lib().salr_moe_expert(C.byref(d), 2, C.byref(out)) == 0
+    assert (out.N, out.K, out.n_keep, out.r_cat, out.n_parts) == (7, 520, 9, 5, 0)
+    assert out.values == d.values + 2 * sz["values_stride"] * 2
+    assert out.masks == d.masks + 2 * sz["masks_stride"] * 8
+    assert out.offsets == d.offsets + 2 * sz["offsets_stride"] * 4
+    assert out.a_cat == d.a_cat + 2 * sz["a_cat_stride"] * 2
+    assert out.b_cat == d.b_cat + 2 * sz["b_cat_stride"] * 2
+    assert srl.lib().salr_moe_expert(C.byref(d), 3, C.byref(out)) == -1
+    assert srl.lib().salr_moe_expert(C.byref(d), -1, C.byref(out)) == -1
+
+
+def test_moe_validation_paths():
+    lib = srl.lib()
+    out = B.salr_moe_sizes_t()
+    assert lib.salr_moe_query_sizes(0, 64, 128, 64, 8, 1, C.byref(out)) == -1      # E < 1
+    assert lib.salr_moe_query_sizes(4097, 64, 128, 64, 8, 1, C.byref(out)) == -1   # too many experts
+    assert lib.salr_moe_query_sizes(4, 64, 128, 129, 8, 1, C.byref(out)) == -1     # n_keep > K
+    assert lib.salr_moe_query_sizes(4, 64, 60, 8, 8, 1, C.byref(out)) == -1        # K % 8
+
+    def fwd(d, X=0x20000000, T=4, off=0x21000000, m_cap=0, Y=0x30000000, ws=0x40000000, ws_bytes=1 << 30):
+        vp = lambda a: C.c_void_p(a) if a else None
+        return lib.salr_moe_forward(C.byref(d) if d is not None else None, vp(X), T, vp(off), m_cap, vp(Y), vp(ws),
+                                    ws_bytes, None)
+
+    assert fwd(_moe(), T=0) == 0                     # no rows: a no-op
+    assert fwd(None) == -1
+    assert fwd(_moe(), T=-1) == -1
+    assert fwd(_moe(), m_cap=-1) == -1
+    assert fwd(_moe(), X=0) == -1
+    assert fwd(_moe(), Y=0) == -1
+    assert fwd(_moe(), off=0) == -1
+    assert fwd(_moe(), off=0x21000002) == -1         # misaligned offsets
+    assert fwd(_moe(), X=0x20000008) == -1
+    assert fwd(_moe(), X=0x30000000, Y=0x30000000) == -1
+    d = _moe()
+    d.b_cat = None
+    assert fwd(d) == -1
+    assert fwd(_moe(K=60)) == -1
+    assert fwd(_moe(), ws=0) == -3
+    assert fwd(_moe(), ws_bytes=64) == -3
