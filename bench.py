@@ -35,6 +35,14 @@ Printed JSON fields beyond the common contract:
   l70b_up_s50   the 70B-shaped layer (28672x8192, Student-t, 50%, r_cat 160)
                 at 8192 tokens, likewise
   encode        wall time of salr_encode for the headline layer
+  qsalr_nf4     the headline layer with NF4 values (QSALR): bytes per weight
+                element and the HBM fraction at 16 tokens
+  backward      dX, dA_cat, dB_cat of the headline layer at 2048 tokens
+                against the bf16 matrix-core peak, and the one-off build of
+                the transposed encoding
+  moe           grouped expert layers (Mixtral-8x7B and DeepSeek-V2-Lite
+                expert shapes, seeded top-k routing of 16 tokens) against
+                HBM peak on the routed experts' bytes
 
     python bench.py --configs
 
@@ -505,11 +513,133 @@ def main():
                                          steps=20, warmup=3)
         out["l70b_up_s50"] = many_token_line(dev, "l70b_up_s50", "l70b_up_28672x8192_s50_m8192", peaks,
                                              steps=5, warmup=2)
+        out["qsalr_nf4"] = nf4_line(dev, layer, wl, steps=128, warmup=16)
+        out["backward"] = backward_line(dev, layer, wl, M=2048, steps=10, warmup=2)
+        del layer
+        torch.cuda.empty_cache()
+        out["moe"] = [moe_line(dev, name, steps=64, warmup=8) for name in ("mixtral_8x7b_w1", "deepseek_v2_lite_up")]
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out), flush=True)
     if not checks["ok"]:
         print(f"bench.py: the timed run failed its checks: {checks}", file=sys.stderr)
         sys.exit(1)
+
+
+def nf4_line(dev, layer, wl, steps, warmup):
+    """The headline layer with its kept values in NF4 (QSALR): rotating
+    quantized copies (> 512 MB), 16 tokens, against HBM peak."""
+    import torch
+    import sparse_rank_linear_amd as srl
+    from sparse_rank_linear_amd import synth
+
+    q = srl.quantize_nf4(layer.clone())
+    cb = q.compressed_bytes()
+    copies = max(2, -(-600_000_000 // cb))
+    layers = [q] + [q.clone() for _ in range(copies - 1)]
+    M = wl.M
+    X = _dev_bits(synth.make_x(wl.K, M, seed=13), dev)
+    ws = srl.forward_workspace(q, M)
+    r = measure_decode(layers, X, ws, steps, warmup, reps=4, detail=True)
+    t = r["mean"]
+    algo = cb + 2 * M * (wl.K + wl.N)
+    adapters = 2 * wl.r_cat * (wl.K + wl.N)
+    line = {"workload": "llama7b_attn_4096x4096_decode_nf4", "M": M, "rotating_copies": copies,
+            "compressed_weight_bytes": cb, "weight_bytes_per_element": round((cb - adapters) / (wl.N * wl.K), 4),
+            "us_per_step": round(t * 1e6, 3), "us_median": round(r["median"] * 1e6, 3),
+            "compressed_GBs": round(cb / t / 1e9, 1), "hbm_frac": round(algo / t / 1e9 / HBM_PEAK_GBS, 4),
+            "wait_error": srl.wait_error(ws)}
+    del layers, q, ws
+    torch.cuda.empty_cache()
+    return line
+
+
+def backward_line(dev, layer, wl, M, steps, warmup):
+    """One backward call of the headline layer (dX, dA_cat, dB_cat) at M
+    tokens, graph-replayed, against the bf16 matrix-core peak; plus the
+    one-off build of the transposed encoding."""
+    import torch
+    import sparse_rank_linear_amd as srl
+    from sparse_rank_linear_amd import synth
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    lt = srl.transpose_layer(layer)
+    t_transpose = time.perf_counter() - t0
+    X = _dev_bits(synth.make_x(wl.K, M, seed=14), dev)
+    dY = _dev_bits(synth.make_x(wl.N, M, seed=15), dev)
+    ws = srl.backward_workspace(layer, lt, M)
+    dX = torch.empty((M, wl.K), dtype=torch.bfloat16, device=dev)
+    dA = torch.empty((wl.r_cat, wl.K), dtype=torch.float32, device=dev)
+    dB = torch.empty((wl.N, wl.r_cat), dtype=torch.float32, device=dev)
+    call = lambda: srl.linear_backward(layer, lt, X, dY, dX=dX, dA=dA, dB=dB, ws=ws)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    g = _timed_graph([call], steps)
+    g.replay()
+    torch.cuda.synchronize()
+    t = _time_replay(g) / steps
+    r = wl.r_cat
+    dense = 2 * M * wl.N * wl.K + 2 * M * r * (wl.K + wl.N) * 3  # dX (dense-equiv, with its low-rank), G, T, dA, dB
+    line = {"workload": "llama7b_attn_4096x4096_backward", "M": M, "r_cat": r, "ms_per_step": round(t * 1e3, 4),
+            "tflops_dense_equiv": round(dense / t / 1e12, 2),
+            "mfma_frac_dense_equiv": round(dense / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "transpose_build_ms": round(t_transpose * 1e3, 2), "n_keep_transposed": lt.n_keep,
+            "wait_error": srl.wait_error(ws)}
+    del lt, X, dY, ws, dX, dA, dB, g
+    torch.cuda.empty_cache()
+    return line
+
+
+def moe_line(dev, name, steps, warmup):
+    """A grouped expert layer in the decode regime: every expert encoded on
+    the GPU (its own weight, residual SVD and LoRA), a seeded top-k routing
+    of the batch, rotating copies of the whole expert set (> 512 MB), one
+    salr_moe_forward per step; HBM fraction on the bytes the step must read
+    (the routed experts' compressed weights, X and Y)."""
+    import torch
+    import sparse_rank_linear_amd as srl
+    from sparse_rank_linear_amd import synth
+
+    mw = synth.MOE_WORKLOADS[name]
+    moe = srl.SalrMoE.empty(mw.E, mw.N, mw.K, mw.n_keep, mw.r_cat, dev)
+    for e in range(mw.E):
+        inp = synth.make_inputs(mw.expert_workload(e), with_x=False)
+        srl.moe_encode_expert(moe, e, _dev_bits(inp.W, dev), mw.r_svd, [_dev_bits(a, dev) for a in inp.lora_A],
+                              [_dev_bits(b, dev) for b in inp.lora_B])
+    torch.cuda.synchronize()
+    counts, _ = synth.make_routing(mw.E, mw.tokens, mw.top_k, seed=mw.seed + 3)
+    T = int(counts.sum())
+    off = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).to(dev)
+    kw, ng = -(-mw.K // 64), -(-mw.K // 1024)
+    per_expert = mw.N * kw * 8 + mw.N * mw.n_keep * 2 + mw.N * ng * 4 + 2 * mw.r_cat * (mw.K + mw.N)
+    copies = max(1, -(-600_000_000 // (per_expert * mw.E)))
+    sets = [moe]
+    for _ in range(copies - 1):
+        c = srl.SalrMoE.empty(mw.E, mw.N, mw.K, mw.n_keep, mw.r_cat, dev)
+        for f in ("masks", "values", "offsets", "a_cat", "b_cat"):
+            getattr(c, f).copy_(getattr(moe, f))
+        sets.append(c)
+    X = _dev_bits(synth.make_x(mw.K, T, seed=16), dev)
+    Y = torch.empty((T, mw.N), dtype=torch.bfloat16, device=dev)
+    ws = srl.moe_workspace(moe, T, dev)
+    fns = [(lambda m=m: srl.moe_forward(m, X, off, Y=Y, m_cap=int(counts.max()), ws=ws)) for m in sets]
+    for j in range(warmup):
+        fns[j % len(fns)]()
+    torch.cuda.synchronize()
+    g = _timed_graph(fns, steps)
+    g.replay()
+    torch.cuda.synchronize()
+    t = _time_replay(g) / steps
+    active = int((counts > 0).sum())
+    algo = active * per_expert + 2 * T * (mw.K + mw.N)
+    line = {"workload": f"{name}_{mw.E}x{mw.N}x{mw.K}_top{mw.top_k}_of_{mw.tokens}", "rows": T,
+            "active_experts": active, "rotating_copies": copies, "us_per_step": round(t * 1e6, 3),
+            "routed_weight_bytes": active * per_expert, "compressed_GBs": round(active * per_expert / t / 1e9, 1),
+            "hbm_frac": round(algo / t / 1e9 / HBM_PEAK_GBS, 4)}
+    del sets, moe, X, Y, ws, g
+    torch.cuda.empty_cache()
+    return line
 
 
 def many_token_line(dev, name, label, peaks, steps, warmup):

@@ -26,6 +26,7 @@ from .binding import (  # noqa: F401
     linear_backward,
     linear_forward,
     linear_forward_noalloc,
+    moe_encode_expert,
     moe_forward,
     moe_query_sizes,
     moe_workspace,
@@ -44,6 +45,6 @@ from .binding import (  # noqa: F401
 __all__ = [
     "EXPORTS", "LIB_PATH", "NOALLOC_SCRATCH_BYTES", "SalrError", "SalrLayer", "SalrMoE", "WaitTimeout", "backward_workspace",
     "backward_ws_bytes", "encode", "forward_workspace", "fuse", "lib", "linear_backward", "linear_forward",
-    "linear_forward_noalloc", "moe_forward", "moe_query_sizes", "moe_workspace", "nf4_levels", "probe_mfma", "probe_stream_read", "quantize_nf4", "query_sizes",
+    "linear_forward_noalloc", "moe_encode_expert", "moe_forward", "moe_query_sizes", "moe_workspace", "nf4_levels", "probe_mfma", "probe_stream_read", "quantize_nf4", "query_sizes",
     "transpose_count", "transpose_layer", "transpose_ws_bytes", "wait_error", "workspace",
 ]

@@ -356,6 +356,15 @@ def encode(W, n_keep: int, r_svd: int, lora_A=(), lora_B=(), oversample: int | N
     ranks = [int(a.shape[0]) for a in lora_A]
     r_cat = r_svd + sum(ranks)
     layer = SalrLayer.empty(N, K, n_keep, r_svd, r_cat, W.device)
+    sig = _encode_into(layer.descriptor(), W, n_keep, r_svd, lora_A, lora_B, oversample, iters, seed, ws, stream)
+    return layer, sig
+
+
+def _encode_into(desc, W, n_keep, r_svd, lora_A, lora_B, oversample, iters, seed, ws, stream):
+    """salr_encode into the buffers of an existing descriptor."""
+    N, K = W.shape
+    ranks = [int(a.shape[0]) for a in lora_A]
+    r_cat = r_svd + sum(ranks)
     sz = query_sizes(N, K, n_keep, r_svd, r_cat, 0)
     if ws is None:
         ws = workspace(sz["encode_ws_bytes"], W.device)
@@ -367,7 +376,6 @@ def encode(W, n_keep: int, r_svd: int, lora_A=(), lora_B=(), oversample: int | N
     if oversample is not None or iters is not None or seed:
         opts = salr_encode_opts_t(32 if oversample is None else oversample, 24 if iters is None else iters, seed)
     sig = (C.c_double * max(r_svd, 1))()
-    desc = layer.descriptor()
     st = _lib().salr_encode(
         C.c_void_p(_dev_ptr(W, "W")), N, K, n_keep, r_svd, nl,
         C.cast(a_ptrs, C.POINTER(C.c_void_p)) if nl else None,
@@ -376,7 +384,7 @@ def encode(W, n_keep: int, r_svd: int, lora_A=(), lora_B=(), oversample: int | N
         C.byref(opts) if opts is not None else None, C.byref(desc), sig,
         C.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), _stream_ptr(stream))
     _check(st, "salr_encode")
-    return layer, [sig[i] for i in range(r_svd)]
+    return [sig[i] for i in range(r_svd)]
 
 
 def forward_workspace(layer: SalrLayer, M_max: int, device="cuda"):
@@ -647,6 +655,15 @@ class SalrMoE:
             start = e * stride * esize // 2
             import torch
             buf[start:start + flat.size].copy_(torch.from_numpy(flat))
+
+
+def moe_encode_expert(moe: SalrMoE, e: int, W, r_svd: int, lora_A=(), lora_B=(), ws=None, stream=None):
+    """salr_encode expert e's weight W (bf16 [N][K]) in place into the
+    stacked buffers (r_svd + the LoRA ranks must equal moe.r_cat)."""
+    W = _as_bf16_bits(W, "W")
+    if tuple(W.shape) != (moe.N, moe.K):
+        raise ValueError("W must be [N][K]")
+    return _encode_into(moe.expert(e), W, moe.n_keep, r_svd, lora_A, lora_B, None, None, 0, ws, stream)
 
 
 def moe_workspace(moe: SalrMoE, T_max: int, device="cuda"):

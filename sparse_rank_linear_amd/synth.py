@@ -149,3 +149,54 @@ for _s in (0.6, 0.7):
                                              r_svd=128, lora_ranks=(32,), w_dist="t3")
     WORKLOADS[f"l70b_down_s{_tag}"] = Workload(f"l70b_down_s{_tag}", N=8192, K=28672, M=8192,
                                                sparsity=_s, r_svd=128, lora_ranks=(32,), w_dist="t3")
+
+
+# Mixture-of-experts expert layers in the decode regime (the MoE models of
+# the same summary's Experimental Results: Mixtral-8x7B and
+# DeepSeek-V2-Lite), each expert its own weight and adapters.
+@dataclass
+class MoeWorkload:
+    name: str
+    E: int          # experts
+    N: int
+    K: int
+    tokens: int     # tokens in the batch
+    top_k: int      # experts per token
+    sparsity: float = 0.5
+    r_svd: int = 64
+    lora_ranks: tuple = (16,)
+    seed: int = 0
+
+    @property
+    def n_keep(self) -> int:
+        return n_keep_for(self.K, self.sparsity)
+
+    @property
+    def r_cat(self) -> int:
+        return self.r_svd + sum(self.lora_ranks)
+
+    def expert_workload(self, e: int) -> Workload:
+        """Expert e's layer (its own seed)."""
+        return Workload(f"{self.name}_e{e}", N=self.N, K=self.K, M=0, sparsity=self.sparsity, r_svd=self.r_svd,
+                        lora_ranks=self.lora_ranks, seed=self.seed * 1000 + e + 1)
+
+
+MOE_WORKLOADS = {
+    # expert up/gate projection 14336 x 4096, 8 experts, top-2 of 16 tokens
+    "mixtral_8x7b_w1": MoeWorkload("mixtral_8x7b_w1", E=8, N=14336, K=4096, tokens=16, top_k=2),
+    # routed expert up projection 1408 x 2048, 64 experts, top-6 of 16 tokens
+    "deepseek_v2_lite_up": MoeWorkload("deepseek_v2_lite_up", E=64, N=1408, K=2048, tokens=16, top_k=6),
+}
+
+
+def make_routing(E: int, tokens: int, top_k: int, seed: int):
+    """A seeded random routing: each token picks top_k distinct experts
+    uniformly.  Returns (counts per expert, int64 [tokens*top_k] token index
+    of each grouped row: the rows of expert 0 first, then expert 1, ...)."""
+    rng = np.random.default_rng(seed)
+    picks = np.stack([rng.choice(E, top_k, replace=False) for _ in range(tokens)])  # [tokens x top_k]
+    expert = picks.reshape(-1)
+    token = np.repeat(np.arange(tokens), top_k)
+    order = np.argsort(expert, kind="stable")
+    counts = np.bincount(expert, minlength=E)
+    return counts, token[order]
