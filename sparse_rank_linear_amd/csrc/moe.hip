@@ -8,8 +8,11 @@
 // routing needs no host round trip, and an expert with no rows costs one
 // early exit per workgroup and none of its weight bytes.
 //
-//   1. moe_lowrank_kernel: T = X_e A_cat,e for every expert's rows, rounded
-//      to bf16 [T][r_pad] (the same rounding as the single-layer forward).
+//   1. moe_lowrank_kernel: partials of T = X_e A_cat,e for every expert's
+//      rows over K ranges (many workgroups per expert, each with all of a
+//      step's loads in flight), then moe_tsum_kernel: their sum in range
+//      order rounded to bf16 [T][r_pad] (the same rounding as the
+//      single-layer forward).
 //   2. moe_fwd_kernel: one workgroup per (16-row tile, expert).  It streams
 //      the tile's compressed rows in 1024-column chunks (bitmap words to
 //      LDS, each row's kept-value segment -- located by the lookup table --
@@ -38,7 +41,9 @@ constexpr int kMoeTok = 64;         // tokens per pass (4 MFMA column blocks)
 constexpr int kMoeRowStride = 1048; // bf16 per LDS row buffer: 7 lead + 1024 + window overrun
 constexpr int kMoePieces = (kMoeChunk + 7 + 7) / 8;  // 16-byte pieces per row segment, at most
 constexpr int kMoeMaxRT = 16;       // rank tiles of 16 (r_cat <= 256)
-constexpr int kMoeALds = 72;        // bf16 per LDS row of the A_cat stage (64 + 8 pad)
+constexpr int kMoeTK = 128;         // A_cat columns per low-rank step
+constexpr int64_t kMoeTPartCap = int64_t(32) << 20;  // bytes of fp32 T partials (more K splits while under it)
+constexpr int kMoeTLds = kMoeTK + 8;  // bf16 per LDS row of the A_cat stage
 
 // Expert e's token rows [s, t), clamped into [0, T] so that malformed
 // boundaries can never send a workgroup out of X or Y.
@@ -47,54 +52,77 @@ __device__ __forceinline__ void expert_rows(const int32_t* eoff, int e, int32_t 
   t = min(max(eoff[e + 1], s), T);
 }
 
-// 1. T rows of one expert: workgroup (e, c) takes 64-row blocks c, c + gridDim.y, ...
+// 1a. Partial T of one expert over one K range: workgroup (e, ks, cb)
+// takes the columns [ks kspan, + kspan) in steps of kMoeTK (all of a step's
+// A_cat loads issued at once) and the expert's 64-row blocks cb, cb + CB,
+// ...; fp32 partials tpart[ks][token][r_pad].
 __global__ __launch_bounds__(kMoeThreads) void moe_lowrank_kernel(MoeArgs a) {
-  __shared__ uint32_t al[kMoeMaxRT * 16 * (kMoeALds / 2)];
-  const int e = blockIdx.x;
+  __shared__ uint16_t al[kMoeMaxRT * 16 * kMoeTLds];
+  const int e = blockIdx.x, ks = blockIdx.y;
   int32_t s, t;
   expert_rows(a.eoff, e, a.T, s, t);
+  if (s >= t) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, g = lane >> 4;
   const int rt = a.r_pad / 16;
+  const int k0 = ks * a.kspan, k1 = min(a.K, k0 + a.kspan);
   const uint16_t* A = a.a_cat + (size_t)e * a.astride;
-  for (int32_t base = s + kMoeTok * (int32_t)blockIdx.y; base < t; base += kMoeTok * (int32_t)gridDim.y) {
+  constexpr int kPer = kMoeMaxRT * 16 * (kMoeTK / 8) / kMoeThreads;  // 16-byte chunks per thread, at most
+  for (int32_t base = s + kMoeTok * (int32_t)blockIdx.z; base < t; base += kMoeTok * (int32_t)gridDim.z) {
     const int32_t token = base + wave * 16 + i;
     const bool live = token < t;
     f32x4_t acc[kMoeMaxRT];
 #pragma unroll
     for (int j = 0; j < kMoeMaxRT; ++j) acc[j] = zero4();
-    for (int kt = 0; kt < a.K; kt += 64) {
+    for (int kt = k0; kt < k1; kt += kMoeTK) {
+      u32x4_t av[kPer], xv[kMoeTK / 32];
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int c = tid + kMoeThreads * u;
+        const int r = c / (kMoeTK / 8), k = kt + 8 * (c % (kMoeTK / 8));
+        av[u] = (r < a.r_cat && k < k1) ? load16(A + (size_t)r * a.K + k) : zero_u4();
+      }
+#pragma unroll
+      for (int h = 0; h < kMoeTK / 32; ++h) {
+        const int k = kt + 32 * h + 8 * g;
+        xv[h] = (live && k < k1) ? load16(a.X + (size_t)token * a.K + k) : zero_u4();
+      }
       __syncthreads();  // (the previous step's reads of al are done)
-      for (int c = tid; c < a.r_pad * 8; c += kMoeThreads) {
-        const int r = c >> 3, k = kt + 8 * (c & 7);
-        const u32x4_t v = (r < a.r_cat && k < a.K) ? load16(A + (size_t)r * a.K + k) : zero_u4();
-        *reinterpret_cast<u32x4_t*>(&al[r * (kMoeALds / 2) + (c & 7) * 4]) = v;
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int c = tid + kMoeThreads * u;
+        const int r = c / (kMoeTK / 8);
+        if (r < a.r_pad) *reinterpret_cast<u32x4_t*>(&al[r * kMoeTLds + 8 * (c % (kMoeTK / 8))]) = av[u];
       }
       __syncthreads();
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int k = kt + 32 * h + 8 * g;
-        const u32x4_t xv = (live && k < a.K) ? load16(a.X + (size_t)token * a.K + k) : zero_u4();
+      for (int h = 0; h < kMoeTK / 32; ++h)
 #pragma unroll
         for (int j = 0; j < kMoeMaxRT; ++j)
           if (j < rt) {
-            const u32x4_t av = *reinterpret_cast<const u32x4_t*>(&al[(16 * j + i) * (kMoeALds / 2) + h * 16 + g * 4]);
-            acc[j] = mfma_16x16x32(av, xv, acc[j]);
+            const u32x4_t w = *reinterpret_cast<const u32x4_t*>(&al[(16 * j + i) * kMoeTLds + 32 * h + 8 * g]);
+            acc[j] = mfma_16x16x32(w, xv[h], acc[j]);
           }
-      }
     }
     // lane holds T[token i][rank 16j + 4g + e'] (e' = 0..3)
     if (live) {
+      float* dst = a.tpart + ((size_t)ks * a.T + token) * a.r_pad;
 #pragma unroll
       for (int j = 0; j < kMoeMaxRT; ++j)
-        if (j < rt) {
-          const f32x4_t v = acc[j];
-          *reinterpret_cast<u32x2_t*>(a.t16 + (size_t)token * a.r_pad + 16 * j + 4 * g) =
-              u32x2_t{(uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
-                      (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16)};
-        }
+        if (j < rt) *reinterpret_cast<f32x4_t*>(dst + 16 * j + 4 * g) = acc[j];
     }
   }
+}
+
+// 1b. T = bf16(sum of the K-range partials, in range order): 4 entries a
+// thread (rows of tokens outside every expert's range are never read).
+__global__ __launch_bounds__(256) void moe_tsum_kernel(const float* tpart, int splits, int64_t n, uint16_t* t16) {
+  const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e0 >= n) return;
+  f32x4_t v = zero4();
+  for (int sp = 0; sp < splits; ++sp) v += *reinterpret_cast<const f32x4_t*>(tpart + (size_t)sp * n + e0);
+  *reinterpret_cast<u32x2_t*>(t16 + e0) = u32x2_t{(uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                                                  (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16)};
 }
 
 struct MoeLds {
@@ -107,7 +135,7 @@ static_assert(sizeof(MoeLds) <= 48 * 1024, "MoE workgroup LDS");
 static_assert(kMoeRows * kMoeTok * 4 * 4 <= sizeof(uint16_t) * kMoeRows * kMoeRowStride, "partial sums fit");
 
 // 2. Y rows of one expert for one 16-row tile.
-__global__ __launch_bounds__(kMoeThreads) void moe_fwd_kernel(MoeArgs a) {
+__global__ __launch_bounds__(kMoeThreads) __attribute__((amdgpu_waves_per_eu(3))) void moe_fwd_kernel(MoeArgs a) {
   __shared__ MoeLds L;
   const int e = blockIdx.y;
   int32_t s, t;
@@ -128,19 +156,28 @@ __global__ __launch_bounds__(kMoeThreads) void moe_fwd_kernel(MoeArgs a) {
   const bool srow_ok = srow < a.N;
   const int nchunks = (a.K + kMoeChunk - 1) / kMoeChunk;
 
+  // a chunk's bitmap word and value range [lo, hi) (requested one chunk
+  // ahead, so a chunk's value loads wait for no lookup-table round trip)
+  const auto load_meta = [&](int ch, uint64_t& mw, uint32_t& lo, uint32_t& hi) __attribute__((always_inline)) {
+    const int w = ch * kMoeWords + sl;
+    mw = (srow_ok && ch < nchunks && w < a.kw) ? masks[srow * a.kw + w] : 0ull;
+    lo = hi = 0u;
+    if (srow_ok && ch < nchunks) {
+      lo = offs[srow * a.ng + ch];
+      hi = ch + 1 < a.ng ? offs[srow * a.ng + ch + 1] : (uint32_t)a.n_keep;
+    }
+  };
+
   for (int32_t base = s; base < t; base += kMoeTok) {
     const int nq = min(kMoeTok, t - base + 15) / 16;  // live 16-token blocks (1..4)
     f32x4_t acc[4] = {zero4(), zero4(), zero4(), zero4()};
+    uint64_t mw_next;
+    uint32_t lo_next, hi_next;
+    load_meta(0, mw_next, lo_next, hi_next);
     for (int ch = 0; ch < nchunks; ++ch) {
       // ---- stage chunk ch: masks, per-word prefix counts, value segments
-      const int kw0 = ch * kMoeWords;
-      const int w = kw0 + sl;
-      const uint64_t mw = (srow_ok && w < a.kw) ? masks[srow * a.kw + w] : 0ull;
-      uint32_t lo = 0, hi = 0;
-      if (srow_ok) {
-        lo = offs[srow * a.ng + ch];
-        hi = ch + 1 < a.ng ? offs[srow * a.ng + ch + 1] : (uint32_t)a.n_keep;
-      }
+      const uint64_t mw = mw_next;
+      const uint32_t lo = lo_next, hi = hi_next;
       const int64_t vfirst = srow * (int64_t)a.n_keep + lo;  // global index of the segment's first value
       const int64_t vstart = vfirst & ~int64_t(7);
       const int lead = (int)(vfirst - vstart);
@@ -151,6 +188,7 @@ __global__ __launch_bounds__(kMoeThreads) void moe_fwd_kernel(MoeArgs a) {
         const int p = sl + 16 * u;
         pv[u] = p < pieces ? load16(values + vstart + 8 * p) : zero_u4();
       }
+      load_meta(ch + 1, mw_next, lo_next, hi_next);
       // exclusive prefix of the row's word popcounts across its 16 lanes
       const uint32_t pc = (uint32_t)__popcll(mw);
       uint32_t incl = pc;
@@ -170,6 +208,28 @@ __global__ __launch_bounds__(kMoeThreads) void moe_fwd_kernel(MoeArgs a) {
       __syncthreads();
       // ---- decode and multiply: wave takes 32-column steps wave, wave + 4, ...
       const int cbase = ch * kMoeChunk;
+      if (nq == 1) {
+        // (one token block, the decode regime: X of all the wave's steps
+        // requested at once, so the steps wait for one L2 round trip)
+        u32x4_t xf[kMoeChunk / 32 / 4];
+#pragma unroll
+        for (int k = 0; k < kMoeChunk / 32 / 4; ++k) {
+          const int col = cbase + 32 * (wave + 4 * k) + 8 * g;
+          const int32_t tok = base + i;
+          xf[k] = (tok < t && col < a.K) ? load16(a.X + (size_t)tok * a.K + col) : zero_u4();
+        }
+#pragma unroll
+        for (int k = 0; k < kMoeChunk / 32 / 4; ++k) {
+          const int ks = wave + 4 * k;
+          if (cbase + 32 * ks >= a.K) break;
+          const uint64_t mk = L.masks[i][ks >> 1];
+          const int bit = 32 * (ks & 1) + 8 * g;
+          const uint32_t byte = (uint32_t)(mk >> bit) & 0xFFu;
+          const uint32_t idx = L.wpre[i][ks >> 1] + (uint32_t)__popcll(mk & ((1ull << bit) - 1ull));
+          acc[0] = mfma_16x16x32(expand_byte(&L.vals[i][0], idx, byte, L.lut), xf[k], acc[0]);
+        }
+        continue;
+      }
       for (int ks = wave; ks < kMoeChunk / 32; ks += 4) {
         const int col = cbase + 32 * ks + 8 * g;
         if (cbase + 32 * ks >= a.K) break;
@@ -246,11 +306,30 @@ __global__ __launch_bounds__(kMoeThreads) void moe_fwd_kernel(MoeArgs a) {
 
 }  // namespace
 
+int moe_lowrank_splits(int64_t T, int64_t K, int r_pad) {
+  const int64_t steps = (K + kMoeTK - 1) / kMoeTK;
+  const int64_t per = std::max<int64_t>(1, T * r_pad * 4);
+  return (int)std::max<int64_t>(1, std::min<int64_t>(steps, kMoeTPartCap / per));
+}
+
+size_t moe_lowrank_part_bytes(int64_t T, int64_t K, int r_pad) {
+  // a bound of splits * T * r_pad * 4 that grows with T: the splits keep the
+  // partials under the cap, down to one split
+  const int64_t steps = (K + kMoeTK - 1) / kMoeTK;
+  const size_t row = (size_t)T * r_pad * 4;
+  const size_t b = std::min<size_t>((size_t)steps * row, std::max<size_t>((size_t)kMoeTPartCap, row));
+  return (b + 255) / 256 * 256;
+}
+
 hipError_t launch_moe_forward(const MoeArgs& a, int32_t m_cap, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   if (a.r_cat > 0) {
-    const int chunks = std::max(1, std::min(1024, (m_cap + kMoeTok - 1) / kMoeTok));
-    hipLaunchKernelGGL(moe_lowrank_kernel, dim3((unsigned)a.E, (unsigned)chunks), dim3(kMoeThreads), 0, s, a);
+    const int blocks = std::max(1, std::min(64, (m_cap + kMoeTok - 1) / kMoeTok));
+    hipLaunchKernelGGL(moe_lowrank_kernel, dim3((unsigned)a.E, (unsigned)a.ksplits, (unsigned)blocks),
+                       dim3(kMoeThreads), 0, s, a);
+    const int64_t n = (int64_t)a.T * a.r_pad;  // (r_pad % 32 == 0)
+    hipLaunchKernelGGL(moe_tsum_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s, a.tpart, a.ksplits,
+                       n, a.t16);
   }
   const int64_t tiles = (a.N + kMoeRows - 1) / kMoeRows;
   hipLaunchKernelGGL(moe_fwd_kernel, dim3((unsigned)tiles, (unsigned)a.E), dim3(kMoeThreads), 0, s, a);

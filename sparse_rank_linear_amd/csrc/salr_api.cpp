@@ -696,7 +696,8 @@ int salr_moe_query_sizes(int32_t E, int64_t N, int64_t K, int32_t n_keep, int32_
   out->offsets_stride = G.os;
   out->a_cat_stride = G.as;
   out->b_cat_stride = G.bs;
-  out->forward_ws_bytes = r_cat > 0 ? align_up((size_t)T_max * G.r_pad * 2, 256) + 256 : 256;
+  out->forward_ws_bytes =
+      r_cat > 0 ? salr::moe_lowrank_part_bytes(T_max, K, G.r_pad) + align_up((size_t)T_max * G.r_pad * 2, 256) : 256;
   return SALR_OK;
 }
 
@@ -734,7 +735,8 @@ int salr_moe_forward(const salr_moe_layer_t* G, const uint16_t* X, int64_t T, co
   if (static_cast<const void*>(X) == static_cast<const void*>(Y)) return SALR_ERR_INVALID_ARG;
   const MoeLayout L = moe_layout(G->E, G->N, G->K, G->n_keep, G->r_cat);
   if (!ws || !aligned16(ws)) return SALR_ERR_WORKSPACE;
-  if (G->r_cat > 0 && ws_bytes < (size_t)T * L.r_pad * 2) return SALR_ERR_WORKSPACE;
+  const size_t part_bytes = G->r_cat > 0 ? salr::moe_lowrank_part_bytes(T, G->K, L.r_pad) : 0;
+  if (G->r_cat > 0 && ws_bytes < part_bytes + (size_t)T * L.r_pad * 2) return SALR_ERR_WORKSPACE;
   salr::MoeArgs a{};
   a.masks = G->masks;
   a.values = G->values;
@@ -749,7 +751,8 @@ int salr_moe_forward(const salr_moe_layer_t* G, const uint16_t* X, int64_t T, co
   a.X = X;
   a.Y = Y;
   a.eoff = expert_offsets;
-  a.t16 = static_cast<uint16_t*>(ws);
+  a.tpart = static_cast<float*>(ws);
+  a.t16 = at<uint16_t>(ws, part_bytes);
   a.N = G->N;
   a.E = G->E;
   a.T = (int32_t)T;
@@ -759,6 +762,12 @@ int salr_moe_forward(const salr_moe_layer_t* G, const uint16_t* X, int64_t T, co
   a.r_pad = G->r_cat > 0 ? L.r_pad : 0;
   a.kw = (int32_t)cdiv(G->K, 64);
   a.ng = (int32_t)cdiv(G->K, 1024);
+  if (G->r_cat > 0) {
+    const int64_t steps = cdiv(G->K, 128);
+    const int64_t splits = salr::moe_lowrank_splits(T, G->K, L.r_pad);
+    a.kspan = (int32_t)(cdiv(steps, splits) * 128);
+    a.ksplits = (int32_t)cdiv(G->K, a.kspan);
+  }
   const int32_t cap = (int32_t)(m_cap > 0 ? std::min<int64_t>(m_cap, T) : T);
   return salr::launch_moe_forward(a, cap, static_cast<hipStream_t>(stream)) == hipSuccess ? SALR_OK : SALR_ERR_HIP;
 }

@@ -220,9 +220,15 @@ struct MoeArgs {
   uint16_t* Y;
   const int32_t* eoff;
   uint16_t* t16;
+  float* tpart;            // fp32 partials of T over K ranges [ksplits][T][r_pad]
   int64_t N;
   int32_t E, T, K, n_keep, r_cat, r_pad, kw, ng;
+  int32_t ksplits, kspan;  // K ranges of the low-rank partials, columns per range (multiple of 128)
 };
+// K ranges of the grouped low-rank partials for T rows, and workspace bytes
+// that hold their partials for any T' <= T (bf16 T follows them).
+int moe_lowrank_splits(int64_t T, int64_t K, int r_pad);
+size_t moe_lowrank_part_bytes(int64_t T, int64_t K, int r_pad);
 // m_cap: the expected most rows of one expert (sets the low-rank grid; any
 // count is computed correctly).
 hipError_t launch_moe_forward(const MoeArgs& a, int32_t m_cap, hipStream_t s);
