@@ -412,6 +412,10 @@ def main():
                     help="time every workload of the synthetic table instead of the headline line")
     ap.add_argument("--probe", choices=["copy"], default=None,
                     help="run a plain 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--line", default=None,
+                    choices=["nf4", "backward", "prefill", "l70b_up_s50", "moe:mixtral_8x7b_w1",
+                             "moe:deepseek_v2_lite_up"],
+                    help="print one extra line of the default run alone (for profiling), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the layer's multi-GPU "
@@ -436,6 +440,9 @@ def main():
 
     if args.layer:
         run_layer(dev, args.layer, args.tokens or 16, args.steps, args.warmup)
+        return
+    if args.line:
+        run_line(dev, args.line, args.steps, args.warmup)
         return
     if args.fused:
         run_fused(dev, args.group, args.tokens)
@@ -523,6 +530,29 @@ def main():
     if not checks["ok"]:
         print(f"bench.py: the timed run failed its checks: {checks}", file=sys.stderr)
         sys.exit(1)
+
+
+def run_line(dev, line, steps, warmup):
+    """One extra line of the default run alone, with the given step counts."""
+    import sparse_rank_linear_amd as srl
+    from sparse_rank_linear_amd import synth
+
+    if line.startswith("moe:"):
+        print(json.dumps(moe_line(dev, line[4:], steps=steps, warmup=warmup)), flush=True)
+        return
+    if line in ("prefill", "l70b_up_s50"):
+        name, label = (("llama7b_mlp_up_11008", "llama7b_mlp_up_11008x4096_prefill") if line == "prefill"
+                       else ("l70b_up_s50", "l70b_up_28672x8192_s50_m8192"))
+        peaks = {"mfma_bf16_TFLOPs": MFMA_BF16_PEAK_TFLOPS}
+        print(json.dumps(many_token_line(dev, name, label, peaks, steps=steps, warmup=warmup)), flush=True)
+        return
+    wl = synth.WORKLOADS["llama7b_attn_4096"]
+    inp = synth.make_inputs(wl, with_x=False)
+    layer, _ = srl.encode(_dev_bits(inp.W, dev), wl.n_keep, wl.r_svd, [_dev_bits(a, dev) for a in inp.lora_A],
+                          [_dev_bits(b, dev) for b in inp.lora_B])
+    fn = nf4_line if line == "nf4" else backward_line
+    kw = {"M": 2048} if line == "backward" else {}
+    print(json.dumps(fn(dev, layer, wl, steps=steps, warmup=warmup, **kw)), flush=True)
 
 
 def nf4_line(dev, layer, wl, steps, warmup):
