@@ -7,7 +7,8 @@
 //   dB_cat = (X A_cat)^T dY.
 // dX is a forward of the transposed layer (W_s^T with adapters B_cat^T,
 // A_cat^T), run by the forward kernels on a column-major copy of W_s's
-// encoding built here once; the adapter gradients contract over the tokens.
+// encoding built here once; the adapter gradients contract over the tokens
+// straight from the token-major X, dY, G and T (tiles transposed in LDS).
 //
 // Transposed encoding (W_s^T, K rows of N columns), built tile-parallel:
 //   1. rowpre[n][w]: kept values of row n before bitmap word w;
@@ -135,34 +136,52 @@ __global__ __launch_bounds__(256) void transpose_bf16_tiles(const uint16_t* src,
   }
 }
 
-// C[p][q] += sum over k in split s of A[p][k] B[q][k] (bf16, k contiguous,
-// row strides lda / ldb, k range padded with zeros to a multiple of 8),
-// fp32 partials part[s][P][Q].  Workgroup: 64 x 64 outputs, 4 waves of
-// 32 x 32 (2 x 2 MFMA tiles), operands loaded straight into MFMA layout.
-__global__ __launch_bounds__(256) void gemm_nt_kernel(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
-                                                      int64_t P, int64_t Q, int64_t Kc, int64_t k_split,
-                                                      float* part) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Token contraction: part[split][p][q] = sum over rows m of the split of
+// A[m][p] B[m][q] (bf16, rows of lda / ldb elements, fp32 products).  A
+// workgroup owns 64 x 64 outputs, 4 waves of 32 x 32 (2 x 2 MFMA tiles);
+// per 32 rows it loads both 32 x 64 tiles with 16-byte loads along p / q and
+// writes them to LDS transposed (k = m contiguous), which is the MFMA
+// operand layout.  Loads read up to pa / qa columns (multiples of 8; the
+// caller guarantees they exist, zero past P / Q).
+constexpr int kTnRowPad = 40;  // LDS row: 32 rows of m + 8 (fewer bank conflicts)
+__global__ __launch_bounds__(256) void gemm_tn_kernel(const uint16_t* A, int64_t lda, int64_t pa, const uint16_t* B,
+                                                      int64_t ldb, int64_t qa, int64_t P, int64_t Q, int64_t M,
+                                                      int64_t m_split, float* part) {
+  __shared__ __attribute__((aligned(16))) uint16_t at[64 * kTnRowPad];
+  __shared__ __attribute__((aligned(16))) uint16_t bt[64 * kTnRowPad];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, g = lane >> 4;
-  const int64_t p0 = (int64_t)blockIdx.y * 64 + (wave >> 1) * 32;
-  const int64_t q0 = (int64_t)blockIdx.x * 64 + (wave & 1) * 32;
-  const int64_t kb = (int64_t)blockIdx.z * k_split, ke = min(Kc, kb + k_split);
+  const int64_t p0 = (int64_t)blockIdx.y * 64, q0 = (int64_t)blockIdx.x * 64;
+  const int64_t mb = (int64_t)blockIdx.z * m_split, me = min(M, mb + m_split);
+  const int wp = (wave >> 1) * 32, wq = (wave & 1) * 32;
+  // staging role: row r = tid / 8 of the 32, 8 columns at c = 8 (tid % 8)
+  const int r = tid >> 3, c = 8 * (tid & 7);
   f32x4_t acc[2][2] = {{zero4(), zero4()}, {zero4(), zero4()}};
-  for (int64_t k = kb; k < ke; k += 32) {
-    const int64_t kk = k + 8 * g;
+  for (int64_t m0 = mb; m0 < me; m0 += 32) {
+    const int64_t m = m0 + r;
+    const u32x4_t va = (m < me && p0 + c < pa) ? load16(A + m * lda + p0 + c) : zero_u4();
+    const u32x4_t vb = (m < me && q0 + c < qa) ? load16(B + m * ldb + q0 + c) : zero_u4();
+    __syncthreads();  // (the previous step's operand reads are done)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      at[(c + 2 * e) * kTnRowPad + r] = (uint16_t)va[e];
+      at[(c + 2 * e + 1) * kTnRowPad + r] = (uint16_t)(va[e] >> 16);
+      bt[(c + 2 * e) * kTnRowPad + r] = (uint16_t)vb[e];
+      bt[(c + 2 * e + 1) * kTnRowPad + r] = (uint16_t)(vb[e] >> 16);
+    }
+    __syncthreads();
     u32x4_t a[2], b[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int64_t p = p0 + 16 * t + i, q = q0 + 16 * t + i;
-      a[t] = (p < P && kk < ke) ? load16(A + p * lda + kk) : zero_u4();
-      b[t] = (q < Q && kk < ke) ? load16(B + q * ldb + kk) : zero_u4();
+      a[t] = *reinterpret_cast<const u32x4_t*>(&at[(wp + 16 * t + i) * kTnRowPad + 8 * g]);
+      b[t] = *reinterpret_cast<const u32x4_t*>(&bt[(wq + 16 * t + i) * kTnRowPad + 8 * g]);
     }
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
       for (int y = 0; y < 2; ++y) acc[x][y] = mfma_16x16x32(a[x], b[y], acc[x][y]);
   }
-  // lane holds C[p0 + 16x + 4g + e][q0 + 16y + i]
+  // lane holds C[p0 + wp + 16x + 4g + e][q0 + wq + 16y + i]
   float* out = part + (size_t)blockIdx.z * P * Q;
 #pragma unroll
   for (int x = 0; x < 2; ++x)
@@ -170,7 +189,7 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(const uint16_t* A, int64_t
     for (int y = 0; y < 2; ++y)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int64_t p = p0 + 16 * x + 4 * g + e, q = q0 + 16 * y + i;
+        const int64_t p = p0 + wp + 16 * x + 4 * g + e, q = q0 + wq + 16 * y + i;
         const float v = acc[x][y][e];
         if (p < P && q < Q) out[p * Q + q] = v;
       }
@@ -216,20 +235,21 @@ hipError_t launch_transpose_bf16(const uint16_t* src, int64_t R, int64_t C, int6
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t P, int64_t Q,
-                          int64_t Kc, int splits, float* part, float* out, hipStream_t s) {
+hipError_t launch_gemm_tn(const uint16_t* A, int64_t lda, int64_t pa, const uint16_t* B, int64_t ldb, int64_t qa,
+                          int64_t P, int64_t Q, int64_t M, int splits, float* part, float* out, hipStream_t s) {
   if (P == 0 || Q == 0) return hipSuccess;
   const int64_t n = P * Q;
-  if (Kc <= 0) {  // (an empty sum: zeros)
+  if (M <= 0) {  // (an empty sum: zeros)
     hipLaunchKernelGGL(sum_parts_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, 0, n, out);
     return hipGetLastError();
   }
-  const int64_t k_split = ((Kc + splits - 1) / splits + 31) / 32 * 32;
-  splits = (int)((Kc + k_split - 1) / k_split);
+  const int64_t m_split = ((M + splits - 1) / splits + 31) / 32 * 32;
+  splits = (int)((M + m_split - 1) / m_split);
   if (splits < 1) splits = 1;
   const dim3 grid((unsigned)((Q + 63) / 64), (unsigned)((P + 63) / 64), (unsigned)splits);
   // (one split: straight into the output)
-  hipLaunchKernelGGL(gemm_nt_kernel, grid, dim3(256), 0, s, A, lda, B, ldb, P, Q, Kc, k_split, splits == 1 ? out : part);
+  hipLaunchKernelGGL(gemm_tn_kernel, grid, dim3(256), 0, s, A, lda, pa, B, ldb, qa, P, Q, M, m_split,
+                     splits == 1 ? out : part);
   if (splits > 1)
     hipLaunchKernelGGL(sum_parts_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, splits, n, out);
   return hipGetLastError();

@@ -448,44 +448,38 @@ int transpose_check(const salr_layer_t* L) {
   return SALR_OK;
 }
 
-// Gradient-GEMM K splits over M tokens: about kGemmItems workgroups, each
-// split at least 256 tokens.
+// Gradient-GEMM splits over the M tokens: about kGemmItems workgroups, each
+// split at least 128 tokens.
 constexpr int64_t kGemmItems = 512;
 int gemm_splits(int64_t P, int64_t Q, int64_t M) {
   const int64_t tiles = cdiv(P, 64) * cdiv(Q, 64);
-  const int64_t s = std::min<int64_t>(std::max<int64_t>(1, kGemmItems / std::max<int64_t>(tiles, 1)), cdiv(M, 256));
+  const int64_t s = std::min<int64_t>(std::max<int64_t>(1, kGemmItems / std::max<int64_t>(tiles, 1)), cdiv(M, 128));
   return (int)std::max<int64_t>(s, 1);
 }
 
 // Backward workspace: the forward workspace of the transposed layer first
 // (its counter header at offset 0), then the transposed adapters, the
-// low-rank activations and their token-major transposes, and the gradient
-// GEMMs' split partials.  Every region grows with M.
+// low-rank activations G and T (bf16 [M][r_pad]) and the gradient GEMMs'
+// split partials.  Every region grows with M.
 struct BwdLayout {
   int r_pad;
-  int64_t m8;
   int splits_a, splits_b;
-  size_t fwd, bt, at_, tpart, g16, t16, xt, dyt, gt, tt, part, total;
+  size_t fwd, bt, at_, tpart, g16, t16, part, total;
 };
 BwdLayout bwd_layout(int64_t N, int64_t K, int32_t n_keep_t, int32_t r_cat, int64_t M) {
   BwdLayout B{};
   B.r_pad = (int)align_up((size_t)r_cat, 16);
-  B.m8 = (int64_t)align_up((size_t)M, 8);
   B.fwd = fwd_layout(K, N, n_keep_t, r_cat, M).total;
   size_t off = align_up(B.fwd, 256);
   B.bt = off;   off = align_up(off + (size_t)r_cat * N * 2, 256);
   B.at_ = off;  off = align_up(off + (size_t)K * r_cat * 2, 256) + kValuesPad;
   B.tpart = off;
-  B.g16 = B.t16 = B.xt = B.dyt = B.gt = B.tt = B.part = off;
+  B.g16 = B.t16 = B.part = off;
   if (r_cat > 0 && M > 0) {
     const size_t rows = (size_t)std::max<int64_t>(64 * 256, cdiv(M, 64) * 64);
     off = align_up(off + rows * B.r_pad * 4, 256);
     B.g16 = off;  off = align_up(off + (size_t)M * B.r_pad * 2, 256);
     B.t16 = off;  off = align_up(off + (size_t)M * B.r_pad * 2, 256);
-    B.xt = off;   off = align_up(off + (size_t)K * B.m8 * 2, 256);
-    B.dyt = off;  off = align_up(off + (size_t)N * B.m8 * 2, 256);
-    B.gt = off;   off = align_up(off + (size_t)r_cat * B.m8 * 2, 256);
-    B.tt = off;   off = align_up(off + (size_t)r_cat * B.m8 * 2, 256);
     B.splits_a = gemm_splits(r_cat, K, M);
     B.splits_b = gemm_splits(N, r_cat, M);
     B.part = off;
@@ -581,8 +575,8 @@ int salr_linear_backward(const salr_layer_t* L, const salr_layer_t* LT, const ui
   const int64_t N = L->N, K = L->K;
   if (M == 0) {
     // an empty token sum: zero adapter gradients (no dX rows)
-    if (r > 0 && (salr::launch_gemm_nt(nullptr, 0, nullptr, 0, r, K, 0, 1, nullptr, dA, s) != hipSuccess ||
-                  salr::launch_gemm_nt(nullptr, 0, nullptr, 0, N, r, 0, 1, nullptr, dB, s) != hipSuccess))
+    if (r > 0 && (salr::launch_gemm_tn(nullptr, 0, 0, nullptr, 0, 0, r, K, 0, 1, nullptr, dA, s) != hipSuccess ||
+                  salr::launch_gemm_tn(nullptr, 0, 0, nullptr, 0, 0, N, r, 0, 1, nullptr, dB, s) != hipSuccess))
       return SALR_ERR_HIP;
     return SALR_OK;
   }
@@ -600,7 +594,8 @@ int salr_linear_backward(const salr_layer_t* L, const salr_layer_t* LT, const ui
     if (e != SALR_OK) return e;
   }
   if (r == 0) return SALR_OK;
-  // G = dY B_cat^T and T = X A_cat, each rounded to bf16 [M][r_pad]
+  // G = dY B_cat^T and T = X A_cat, each rounded to bf16 [M][r_pad] (ranks
+  // past r_cat zero)
   const auto lowrank = [&](const uint16_t* in, const uint16_t* rows, int64_t Kin, uint16_t* out16) {
     LowRankTArgs t{};
     t.X = in;
@@ -616,24 +611,24 @@ int salr_linear_backward(const salr_layer_t* L, const salr_layer_t* LT, const ui
     t.splits = (int32_t)cdiv(Kin, t.k_chunk);
     return salr::launch_lowrank_t(t, s) == hipSuccess;
   };
-  uint16_t* g16 = at<uint16_t>(ws, B.g16);
-  uint16_t* t16 = at<uint16_t>(ws, B.t16);
-  if (!lowrank(dY, bt, N, g16) || !lowrank(X, L->a_cat, K, t16)) return SALR_ERR_HIP;
-  // token-major operands of the two gradient GEMMs (rows zero-padded to m8)
-  uint16_t* xt = at<uint16_t>(ws, B.xt);
-  uint16_t* dyt = at<uint16_t>(ws, B.dyt);
-  uint16_t* gt = at<uint16_t>(ws, B.gt);
-  uint16_t* tt = at<uint16_t>(ws, B.tt);
-  if (salr::launch_transpose_bf16(X, M, K, K, xt, B.m8, s) != hipSuccess ||
-      salr::launch_transpose_bf16(dY, M, N, N, dyt, B.m8, s) != hipSuccess ||
-      salr::launch_transpose_bf16(g16, M, r, B.r_pad, gt, B.m8, s) != hipSuccess ||
-      salr::launch_transpose_bf16(t16, M, r, B.r_pad, tt, B.m8, s) != hipSuccess)
+  // (with dX over many rows the forward of the transposed layer has just
+  // made G the same way, as its own X A_cat: it is read from its workspace)
+  const uint16_t* g16 = at<uint16_t>(ws, B.g16);
+  if (dX && M > kSmallM) {
+    g16 = at<uint16_t>(ws, fwd_layout(K, N, LT->n_keep, r, M).t16);
+  } else if (!lowrank(dY, bt, N, at<uint16_t>(ws, B.g16))) {
     return SALR_ERR_HIP;
+  }
+  uint16_t* t16 = at<uint16_t>(ws, B.t16);
+  if (!lowrank(X, L->a_cat, K, t16)) return SALR_ERR_HIP;
   float* part = at<float>(ws, B.part);
+  const int64_t r8 = (int64_t)align_up((size_t)r, 8);  // (<= r_pad, zeros past r)
   // dA_cat (stored [r][K]) [j][k] = sum_m G[m][j] X[m][k]
-  if (salr::launch_gemm_nt(gt, B.m8, xt, B.m8, r, K, M, B.splits_a, part, dA, s) != hipSuccess) return SALR_ERR_HIP;
+  if (salr::launch_gemm_tn(g16, B.r_pad, r8, X, K, K, r, K, M, B.splits_a, part, dA, s) != hipSuccess)
+    return SALR_ERR_HIP;
   // dB_cat (stored [N][r]) [n][j] = sum_m dY[m][n] T[m][j]
-  if (salr::launch_gemm_nt(dyt, B.m8, tt, B.m8, N, r, M, B.splits_b, part, dB, s) != hipSuccess) return SALR_ERR_HIP;
+  if (salr::launch_gemm_tn(dY, N, N, t16, B.r_pad, r8, N, r, M, B.splits_b, part, dB, s) != hipSuccess)
+    return SALR_ERR_HIP;
   return SALR_OK;
 }
 

@@ -198,11 +198,12 @@ hipError_t launch_transpose_scatter(const uint64_t* masks, const uint16_t* value
 // dst[c][r] = src[r][c] (bf16), dst rows of ld_dst >= R entries, zero past R.
 hipError_t launch_transpose_bf16(const uint16_t* src, int64_t R, int64_t C, int64_t ld_src, uint16_t* dst,
                                  int64_t ld_dst, hipStream_t s);
-// out[p][q] = sum_k A[p][k] B[q][k] (bf16 rows, k contiguous, zero-padded to
-// a multiple of 8), fp32, the k range cut into `splits` partials (part:
-// splits * P * Q floats) summed in order.
-hipError_t launch_gemm_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t P, int64_t Q,
-                          int64_t Kc, int splits, float* part, float* out, hipStream_t s);
+// out[p][q] = sum over m < M of A[m][p] B[m][q] (bf16, row strides lda /
+// ldb; up to pa / qa columns readable, multiples of 8, zero past P / Q),
+// fp32, the rows cut into `splits` partials (part: splits * P * Q floats)
+// summed in order.
+hipError_t launch_gemm_tn(const uint16_t* A, int64_t lda, int64_t pa, const uint16_t* B, int64_t ldb, int64_t qa,
+                          int64_t P, int64_t Q, int64_t M, int splits, float* part, float* out, hipStream_t s);
 
 // ----------------------------------------------------------------------------
 // Grouped (mixture-of-experts) forward: E experts stacked at fixed strides
