@@ -419,26 +419,48 @@ __global__ __launch_bounds__(kTThreads) void lowrank_t_kernel(LowRankTArgs a) {
 #pragma unroll
   for (int j = 0; j < kMaxRTiles; ++j) acc[j] = zero4();
 
-  for (int kt = k0; kt < k1; kt += 64) {
-    // stage A_cat[0..r_pad)[kt .. kt+64)
-    for (int c = tid; c < a.r_pad * 8; c += kTThreads) {
+  // The A_cat slice and the X operands of the next 64-column tile are
+  // requested before this tile's MFMAs (registers), so each tile waits for
+  // one load round trip less.
+  constexpr int kPer = kMaxRTiles * 16 * 8 / kTThreads;  // A_cat chunks per thread, at most
+  u32x4_t an[kPer], xn[2];
+  const auto load_tile = [&](int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int c = tid + kTThreads * u;
       const int r = c >> 3, k = kt + 8 * (c & 7);
-      const u32x4_t v = (r < a.r_cat && k < k1) ? load16(a.a_cat + (size_t)r * a.K + k) : zero_u4();
-      *reinterpret_cast<u32x4_t*>(&al[r * kLdsRow + (c & 7) * 4]) = v;
+      an[u] = (r < a.r_cat && k < k1) ? load16(a.a_cat + (size_t)r * a.K + k) : zero_u4();
     }
-    __syncthreads();
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int k = kt + 32 * s + 8 * g;
-      const u32x4_t xv = (token < a.M && k < k1) ? load16(a.X + (size_t)token * a.K + k) : zero_u4();
+      xn[s] = (token < a.M && k < k1) ? load16(a.X + (size_t)token * a.K + k) : zero_u4();
+    }
+  };
+  if (k0 < k1) load_tile(k0);
+  for (int kt = k0; kt < k1; kt += 64) {
+    u32x4_t av[kPer], xv[2];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) av[u] = an[u];
+    xv[0] = xn[0];
+    xv[1] = xn[1];
+    if (kt + 64 < k1) load_tile(kt + 64);
+    __syncthreads();  // (the previous tile's reads of al are done)
+    // stage A_cat[0..r_pad)[kt .. kt+64)
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int c = tid + kTThreads * u;
+      if ((c >> 3) < a.r_pad) *reinterpret_cast<u32x4_t*>(&al[(c >> 3) * kLdsRow + (c & 7) * 4]) = av[u];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int j = 0; j < kMaxRTiles; ++j)
         if (j < rt) {
-          const u32x4_t av = *reinterpret_cast<const u32x4_t*>(&al[(16 * j + i) * kLdsRow + s * 16 + g * 4]);
-          acc[j] = mfma_16x16x32(av, xv, acc[j]);
+          const u32x4_t w = *reinterpret_cast<const u32x4_t*>(&al[(16 * j + i) * kLdsRow + s * 16 + g * 4]);
+          acc[j] = mfma_16x16x32(w, xv[s], acc[j]);
         }
-    }
-    __syncthreads();
   }
 
   // lane holds T[token][16j + 4g + e]
