@@ -496,7 +496,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "fwd_small_kernel", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic()},
-        "encode": {"seconds": round(encode_s, 4), "iters": 24, "oversample": 32, "call": "second"},
+        "encode": {"seconds": round(encode_s, 4), "iters": 40, "oversample": 32, "call": "second"},
         "checks": {k: v for k, v in checks.items()},
     }
     if not args.no_extra:

@@ -125,7 +125,7 @@ typedef struct salr_sizes {
  * defaults below).  The SVD is computed by randomized subspace iteration:
  * `oversample` extra basis vectors (default 32, at most 64; the basis width
  * r_svd + oversample is capped at min(N, K, 320)), `iters` power iterations
- * (default 24, at most 1000), starting block drawn from a counter-based
+ * (default 40, at most 1000), starting block drawn from a counter-based
  * generator keyed by `seed` (default 0).  encode_ws_bytes from
  * salr_query_sizes covers every allowed oversample. */
 typedef struct salr_encode_opts {

@@ -374,7 +374,7 @@ def _encode_into(desc, W, n_keep, r_svd, lora_A, lora_B, oversample, iters, seed
     r_arr = (C.c_int32 * max(nl, 1))(*ranks)
     opts = None
     if oversample is not None or iters is not None or seed:
-        opts = salr_encode_opts_t(32 if oversample is None else oversample, 24 if iters is None else iters, seed)
+        opts = salr_encode_opts_t(32 if oversample is None else oversample, 40 if iters is None else iters, seed)
     sig = (C.c_double * max(r_svd, 1))()
     st = _lib().salr_encode(
         C.c_void_p(_dev_ptr(W, "W")), N, K, n_keep, r_svd, nl,

@@ -28,7 +28,7 @@ constexpr int64_t kFillWgs = 256;               // few-row consumers wanted to f
 constexpr size_t kValuesPad = 256;   // tail bytes kernels may over-read
 constexpr int32_t kDefaultOversample = 32;
 constexpr int32_t kMaxOversample = 64;
-constexpr int32_t kDefaultIters = 24;
+constexpr int32_t kDefaultIters = 40;
 constexpr int32_t kMaxIters = 1000;
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
