@@ -54,12 +54,18 @@ constexpr int kMaxWaveWords = kMaxSteps / 2;           // bitmap words per wave
 // Bitmap words per row in LDS: one word of padding puts the 16 rows' words
 // in 16 distinct bank pairs.
 constexpr int kMaskRowWords = kMaxRangeCols / 64 + 1;
+constexpr int kPrefixReads = (kMaskRowWords - 1) / 4;  // bitmap words per lane for a row's prefix
 constexpr int kPollBatch = 8;
 constexpr int kBatch = 4;  // decode steps whose LDS reads are issued together
 
-// LDS carve-up (dynamic shared memory): a fixed part, then the values area.
-struct alignas(16) Lds {
+// LDS carve-up (dynamic shared memory): the selector table, the values area
+// (at a small constant offset, which the decode's reads take as an immediate
+// offset), the rest of the fixed part, then the tile's B_cat rows.
+struct alignas(16) LdsHead {
   u32x2_t lut[16];
+  u32x4_t zero16;  // sixteen zero bytes (reads outside an operand)
+};
+struct alignas(16) Lds {
   float levels[16];        // NF4 levels (NF4 layers)
   uint32_t seg[kRows][2];  // per-row range of kept-value indices (within the row)
   int64_t vorg[kRows];     // global value index = LDS value slot + vorg (per row)
@@ -72,11 +78,39 @@ template <bool kOneRound>
 constexpr int piece_cols() { return kOneRound ? 512 : 1024; }
 template <bool kOneRound>
 constexpr int piece_steps() { return piece_cols<kOneRound>() / 32 / kWaves; }
-constexpr int kFinBatch = 4;                      // pieces requested together when finishing T
+constexpr int kFinBatch = 8;
+constexpr int kLrBatch = 4;                       // low-rank chunks whose operands are read together                      // pieces requested together when finishing T
 constexpr int kMaxLoadRows = kRows / kWaves;      // rows per load-issuing wave
-static_assert(sizeof(Lds) % 16 == 0, "values area must stay 16-byte aligned");
+static_assert(sizeof(LdsHead) % 16 == 0 && sizeof(Lds) % 16 == 0, "areas must stay 16-byte aligned");
 static_assert(offsetof(Lds, masks) % 16 == 0 && sizeof(Lds::masks) >= 8 * 1024,
               "the T operands of up to 256 ranks live in the bitmap-word area");
+
+// Decode reads address LDS with plain byte offsets: the dynamic area starts at
+// byte 0 (these kernels declare no static LDS; the kernel checks), so the
+// constant part of an address folds into the read's immediate offset.
+typedef __attribute__((address_space(3))) const uint32_t lds_u32_t;
+typedef __attribute__((address_space(3))) const u32x2_t lds_u32x2_t;
+constexpr uint32_t kValsOff = sizeof(LdsHead);  // byte offset of the values area
+// The 4-value window at value index idx of the values area (see
+// lds_window_words) and the selector pair of nibble q.
+__device__ __forceinline__ Window3 vals_window(uint32_t idx) {
+  lds_u32_t* w = reinterpret_cast<lds_u32_t*>((size_t)(kValsOff + ((idx >> 1) << 2)));
+  return Window3{w[0], w[1], w[2]};
+}
+__device__ __forceinline__ u32x2_t lut_entry(uint32_t q) {
+  return *reinterpret_cast<lds_u32x2_t*>((size_t)(offsetof(LdsHead, lut) + (q << 3)));
+}
+
+// Make the compiler hold every word in a register here (one wait for all the
+// reads before it; see the decode).
+__device__ __forceinline__ void pin_words(uint64_t (&p)[kPrefixReads], uint64_t (&m)[kMaxWaveWords]) {
+  static_assert(kPrefixReads == 16 && kMaxWaveWords == 8, "operand list below");
+  asm volatile(""
+               : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]), "+v"(p[3]), "+v"(p[4]), "+v"(p[5]), "+v"(p[6]), "+v"(p[7]),
+                 "+v"(p[8]), "+v"(p[9]), "+v"(p[10]), "+v"(p[11]), "+v"(p[12]), "+v"(p[13]), "+v"(p[14]),
+                 "+v"(p[15]), "+v"(m[0]), "+v"(m[1]), "+v"(m[2]), "+v"(m[3]), "+v"(m[4]), "+v"(m[5]), "+v"(m[6]),
+                 "+v"(m[7]));
+}
 
 __device__ __forceinline__ u32x4_t load_x_frag(const uint16_t* X, int M, int K, int m, int col) {
   if (m < M && col < K) return load16(X + (size_t)m * K + col);
@@ -234,8 +268,9 @@ template <bool kOneRound, bool kWin, bool kNF4>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void fwd_small_kernel(SmallFwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  Lds& L = *reinterpret_cast<Lds*>(smem);
-  uint32_t* const vals = reinterpret_cast<uint32_t*>(smem + sizeof(Lds));
+  LdsHead& H = *reinterpret_cast<LdsHead*>(smem);
+  uint32_t* const vals = reinterpret_cast<uint32_t*>(smem + sizeof(LdsHead));
+  Lds& L = *reinterpret_cast<Lds*>(smem + sizeof(LdsHead) + a.vals_bytes);
   f32x4_t* const red = reinterpret_cast<f32x4_t*>(vals);
   // This workgroup's T chunks as MFMA operands [chunk][64 lanes] (bf16
   // pairs) reuse the bitmap-word area: they are written only after the
@@ -243,10 +278,15 @@ void fwd_small_kernel(SmallFwdArgs a) {
   // words in registers (so two workgroups with 112 adapter ranks still share
   // a CU).  After the values area: the tile's B_cat rows [16][r_cat].
   u32x4_t* const tl = reinterpret_cast<u32x4_t*>(L.masks);
-  uint16_t* const bl = reinterpret_cast<uint16_t*>(smem + sizeof(Lds) + a.vals_bytes);
+  uint16_t* const bl = reinterpret_cast<uint16_t*>(smem + sizeof(LdsHead) + a.vals_bytes + sizeof(Lds));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  // (the decode's reads assume the dynamic area at LDS byte 0)
+  if ((uint32_t)(size_t)(__attribute__((address_space(3))) unsigned char*)smem != 0u) {
+    if (tid == 0) store_coherent(a.err, 2u);
+    return;
+  }
   const int i = lane & 15, g = lane >> 4;
   const uint32_t n_wgs = gridDim.x;
   const bool talk = a.splits > 1 || a.r_cat > 0;  // any cross-workgroup data?
@@ -304,7 +344,8 @@ void fwd_small_kernel(SmallFwdArgs a) {
     // first)
     if (kOneRound) __builtin_amdgcn_s_setprio(3);
     load_x_frags();
-    if (tid < 16) L.lut[tid] = nibble_selectors(tid);
+    if (tid < 16) H.lut[tid] = nibble_selectors(tid);
+    if (tid == 16) H.zero16 = zero_u4();
     if (kNF4 && tid >= 64 && tid < 80) L.levels[tid - 64] = a.levels[tid - 64];
     const int lw = wave, lws = kWaves;
     // Bitmap words of the range, per row 2*nwords dwords direct to LDS; rows
@@ -405,11 +446,6 @@ void fwd_small_kernel(SmallFwdArgs a) {
   // tile is held up by it.
   if (producer) {
     if (tid == 0) drawn = draw_ticket(a.tickets, blockIdx.x, n_wgs);
-    // With all weight workgroups resident, a producer shares its CU with one
-    // of them, whose loads it would otherwise delay while they are issued:
-    // start later (psleep x 64 clocks; T is needed only after the decode).
-    if (kOneRound)
-      for (int k = 0; k < a.psleep; ++k) __builtin_amdgcn_s_sleep(1);
     const int piece = c;
     const int j = piece / a.t_pieces, kp = piece % a.t_pieces;
     const int rank = 16 * j + i;
@@ -499,24 +535,28 @@ void fwd_small_kernel(SmallFwdArgs a) {
   {
     const bool live = i < rows_here;
     const uint64_t* mrow = &L.masks[i * kMaskRowWords];
-    const uint16_t* vals16 = reinterpret_cast<const uint16_t*>(vals);
     // LDS slot of the row's first value in the range, plus the kept bits of
     // the range before this wave's first word
     const uint32_t base = live ? (uint32_t)((row0 + i) * a.n_keep + L.seg[i][0] - L.vorg[i]) : 0u;
     const int w0 = s0 >> 1;
-    uint32_t part = 0;
-    // (all reads issued together: clamped in-row indices, masked counts)
+    // Every bitmap read of the prefix and of this wave's words is issued
+    // before any is used (clamped in-row indices), and the words are then
+    // pinned in registers: a count that uses its word only under a lane
+    // condition is otherwise compiled as a branch around the read and its
+    // wait, one LDS round trip per word.
+    uint64_t pm[kPrefixReads], mw[kMaxWaveWords];
 #pragma unroll
-    for (int k = 0; k < (kMaskRowWords - 1) / 4; ++k) {
-      const int w = g + 4 * k;
-      const uint64_t m = mrow[min(w, kMaskRowWords - 1)];
-      part += w < w0 ? (uint32_t)__popcll(m) : 0u;
-    }
+    for (int k = 0; k < kPrefixReads; ++k) pm[k] = mrow[min(g + 4 * k, kMaskRowWords - 1)];
+#pragma unroll
+    for (int q = 0; q < kMaxWaveWords; ++q) mw[q] = mrow[min(w0 + q, kMaskRowWords - 1)];
+    pin_words(pm, mw);
+    uint32_t part = 0;
+#pragma unroll
+    for (int k = 0; k < kPrefixReads; ++k) part += g + 4 * k < w0 ? (uint32_t)__popcll(pm[k]) : 0u;
     part += __shfl_xor(part, 16);
     part += __shfl_xor(part, 32);
-    uint64_t mw[kMaxWaveWords];
 #pragma unroll
-    for (int q = 0; q < kMaxWaveWords; ++q) mw[q] = (2 * q < spw && w0 + q < nwords) ? mrow[w0 + q] : 0ull;
+    for (int q = 0; q < kMaxWaveWords; ++q) mw[q] = (2 * q < spw && w0 + q < nwords) ? mw[q] : 0ull;
     uint32_t run = base + part;
     const uint32_t below = (1u << (8 * g)) - 1u;
 #pragma unroll
@@ -533,10 +573,10 @@ void fwd_small_kernel(SmallFwdArgs a) {
           const uint32_t lo = byte & 15u, hi = byte >> 4;
           ia[b] = run + __popc(h & below);
           ib[b] = ia[b] + __popc(lo);
-          wa[b] = lds_window_words(vals16, ia[b]);
-          wb[b] = lds_window_words(vals16, ib[b]);
-          la[b] = L.lut[lo];
-          lb[b] = L.lut[hi];
+          wa[b] = vals_window(ia[b]);
+          wb[b] = vals_window(ib[b]);
+          la[b] = lut_entry(lo);
+          lb[b] = lut_entry(hi);
           run += __popc(h);
         }
 #pragma unroll
@@ -598,31 +638,43 @@ void fwd_small_kernel(SmallFwdArgs a) {
   for (int w = 0; w < kWaves - 1; ++w) acc += red[w * 64 + lane];
 
   // Low-rank term for this workgroup's chunks: acc += B_cat^T[rows, chunk]
-  // T^T[chunk, :], as extra K steps (T already rounded to bf16).
-  for (int k = 0; k < n_own; ++k) {
-    const int rb = 32 * (clo + rng + k * a.splits) + 8 * g;
-    u32x4_t wv;
-    if (kWin) {
-      // eight ranks in one aligned 16-byte read (ranks outside the tile's
-      // block: zero)
-      const int rr = rb - rlo;
-      wv = (i < rows_here && rr >= 0 && rr < rn) ? *reinterpret_cast<const u32x4_t*>(bl + i * bstride + rr)
-                                                  : zero_u4();
-    } else if (a.r_cat % 8 == 0) {
-      // eight ranks in one aligned 16-byte read (ranks past r_cat: zero)
-      wv = (i < rows_here && rb < a.r_cat) ? *reinterpret_cast<const u32x4_t*>(bl + i * a.r_cat + rb) : zero_u4();
-    } else {
-      uint32_t w[4];
+  // T^T[chunk, :], as extra K steps (T already rounded to bf16).  The
+  // operands of kLrBatch chunks are read together; a read outside the tile's
+  // ranks or rows is pointed at the zero chunk instead of being skipped (a
+  // skipped read is compiled as a branch around the read and its wait).
+  for (int k0 = 0; k0 < n_own; k0 += kLrBatch) {
+    u32x4_t wv[kLrBatch], tv[kLrBatch];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int ra = rb + 2 * e;
-        const uint32_t lo = (i < rows_here && ra < a.r_cat) ? bl[i * a.r_cat + ra] : 0u;
-        const uint32_t hi = (i < rows_here && ra + 1 < a.r_cat) ? bl[i * a.r_cat + ra + 1] : 0u;
-        w[e] = lo | (hi << 16);
+    for (int b = 0; b < kLrBatch; ++b) {
+      const int k = min(k0 + b, n_own - 1);
+      const int rb = 32 * (clo + rng + k * a.splits) + 8 * g;
+      tv[b] = tl[k * 64 + lane];
+      if (kWin) {
+        // eight ranks in one aligned 16-byte read (ranks outside the tile's
+        // block: zero)
+        const int rr = rb - rlo;
+        wv[b] = *(i < rows_here && rr >= 0 && rr < rn ? reinterpret_cast<const u32x4_t*>(bl + i * bstride + rr)
+                                                       : &H.zero16);
+      } else if (a.r_cat % 8 == 0) {
+        // eight ranks in one aligned 16-byte read (ranks past r_cat: zero)
+        wv[b] = *(i < rows_here && rb < a.r_cat ? reinterpret_cast<const u32x4_t*>(bl + i * a.r_cat + rb)
+                                                 : &H.zero16);
+      } else {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ra = rb + 2 * e;
+          const uint16_t* zh = reinterpret_cast<const uint16_t*>(&H.zero16);
+          const uint32_t lo = *(i < rows_here && ra < a.r_cat ? bl + i * a.r_cat + ra : zh);
+          const uint32_t hi = *(i < rows_here && ra + 1 < a.r_cat ? bl + i * a.r_cat + ra + 1 : zh);
+          w[e] = lo | (hi << 16);
+        }
+        wv[b] = u32x4_t{w[0], w[1], w[2], w[3]};
       }
-      wv = u32x4_t{w[0], w[1], w[2], w[3]};
     }
-    acc = mfma_16x16x32(wv, tl[k * 64 + lane], acc);
+#pragma unroll
+    for (int b = 0; b < kLrBatch; ++b)
+      if (k0 + b < n_own) acc = mfma_16x16x32(wv[b], tv[b], acc);
   }
   if (a.splits > 1) {
     if (!reduce_parts(acc, a.ypart + (size_t)tile * a.splits * 256, a.splits, rng, &a.ycount[tile], tag, err,
@@ -630,12 +682,19 @@ void fwd_small_kernel(SmallFwdArgs a) {
       return;
   }
 
-  // lane holds Y^T[row0 + 4g + e][token i]
+  // lane holds Y^T[row0 + 4g + e][token i]: four consecutive outputs of
+  // token i, one 8-byte store when they are aligned and inside the layer
   if (i < a.M) {
+    const int64_t n0 = row0 + 4 * g;
+    uint16_t* yp = a.Y + (size_t)i * a.N + n0;
+    if (n0 + 3 < a.N && (reinterpret_cast<uintptr_t>(yp) & 7) == 0) {
+      const float v0 = acc[0], v1 = acc[1], v2 = acc[2], v3 = acc[3];  // (scalar copies: see reduce_parts)
+      *reinterpret_cast<u32x2_t*>(yp) = u32x2_t{(uint32_t)f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16),
+                                                (uint32_t)f32_to_bf16(v2) | ((uint32_t)f32_to_bf16(v3) << 16)};
+    } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t n = row0 + 4 * g + e;
-      if (n < a.N) a.Y[(size_t)i * a.N + n] = f32_to_bf16(acc[e]);
+      for (int e = 0; e < 4; ++e)
+        if (n0 + e < a.N) yp[e] = f32_to_bf16(acc[e]);
     }
   }
 }
@@ -649,7 +708,7 @@ size_t fwd_small_vals_bytes(int vcap) {
 }
 
 size_t fwd_small_lds_bytes(int vcap, int bl_bytes) {
-  return sizeof(Lds) + fwd_small_vals_bytes(vcap) + (size_t)bl_bytes;
+  return sizeof(LdsHead) + fwd_small_vals_bytes(vcap) + sizeof(Lds) + (size_t)bl_bytes;
 }
 
 template <bool kNF4>

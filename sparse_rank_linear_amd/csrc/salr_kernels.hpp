@@ -44,7 +44,6 @@ struct SmallFwdArgs {
   int32_t vals_bytes;      // LDS bytes of the values area
   int32_t tl_bytes;        // bytes of the T operands (r_pad / 32 chunks x 1 KB, in the bitmap-word area)
   int32_t bl_bytes;        // LDS bytes of the B_cat rows (16 * r_cat * 2, rounded up to 16)
-  int32_t psleep;          // one-round launches: producers' start delay in units of 64 clocks
   // fused layers (0 parts: one block of r_cat ranks): part p owns the row
   // tiles below part_tile_end[p] and the ranks [part_rank0[p], + part_nrank[p])
   int32_t nparts;
