@@ -57,6 +57,7 @@ constexpr int kMaskRowWords = kMaxRangeCols / 64 + 1;
 constexpr int kPrefixReads = (kMaskRowWords - 1) / 4;  // bitmap words per lane for a row's prefix
 constexpr int kPollBatch = 8;
 constexpr int kBatch = 4;  // decode steps whose LDS reads are issued together
+static_assert(kMaxSteps % kBatch == 0, "X operands are requested a batch at a time");
 
 // LDS carve-up (dynamic shared memory): the selector table, the values area
 // (at a small constant offset, which the decode's reads take as an immediate
@@ -332,18 +333,24 @@ void fwd_small_kernel(SmallFwdArgs a) {
   const int nwords = (ncols + 63) / 64;            // bitmap words in the range
   const int rows_here = (int)min<int64_t>(kRows, a.N - row0);
 
+  // X operands of this wave's steps: those of the first decode batch are
+  // requested with the weights, each later batch's at the start of the
+  // batch before it (so X is not in the way of the weight stream, and only
+  // two batches of it are held in registers).
   u32x4_t xf[kMaxSteps];
-  const auto load_x_frags = [&]() {
+  const auto load_x_batch = [&](int q0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < kMaxSteps; ++q)
+    for (int b = 0; b < kBatch; ++b) {
+      const int q = q0 + b;
       xf[q] = (q < spw) ? load_x_frag(a.X, a.M, a.K, i, col0 + 32 * (s0 + q) + 8 * g) : zero_u4();
+    }
   };
 
   if (!producer) {
     // (beside a T producer, this workgroup's waves take every issue slot
     // first)
     if (kOneRound) __builtin_amdgcn_s_setprio(3);
-    load_x_frags();
+    load_x_batch(0);
     if (tid < 16) H.lut[tid] = nibble_selectors(tid);
     if (tid == 16) H.zero16 = zero_u4();
     if (kNF4 && tid >= 64 && tid < 80) L.levels[tid - 64] = a.levels[tid - 64];
@@ -561,6 +568,7 @@ void fwd_small_kernel(SmallFwdArgs a) {
     const uint32_t below = (1u << (8 * g)) - 1u;
 #pragma unroll
     for (int q0 = 0; q0 < kMaxSteps; q0 += kBatch) {
+      if (q0 + kBatch < kMaxSteps) load_x_batch(q0 + kBatch);
       if (q0 < spw && s0 + q0 < nsteps) {
         Window3 wa[kBatch], wb[kBatch];
         uint32_t ia[kBatch], ib[kBatch];
