@@ -334,7 +334,7 @@ void fwd_small_kernel(SmallFwdArgs a) {
   const int rows_here = (int)min<int64_t>(kRows, a.N - row0);
 
   // X operands of this wave's steps: those of the first decode batch are
-  // requested with the weights, each later batch's at the start of the
+  // requested right after the weights, each later batch's at the start of the
   // batch before it (so X is not in the way of the weight stream, and only
   // two batches of it are held in registers).
   u32x4_t xf[kMaxSteps];
@@ -350,7 +350,6 @@ void fwd_small_kernel(SmallFwdArgs a) {
     // (beside a T producer, this workgroup's waves take every issue slot
     // first)
     if (kOneRound) __builtin_amdgcn_s_setprio(3);
-    load_x_batch(0);
     if (tid < 16) H.lut[tid] = nibble_selectors(tid);
     if (tid == 16) H.zero16 = zero_u4();
     if (kNF4 && tid >= 64 && tid < 80) L.levels[tid - 64] = a.levels[tid - 64];
@@ -437,6 +436,10 @@ void fwd_small_kernel(SmallFwdArgs a) {
                          (bbytes + 15) / 16, lw, lws, lane);
     }
   }
+
+  // (the first batch's X after the weights: it comes from L2, the weights
+  // from HBM)
+  if (!producer) load_x_batch(0);
 
   // ---------------- T pieces (producer workgroups)
   // Piece p = (rank tile j, K range kp) is T^T[16 ranks][16 tokens] summed
