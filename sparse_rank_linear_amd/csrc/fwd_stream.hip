@@ -140,16 +140,13 @@ __global__ __launch_bounds__(kSThreads) void fwd_stream_kernel(StreamFwdArgs a) 
     const int nwords = (ncols + 63) / 64;
     uint64_t* const mdst = reinterpret_cast<uint64_t*>(buf) + wave * kCMaskRow;
     uint32_t* const vdst = reinterpret_cast<uint32_t*>(buf + (size_t)kSRows * kCMaskRow * 8) + (size_t)wave * a.vcap * 4;
-    // bitmap words (no dependence on the table), X slices, B_cat operand
+    // bitmap words (no dependence on the table), B_cat operand
     if (live) {
       const uint32_t* msrc = reinterpret_cast<const uint32_t*>(a.masks + row * a.kw + c * kCWords);
       if (lane < 2 * nwords) __builtin_amdgcn_global_load_lds(msrc + lane, reinterpret_cast<uint32_t*>(mdst), 4, 0, 0);
     } else {
       for (int w = lane; w < 2 * kCMaskRow; w += 64) reinterpret_cast<uint32_t*>(mdst)[w] = 0u;
     }
-#pragma unroll
-    for (int s = 0; s < kCSteps; ++s)
-      xd[s] = load_x_frag_s(a.X, a.M, a.K, i, col0 + 32 * (wave * kCSteps + s) + 8 * g);
     if (nc > 1 && c == nc - 1) load_bc(t);
     // the row's kept values of the chunk: bounds from the table row
     if (c == 0) {
@@ -172,6 +169,10 @@ __global__ __launch_bounds__(kSThreads) void fwd_stream_kernel(StreamFwdArgs a) 
     } else {
       if (lane == 0) H.vbase[bsel][wave] = (uint32_t)(wave * a.vcap * 8);
     }
+    // X slices last: they come from L2, the values from HBM
+#pragma unroll
+    for (int s = 0; s < kCSteps; ++s)
+      xd[s] = load_x_frag_s(a.X, a.M, a.K, i, col0 + 32 * (wave * kCSteps + s) + 8 * g);
   };
 
   // ---- T pieces: workgroup p < n_pieces computes piece p = (rank tile j,
@@ -299,18 +300,24 @@ __global__ __launch_bounds__(kSThreads) void fwd_stream_kernel(StreamFwdArgs a) 
       const uint64_t* mrow = reinterpret_cast<const uint64_t*>(bcur) + i * kCMaskRow;
       const uint16_t* vals16 = reinterpret_cast<const uint16_t*>(bcur + (size_t)kSRows * kCMaskRow * 8);
       const int w0 = s0 >> 1;
-      uint32_t part = 0;
+      // every bitmap read is issued before any is used, and the prefix words
+      // are pinned in registers: a count that uses its word only under a lane
+      // condition is otherwise compiled as a branch around the read and its
+      // wait, one LDS round trip per word
+      uint64_t pm[kCWords / 4], mw[kCSteps / 2];
 #pragma unroll
-      for (int k = 0; k < kCWords / 4; ++k) {
-        const int w = g + 4 * k;
-        const uint64_t m = mrow[w];
-        part += w < w0 ? (uint32_t)__popcll(m) : 0u;
-      }
-      part += __shfl_xor(part, 16);
-      part += __shfl_xor(part, 32);
-      uint64_t mw[kCSteps / 2];
+      for (int k = 0; k < kCWords / 4; ++k) pm[k] = mrow[g + 4 * k];
 #pragma unroll
       for (int u = 0; u < kCSteps / 2; ++u) mw[u] = mrow[w0 + u];
+      static_assert(kCWords / 4 == 8, "operand list below");
+      asm volatile(""
+                   : "+v"(pm[0]), "+v"(pm[1]), "+v"(pm[2]), "+v"(pm[3]), "+v"(pm[4]), "+v"(pm[5]), "+v"(pm[6]),
+                     "+v"(pm[7]));
+      uint32_t part = 0;
+#pragma unroll
+      for (int k = 0; k < kCWords / 4; ++k) part += g + 4 * k < w0 ? (uint32_t)__popcll(pm[k]) : 0u;
+      part += __shfl_xor(part, 16);
+      part += __shfl_xor(part, 32);
       uint32_t run = H.vbase[bsel][i] + part;
       // two steps (one bitmap word) per batch: all LDS reads of a batch are
       // issued before any is used
