@@ -79,12 +79,10 @@ template <bool kOneRound>
 constexpr int piece_cols() { return kOneRound ? 512 : 1024; }
 template <bool kOneRound>
 constexpr int piece_steps() { return piece_cols<kOneRound>() / 32 / kWaves; }
-constexpr int kFinBatch = 8;
-constexpr int kLrBatch = 4;                       // low-rank chunks whose operands are read together                      // pieces requested together when finishing T
+constexpr int kFinBatch = 8;                      // pieces requested together when finishing T
 constexpr int kMaxLoadRows = kRows / kWaves;      // rows per load-issuing wave
 static_assert(sizeof(LdsHead) % 16 == 0 && sizeof(Lds) % 16 == 0, "areas must stay 16-byte aligned");
-static_assert(offsetof(Lds, masks) % 16 == 0 && sizeof(Lds::masks) >= 8 * 1024,
-              "the T operands of up to 256 ranks live in the bitmap-word area");
+static_assert(offsetof(Lds, masks) % 16 == 0, "bitmap rows must stay 16-byte aligned");
 
 // Decode reads address LDS with plain byte offsets: the dynamic area starts at
 // byte 0 (these kernels declare no static LDS; the kernel checks), so the
@@ -273,12 +271,7 @@ void fwd_small_kernel(SmallFwdArgs a) {
   uint32_t* const vals = reinterpret_cast<uint32_t*>(smem + sizeof(LdsHead));
   Lds& L = *reinterpret_cast<Lds*>(smem + sizeof(LdsHead) + a.vals_bytes);
   f32x4_t* const red = reinterpret_cast<f32x4_t*>(vals);
-  // This workgroup's T chunks as MFMA operands [chunk][64 lanes] (bf16
-  // pairs) reuse the bitmap-word area: they are written only after the
-  // barrier that ends every wave's decode, and the decode keeps its bitmap
-  // words in registers (so two workgroups with 112 adapter ranks still share
-  // a CU).  After the values area: the tile's B_cat rows [16][r_cat].
-  u32x4_t* const tl = reinterpret_cast<u32x4_t*>(L.masks);
+  // After the fixed part: the tile's B_cat rows [16][r_cat].
   uint16_t* const bl = reinterpret_cast<uint16_t*>(smem + sizeof(LdsHead) + a.vals_bytes + sizeof(Lds));
 
   const int tid = threadIdx.x;
@@ -603,12 +596,11 @@ void fwd_small_kernel(SmallFwdArgs a) {
     }
   }
 
-  // The launch tag, then the T operand of this wave's chunk into LDS for
-  // the epilogue.  Both are requested only now: a load in flight holds up
-  // every later wait of its wave (the weights must not wait for the ticket),
-  // and T held across the decode would not fit two workgroups per CU.  The
-  // first barrier also ends every wave's reads of the values area, which
-  // the wave sums then reuse.
+  // The launch tag, then the T operand of this wave's chunk.  Both are
+  // requested only now: a load in flight holds up every later wait of its
+  // wave (the weights must not wait for the ticket), and T is published
+  // about when the decodes end.  The first barrier also ends every wave's
+  // reads of the values area, which the wave sums then reuse.
   if (talk && tid == 0) drawn = draw_ticket(a.tickets, blockIdx.x, n_wgs);
   uint64_t tw[4] = {0ull, 0ull, 0ull, 0ull};
   if (t_live) {
@@ -621,8 +613,38 @@ void fwd_small_kernel(SmallFwdArgs a) {
     resolve_tag();
     if (lane == 0) L.tag = tag;
   }
+  // B_cat operand of this wave's chunk (read before the barrier; a read
+  // outside the tile's ranks or rows is pointed at the zero chunk)
+  u32x4_t wv = zero_u4();
+  if (wave < n_own) {
+    const int rb = 32 * my_chunk + 8 * g;
+    if (kWin) {
+      // eight ranks in one aligned 16-byte read (ranks outside the tile's
+      // block: zero)
+      const int rr = rb - rlo;
+      wv = *(i < rows_here && rr >= 0 && rr < rn ? reinterpret_cast<const u32x4_t*>(bl + i * bstride + rr)
+                                                  : &H.zero16);
+    } else if (a.r_cat % 8 == 0) {
+      // eight ranks in one aligned 16-byte read (ranks past r_cat: zero)
+      wv = *(i < rows_here && rb < a.r_cat ? reinterpret_cast<const u32x4_t*>(bl + i * a.r_cat + rb) : &H.zero16);
+    } else {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ra = rb + 2 * e;
+        const uint16_t* zh = reinterpret_cast<const uint16_t*>(&H.zero16);
+        const uint32_t lo = *(i < rows_here && ra < a.r_cat ? bl + i * a.r_cat + ra : zh);
+        const uint32_t hi = *(i < rows_here && ra + 1 < a.r_cat ? bl + i * a.r_cat + ra + 1 : zh);
+        w[e] = lo | (hi << 16);
+      }
+      wv = u32x4_t{w[0], w[1], w[2], w[3]};
+    }
+  }
   lds_barrier();
   if (talk) tag = L.tag;
+  // Low-rank term of this wave's chunk, in its own accumulator:
+  // acc += B_cat^T[rows, chunk] T^T[chunk, :] as one more K step (T already
+  // rounded to bf16); the waves' sums below then carry it.
   if (wave < n_own) {
     uint32_t d[4] = {0u, 0u, 0u, 0u};
     if (t_live) {
@@ -639,7 +661,7 @@ void fwd_small_kernel(SmallFwdArgs a) {
         d[0] = d0[0], d[1] = d0[1], d[2] = d1[0], d[3] = d1[1];
       }
     }
-    tl[wave * 64 + lane] = u32x4_t{d[0], d[1], d[2], d[3]};
+    acc = mfma_16x16x32(wv, u32x4_t{d[0], d[1], d[2], d[3]}, acc);
   }
   // sum the waves' accumulators into wave 0 (fixed order)
   if (wave > 0) red[(wave - 1) * 64 + lane] = acc;
@@ -647,46 +669,6 @@ void fwd_small_kernel(SmallFwdArgs a) {
   if (wave > 0) return;
 #pragma unroll
   for (int w = 0; w < kWaves - 1; ++w) acc += red[w * 64 + lane];
-
-  // Low-rank term for this workgroup's chunks: acc += B_cat^T[rows, chunk]
-  // T^T[chunk, :], as extra K steps (T already rounded to bf16).  The
-  // operands of kLrBatch chunks are read together; a read outside the tile's
-  // ranks or rows is pointed at the zero chunk instead of being skipped (a
-  // skipped read is compiled as a branch around the read and its wait).
-  for (int k0 = 0; k0 < n_own; k0 += kLrBatch) {
-    u32x4_t wv[kLrBatch], tv[kLrBatch];
-#pragma unroll
-    for (int b = 0; b < kLrBatch; ++b) {
-      const int k = min(k0 + b, n_own - 1);
-      const int rb = 32 * (clo + rng + k * a.splits) + 8 * g;
-      tv[b] = tl[k * 64 + lane];
-      if (kWin) {
-        // eight ranks in one aligned 16-byte read (ranks outside the tile's
-        // block: zero)
-        const int rr = rb - rlo;
-        wv[b] = *(i < rows_here && rr >= 0 && rr < rn ? reinterpret_cast<const u32x4_t*>(bl + i * bstride + rr)
-                                                       : &H.zero16);
-      } else if (a.r_cat % 8 == 0) {
-        // eight ranks in one aligned 16-byte read (ranks past r_cat: zero)
-        wv[b] = *(i < rows_here && rb < a.r_cat ? reinterpret_cast<const u32x4_t*>(bl + i * a.r_cat + rb)
-                                                 : &H.zero16);
-      } else {
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int ra = rb + 2 * e;
-          const uint16_t* zh = reinterpret_cast<const uint16_t*>(&H.zero16);
-          const uint32_t lo = *(i < rows_here && ra < a.r_cat ? bl + i * a.r_cat + ra : zh);
-          const uint32_t hi = *(i < rows_here && ra + 1 < a.r_cat ? bl + i * a.r_cat + ra + 1 : zh);
-          w[e] = lo | (hi << 16);
-        }
-        wv[b] = u32x4_t{w[0], w[1], w[2], w[3]};
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < kLrBatch; ++b)
-      if (k0 + b < n_own) acc = mfma_16x16x32(wv[b], tv[b], acc);
-  }
   if (a.splits > 1) {
     if (!reduce_parts(acc, a.ypart + (size_t)tile * a.splits * 256, a.splits, rng, &a.ycount[tile], tag, err,
                       lane))
@@ -738,7 +720,8 @@ void launch_small(const SmallFwdArgs& a, int grid, size_t lds, bool one_round, h
 
 hipError_t launch_fwd_small(const SmallFwdArgs& a, hipStream_t s) {
   const int grid = a.n_tiles * a.splits + a.r_tiles * a.t_pieces;
-  if (a.tl_bytes > 8 * 1024) return hipErrorInvalidValue;  // (r_cat <= 256)
+  // (r_cat <= 256: at most 8 rank chunks, one per wave)
+  if (a.tl_bytes > 8 * 1024) return hipErrorInvalidValue;
   const size_t lds = fwd_small_lds_bytes(a.vcap, a.bl_bytes);
   // one weight workgroup per CU at most: all resident in one round
   const bool one_round = (int64_t)a.n_tiles * a.splits <= kCus;
