@@ -193,8 +193,53 @@ __device__ __forceinline__ void copy_chunks_to_lds(const uint32_t* src, uint32_t
 // (value group g of a row is LDS chunk g of its area, as in the bf16 layout),
 // and after a barrier write their bf16 values, level[code] * scale rounded
 // in float32, over the same area.
+// Whole rows of a multiple of 8 values (one column range): value group g of
+// a row is code word g of the row's codes (the codes start on a 16-byte
+// boundary) and lies in scale block g / 8, so the indices are plain 32-bit
+// offsets.
+__device__ __forceinline__ void nf4_dequantize_rows(const SmallFwdArgs& a, const Lds& L, uint32_t* vals,
+                                                    int64_t row0, int rows_here, int tid) {
+  const int r = tid >> 5, p = tid & 31;
+  const int nch = r < rows_here ? a.n_keep >> 3 : 0;
+  const uint32_t* cw32 = vals + (size_t)r * a.vcap * 4 + a.cofs * 4;
+  const uint16_t* sl = reinterpret_cast<const uint16_t*>(vals + (size_t)r * a.vcap * 4 + a.sofs * 4) +
+                       (((row0 + r) * a.nblk) & 7);  // (the scales' copy starts at a 16-byte boundary)
+  const int gmax = nch > 0 ? nch - 1 : 0;
+  uint32_t cw[kNf4Groups], sc[kNf4Groups];
+#pragma unroll
+  for (int q = 0; q < kNf4Groups; ++q) {
+    const int g = min(p + 32 * q, gmax);  // (clamped, read unconditionally)
+    cw[q] = cw32[g];
+    sc[q] = sl[g >> 3];
+  }
+  static_assert(kNf4Groups == 9, "operand list below");
+  asm volatile("" : "+v"(cw[0]), "+v"(cw[1]), "+v"(cw[2]), "+v"(cw[3]), "+v"(cw[4]), "+v"(cw[5]), "+v"(cw[6]),
+               "+v"(cw[7]), "+v"(cw[8]), "+v"(sc[0]), "+v"(sc[1]), "+v"(sc[2]), "+v"(sc[3]), "+v"(sc[4]),
+               "+v"(sc[5]), "+v"(sc[6]), "+v"(sc[7]), "+v"(sc[8]));
+  lds_barrier();  // every thread has its codes and scales: the area is free
+#pragma unroll
+  for (int q = 0; q < kNf4Groups; ++q) {
+    const int g = p + 32 * q;
+    if (g < nch) {
+      const float s = __uint_as_float(sc[q] << 16);
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float f0 = L.levels[(cw[q] >> (4 * e)) & 15u] * s;
+        const float f1 = L.levels[(cw[q] >> (4 * e + 4)) & 15u] * s;
+        w[e / 2] = (uint32_t)f32_to_bf16(f0) | ((uint32_t)f32_to_bf16(f1) << 16);
+      }
+      reinterpret_cast<u32x4_t*>(vals)[(size_t)r * a.vcap + g] = u32x4_t{w[0], w[1], w[2], w[3]};
+    }
+  }
+}
+
 __device__ __forceinline__ void nf4_dequantize(const SmallFwdArgs& a, const Lds& L, uint32_t* vals, int64_t row0,
                                                int rows_here, int tid) {
+  if (a.splits == 1 && (a.n_keep & 7) == 0) {
+    nf4_dequantize_rows(a, L, vals, row0, rows_here, tid);
+    return;
+  }
   const int r = tid >> 5, p = tid & 31;
   const uint32_t lo = L.seg[r][0], hi = L.seg[r][1];
   const bool live = r < rows_here && hi > lo;
