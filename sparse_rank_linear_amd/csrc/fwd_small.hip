@@ -617,8 +617,10 @@ void fwd_small_kernel(SmallFwdArgs a) {
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
           const int q = q0 + b;
+          // (no step guard: a word outside the wave's range was zeroed above,
+          // and a bitmap word has no bits past K or past a column range)
           const uint32_t h = (q & 1) ? (uint32_t)(mw[q >> 1] >> 32) : (uint32_t)mw[q >> 1];
-          const uint32_t byte = (q < spw && s0 + q < nsteps) ? (h >> (8 * g)) & 0xFFu : 0u;
+          const uint32_t byte = (h >> (8 * g)) & 0xFFu;
           const uint32_t lo = byte & 15u, hi = byte >> 4;
           ia[b] = run + __popc(h & below);
           ib[b] = ia[b] + __popc(lo);
@@ -628,14 +630,13 @@ void fwd_small_kernel(SmallFwdArgs a) {
           lb[b] = lut_entry(hi);
           run += __popc(h);
         }
+        // (a step past the wave's range multiplies zeros: its byte is 0,
+        // which selects no value)
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
-          const int q = q0 + b;
-          if (q < spw && s0 + q < nsteps) {
-            const u32x2_t x0 = expand_nibble(window_values(wa[b], ia[b]), la[b]);
-            const u32x2_t x1 = expand_nibble(window_values(wb[b], ib[b]), lb[b]);
-            acc = mfma_16x16x32(u32x4_t{x0.x, x0.y, x1.x, x1.y}, xf[q], acc);
-          }
+          const u32x2_t x0 = expand_nibble(window_values(wa[b], ia[b]), la[b]);
+          const u32x2_t x1 = expand_nibble(window_values(wb[b], ib[b]), lb[b]);
+          acc = mfma_16x16x32(u32x4_t{x0.x, x0.y, x1.x, x1.y}, xf[q0 + b], acc);
         }
       }
     }
