@@ -195,10 +195,15 @@ def measure_peaks(dev):
     out = torch.empty(4096, dtype=torch.float32, device=dev)
     flops = 1024 * 4 * 4000 * 131072
     t = timed(lambda: srl.probe_mfma(out, 1024, 4000, 1), 3)
+    # the 16x16x32 form the forward kernels issue, with one wave per SIMD
+    # (256 workgroups of 4 waves) as in their matrix-core waves, and with four
+    t16 = {wg: flops / timed(lambda wg=wg: srl.probe_mfma(out, wg, 4000 * 1024 // wg, 0), 3) / 1e12
+           for wg in (256, 1024)}
     best_wg = max(read, key=read.get)
     return {"hbm_read_GBs": round(read[best_wg], 1), "hbm_read_workgroups": best_wg,
             "hbm_read_by_grid": {str(k): round(v, 1) for k, v in read.items()},
-            "mfma_bf16_TFLOPs": round(flops / t / 1e12, 1), "mfma_probe": "v_mfma_f32_32x32x16_bf16"}
+            "mfma_bf16_TFLOPs": round(flops / t / 1e12, 1), "mfma_probe": "v_mfma_f32_32x32x16_bf16",
+            "mfma_bf16_16x16x32_TFLOPs": {"1_wave_per_simd": round(t16[256], 1), "4_waves_per_simd": round(t16[1024], 1)}}
 
 
 def check_timed_output(wl, inp, layer, X_bits, X, ws, Y_timed, last_layer, dev):
@@ -237,6 +242,42 @@ def check_timed_output(wl, inp, layer, X_bits, X, ws, Y_timed, last_layer, dev):
     return res
 
 
+def dense_context(dev, N, K, r_cat, M, steps, warmup, rotate_bytes=600_000_000):
+    """Context only: the same shape computed densely with torch's bf16
+    products, Y = X W^T + (X A_cat) B_cat, through the vendor GEMM library
+    (not inspected).  With M <= 16 the dense weight rotates over copies
+    totalling more than the Infinity Cache, as the compressed one does.
+    Graph-replayed like the forward; mean seconds per call."""
+    import torch
+
+    copies = max(1, -(-rotate_bytes // (2 * N * K))) if M <= 16 else 1
+    gen = torch.Generator(device=dev).manual_seed(21)
+    rnd = lambda *shape: (torch.randn(shape, generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+    Ws = [rnd(N, K) for _ in range(copies)]
+    A, B, X = rnd(K, r_cat), rnd(r_cat, N), rnd(M, K)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    T = torch.empty((M, r_cat), dtype=torch.bfloat16, device=dev)
+
+    def call(W):
+        torch.mm(X, W.t(), out=Y)
+        torch.mm(X, A, out=T)
+        Y.addmm_(T, B)
+
+    fns = [(lambda W=W: call(W)) for W in Ws]
+    for j in range(max(warmup, copies)):
+        fns[j % len(fns)]()
+    torch.cuda.synchronize()
+    g = _timed_graph(fns, steps)
+    g.replay()
+    torch.cuda.synchronize()
+    t = min(_time_replay(g) for _ in range(3)) / steps
+    del g, Ws, A, B, X, Y, T
+    torch.cuda.empty_cache()
+    return {"us": round(t * 1e6, 3), "dense_weight_copies": copies,
+            "dense_GBs": round((2 * N * K + 2 * r_cat * (K + N) + 2 * M * (K + N)) / t / 1e9, 1),
+            "dense_tflops": round(2 * M * N * K / t / 1e12, 2)}
+
+
 def run_configs(dev):
     """One JSON line per (workload, token count) of the synthetic table."""
     import torch
@@ -259,18 +300,29 @@ def run_configs(dev):
         copies = max(2, -(-600_000_000 // cbytes))
         layers = [layer] + [layer.clone() for _ in range(copies - 1)]
         tokens = sorted({1, 16, wl.M}) if wl.M <= 16 else [wl.M]
+        if name.startswith("llama3_8b_"):
+            tokens = [1, 16, 256, 4096]  # the Llama-3-8B block from decode to prefill
         ws = srl.forward_workspace(layer, max(tokens))
         for M in tokens:
             X = _dev_bits(synth.make_x(wl.K, M, seed=11), dev)
-            t = measure_decode(layers, X, ws, 32, 4)
+            steps = 32 if M <= 256 else 8
+            t = measure_decode(layers if M <= 256 else [layer], X, ws, steps, 4)
             rec = {"workload": name, "N": wl.N, "K": wl.K, "n_keep": wl.n_keep, "r_cat": wl.r_cat, "M": M,
                    "us": round(t * 1e6, 2), "compressed_GBs": round(cbytes / t / 1e9, 1),
                    "tflops_dense_equiv": round(2 * M * wl.N * wl.K / t / 1e12, 2), "encode_ms": round(encode_ms, 1)}
-            if M <= 16:
+            # bytes bound at few tokens, matrix cores at many; at 256 tokens the
+            # arithmetic intensity sits near the ridge, so both fractions
+            if M <= 256:
                 rec["hbm_frac"] = round((cbytes + 2 * M * (wl.K + wl.N)) / t / 1e9 / HBM_PEAK_GBS, 4)
-            else:
+            if M >= 256:
                 rec["mfma_frac_dense_equiv"] = round(2 * M * wl.N * wl.K / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+                eff = 2 * M * (wl.N * wl.n_keep + wl.r_cat * (wl.K + wl.N))
+                rec["mfma_frac_effective"] = round(eff / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+            d = dense_context(dev, wl.N, wl.K, wl.r_cat, M, steps, 4)
+            rec["dense_bf16_us"] = d["us"]
+            rec["speedup_vs_dense"] = round(d["us"] / (t * 1e6), 3)
             print(json.dumps(rec), flush=True)
+            del X
         del layers, layer, ws
         torch.cuda.empty_cache()
 
@@ -518,6 +570,15 @@ def main():
         # and the 70B-shaped 28672 x 8192 layer at 8192 tokens
         out["prefill"] = many_token_line(dev, "llama7b_mlp_up_11008", "llama7b_mlp_up_11008x4096_prefill", peaks,
                                          steps=20, warmup=3)
+        # context: the same two shapes done densely in bf16 by the vendor GEMM library
+        dh = dense_context(dev, wl.N, wl.K, wl.r_cat, M, 320, 32)
+        dh["workload"] = "llama7b_attn_4096x4096_decode"
+        dh["salr_speedup"] = round(dh["us"] / (t * 1e6), 3)
+        wp = synth.WORKLOADS["llama7b_mlp_up_11008"]
+        dp = dense_context(dev, wp.N, wp.K, wp.r_cat, wp.M, 20, 3)
+        dp["workload"] = "llama7b_mlp_up_11008x4096_prefill"
+        dp["salr_speedup"] = round(dp["us"] / (out["prefill"]["ms_per_step"] * 1e3), 3)
+        out["dense_context"] = [dh, dp]
         out["l70b_up_s50"] = many_token_line(dev, "l70b_up_s50", "l70b_up_28672x8192_s50_m8192", peaks,
                                              steps=5, warmup=2)
         out["qsalr_nf4"] = nf4_line(dev, layer, wl, steps=128, warmup=16)

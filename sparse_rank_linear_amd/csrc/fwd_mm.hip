@@ -203,10 +203,12 @@ __global__ __launch_bounds__(kThreads) void fwd_mm_kernel(LargeFwdArgs a) {
           const int m = m0 + wm * 128 + tm * 16 + i;
           if (m >= a.M) continue;
           float* dst = part + (size_t)m * a.N + n;
+          if ((a.N & 3) == 0 && n + 3 < a.N) {
+            *reinterpret_cast<f32x4_t*>(dst) = acc[tn][tm];
+          } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float v = acc[tn][tm][e];
-            if (n + e < a.N) dst[e] = v;
+            for (int e = 0; e < 4; ++e)
+              if (n + e < a.N) dst[e] = acc[tn][tm][e];
           }
         }
       }
@@ -472,17 +474,39 @@ __global__ __launch_bounds__(kTThreads) void lowrank_t_kernel(LowRankTArgs a) {
   }
 }
 
+// Sum over `splits` partial arrays `stride` floats apart of the 8 floats at
+// p, in split order.  The loads of 8 splits at a time are issued together
+// (clamped to split 0 past the end, those terms not added), so a thread
+// waits for one memory round trip per 8 splits rather than per split.
+__device__ __forceinline__ void sum_split_partials(const float* p, int64_t stride, int splits, f32x4_t& lo,
+                                                   f32x4_t& hi) {
+  constexpr int kU = 8;
+  lo = zero4();
+  hi = zero4();
+  for (int s0 = 0; s0 < splits; s0 += kU) {
+    f32x4_t l[kU], h[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const float* src = p + (size_t)(s0 + u < splits ? s0 + u : 0) * stride;
+      l[u] = *reinterpret_cast<const f32x4_t*>(src);
+      h[u] = *reinterpret_cast<const f32x4_t*>(src + 4);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (s0 + u < splits) {
+        lo += l[u];
+        hi += h[u];
+      }
+  }
+}
+
 // T = bf16(sum of the K-split partials of X A_cat, in split order), [M][r_pad]
 // with r_pad a multiple of 16: 8 ranks a thread.
 __global__ __launch_bounds__(256) void reduce_t_kernel(const float* tpart, int splits, int64_t MR, uint16_t* t16) {
   const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
   if (e0 >= MR) return;
-  f32x4_t lo = zero4(), hi = zero4();
-  for (int sp = 0; sp < splits; ++sp) {
-    const float* src = tpart + (size_t)sp * MR + e0;
-    lo += *reinterpret_cast<const f32x4_t*>(src);
-    hi += *reinterpret_cast<const f32x4_t*>(src + 4);
-  }
+  f32x4_t lo, hi;
+  sum_split_partials(tpart + e0, MR, splits, lo, hi);
   *reinterpret_cast<u32x4_t*>(t16 + e0) =
       u32x4_t{(uint32_t)f32_to_bf16(lo[0]) | ((uint32_t)f32_to_bf16(lo[1]) << 16),
               (uint32_t)f32_to_bf16(lo[2]) | ((uint32_t)f32_to_bf16(lo[3]) << 16),
@@ -496,12 +520,8 @@ __global__ __launch_bounds__(256) void sum_splits_kernel(const float* part, uint
   const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
   if (e0 >= MN) return;
   if ((MN & 7) == 0) {
-    f32x4_t lo = zero4(), hi = zero4();
-    for (int s = 0; s < ksplit; ++s) {
-      const float* src = part + (size_t)s * MN + e0;
-      lo += *reinterpret_cast<const f32x4_t*>(src);
-      hi += *reinterpret_cast<const f32x4_t*>(src + 4);
-    }
+    f32x4_t lo, hi;
+    sum_split_partials(part + e0, MN, ksplit, lo, hi);
     *reinterpret_cast<u32x4_t*>(Y + e0) =
         u32x4_t{(uint32_t)f32_to_bf16(lo[0]) | ((uint32_t)f32_to_bf16(lo[1]) << 16),
                 (uint32_t)f32_to_bf16(lo[2]) | ((uint32_t)f32_to_bf16(lo[3]) << 16),

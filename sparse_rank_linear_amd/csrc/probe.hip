@@ -11,8 +11,6 @@
 namespace salr {
 namespace {
 
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
 constexpr int kReadThreads = 512;
 constexpr int kReadUnroll = 4;  // 16-byte loads in flight per thread per step
 
@@ -79,8 +77,7 @@ __global__ __launch_bounds__(256) void mfma_peak_kernel(float* out, int iters) {
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                         __builtin_bit_cast(bf16x8_t, b), acc[c], 0, 0, 0);
+        acc[c] = mfma_32x32x16(a, b, acc[c]);
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c)

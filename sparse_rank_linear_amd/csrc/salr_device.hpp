@@ -7,6 +7,15 @@
 //   D (16 x 16, fp32):   lane holds D[4g + e][i], e=0..3   (4 floats)
 // Both inputs run along k inside a lane, so a row-major matrix with k
 // contiguous loads straight into either operand.
+//
+// v_mfma_f32_32x32x16_bf16 (twice the work per instruction; in loops of
+// independent instructions on MI355X it sustains 1.7x the 16x16x32 form's
+// rate with four waves per SIMD and 2.5x with one): for lane l, let
+// r = l % 32 and h = l / 32.
+//   A operand (32 x 16): lane holds A[r][8h .. 8h+7]
+//   B operand (16 x 32): lane holds B[8h .. 8h+7][r]
+//   D (32 x 32, fp32):   element 4j + e of the lane is D[8j + 4h + e][r],
+//                        j, e = 0..3
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -20,9 +29,15 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ f32x4_t mfma_16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16_t mfma_32x32x16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
