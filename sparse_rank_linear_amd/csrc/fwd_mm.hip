@@ -421,38 +421,36 @@ __global__ __launch_bounds__(kTThreads) void lowrank_t_kernel(LowRankTArgs a) {
 #pragma unroll
   for (int j = 0; j < kMaxRTiles; ++j) acc[j] = zero4();
 
-  // The A_cat slice and the X operands of the next 64-column tile are
-  // requested before this tile's MFMAs (registers), so each tile waits for
-  // one load round trip less.
+  // The A_cat slice and the X operands of a 64-column tile are requested
+  // two tiles ahead into a ring of three register sets (named, so the ring
+  // stays in registers): a tile's MFMAs wait for a load round trip only at
+  // the start of the range.
   constexpr int kPer = kMaxRTiles * 16 * 8 / kTThreads;  // A_cat chunks per thread, at most
-  u32x4_t an[kPer], xn[2];
-  const auto load_tile = [&](int kt) __attribute__((always_inline)) {
+  struct TileRegs {
+    u32x4_t a[kPer], x[2];
+  };
+  const auto load_tile = [&](int kt, TileRegs& t) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int c = tid + kTThreads * u;
       const int r = c >> 3, k = kt + 8 * (c & 7);
-      an[u] = (r < a.r_cat && k < k1) ? load16(a.a_cat + (size_t)r * a.K + k) : zero_u4();
+      t.a[u] = (r < a.r_cat && k < k1) ? load16(a.a_cat + (size_t)r * a.K + k) : zero_u4();
     }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int k = kt + 32 * s + 8 * g;
-      xn[s] = (token < a.M && k < k1) ? load16(a.X + (size_t)token * a.K + k) : zero_u4();
+      t.x[s] = (token < a.M && k < k1) ? load16(a.X + (size_t)token * a.K + k) : zero_u4();
     }
   };
-  if (k0 < k1) load_tile(k0);
-  for (int kt = k0; kt < k1; kt += 64) {
-    u32x4_t av[kPer], xv[2];
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) av[u] = an[u];
-    xv[0] = xn[0];
-    xv[1] = xn[1];
-    if (kt + 64 < k1) load_tile(kt + 64);
+  // tile kt from `cur`, after requesting tile kt + 128 into `next2`
+  const auto step = [&](int kt, const TileRegs& cur, TileRegs& next2) __attribute__((always_inline)) {
+    if (kt + 128 < k1) load_tile(kt + 128, next2);
     __syncthreads();  // (the previous tile's reads of al are done)
     // stage A_cat[0..r_pad)[kt .. kt+64)
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int c = tid + kTThreads * u;
-      if ((c >> 3) < a.r_pad) *reinterpret_cast<u32x4_t*>(&al[(c >> 3) * kLdsRow + (c & 7) * 4]) = av[u];
+      if ((c >> 3) < a.r_pad) *reinterpret_cast<u32x4_t*>(&al[(c >> 3) * kLdsRow + (c & 7) * 4]) = cur.a[u];
     }
     __syncthreads();
 #pragma unroll
@@ -461,8 +459,16 @@ __global__ __launch_bounds__(kTThreads) void lowrank_t_kernel(LowRankTArgs a) {
       for (int j = 0; j < kMaxRTiles; ++j)
         if (j < rt) {
           const u32x4_t w = *reinterpret_cast<const u32x4_t*>(&al[(16 * j + i) * kLdsRow + s * 16 + g * 4]);
-          acc[j] = mfma_16x16x32(w, xv[s], acc[j]);
+          acc[j] = mfma_16x16x32(w, cur.x[s], acc[j]);
         }
+  };
+  TileRegs t0, t1, t2;
+  if (k0 < k1) load_tile(k0, t0);
+  if (k0 + 64 < k1) load_tile(k0 + 64, t1);
+  for (int kt = k0; kt < k1; kt += 192) {
+    step(kt, t0, t2);
+    if (kt + 64 < k1) step(kt + 64, t1, t0);
+    if (kt + 128 < k1) step(kt + 128, t2, t1);
   }
 
   // lane holds T[token][16j + 4g + e]
