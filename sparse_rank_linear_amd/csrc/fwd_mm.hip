@@ -93,9 +93,11 @@ __global__ __launch_bounds__(kThreads) void fwd_mm_kernel(LargeFwdArgs a) {
   const int nk = min((a.K + 63) / 64, kt0 + a.kt_per);
   const int n_main = nk - kt0;
 
-  // Low-rank tiles (split 0 only): ranks [rlo, rhi) in 64-rank tiles; a
-  // fused layer's row block takes only its part's ranks (b_cat is zero
-  // outside them; every part holds whole 256-row blocks).
+  // Low-rank tiles: ranks [rlo, rhi) in 64-rank tiles, tile j taken by K
+  // split j mod ksplit (the split sums add them like any other K tile), so
+  // no split carries all of them; a fused layer's row block takes only its
+  // part's ranks (b_cat is zero outside them; every part holds whole
+  // 256-row blocks).
   // (static indices: a runtime index into the argument's arrays would move
   // the whole argument block to private memory)
   int rlo = 0, rhi = a.r_cat;
@@ -107,7 +109,8 @@ __global__ __launch_bounds__(kThreads) void fwd_mm_kernel(LargeFwdArgs a) {
       rhi = rlo + a.part_nrank[p];
       found = true;
     }
-  const int n_lr = (split == 0 && rhi > rlo) ? (rhi - rlo + 63) / 64 : 0;
+  const int n_lr_all = rhi > rlo ? (rhi - rlo + 63) / 64 : 0;
+  const int n_lr = n_lr_all > split ? (n_lr_all - split + a.ksplit - 1) / a.ksplit : 0;
   const int phases = n_main + n_lr;
 
   // X buffer of phase p (a ring of three) and W buffer (two)
@@ -282,12 +285,11 @@ __global__ __launch_bounds__(kThreads) void fwd_mm_kernel(LargeFwdArgs a) {
       idx += __popc(byte);
     }
   };
-  // Low-rank tile j into buffers xt (bf16 T = sum of the K-split partials of
-  // X A_cat written by the previous launch) and wt (B_cat^T slices).
-  // (T is the bf16 sum of the K-split partials of X A_cat, made by the
-  // previous launch; ranks at or past rhi meet zero B_cat columns below)
-  auto stage_lowrank = [&](int j, u32x4_t* xt, u32x4_t* wt) __attribute__((always_inline)) {
-    const int r0 = rlo + 64 * j;
+  // Low-rank tile l of this split into buffers xt (bf16 T, the sum of the
+  // K-split partials of X A_cat made by the previous launch) and wt (B_cat^T
+  // slices); ranks at or past rhi meet zero B_cat columns below.
+  auto stage_lowrank = [&](int l, u32x4_t* xt, u32x4_t* wt) __attribute__((always_inline)) {
+    const int r0 = rlo + 64 * (split + l * a.ksplit);  // this split's l-th low-rank tile
     u32x4_t tv[BM * 8 / 256];
 #pragma unroll
     for (int u = 0; u < BM * 8 / 256; ++u) {
