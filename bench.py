@@ -206,6 +206,40 @@ def measure_peaks(dev):
             "mfma_bf16_16x16x32_TFLOPs": {"1_wave_per_simd": round(t16[256], 1), "4_waves_per_simd": round(t16[1024], 1)}}
 
 
+def measure_launch_floor(dev, nbytes: int, copies: int, steps: int):
+    """What one launch that only reads `nbytes` once costs on this GPU: the
+    stream-read probe (include/salr_probe.h) over `copies` rotating buffers of
+    that size (more than the Infinity Cache together), graph-replayed and
+    timed like the forward, at several grid sizes; and the same probe reading
+    16 bytes (the per-launch cost of a graph node with nothing to read).
+    Mean seconds per launch."""
+    import torch
+    import sparse_rank_linear_amd as srl
+
+    nb = (nbytes + 15) // 16 * 16
+    pool = torch.zeros(copies * nb, dtype=torch.uint8, device=dev)
+    bufs = [pool[j * nb:(j + 1) * nb] for j in range(copies)]
+    sink = torch.empty(65536, dtype=torch.int32, device=dev)
+
+    def per_launch(grid, size):
+        fns = [(lambda b=b: srl.probe_stream_read(b[:size], sink, grid)) for b in bufs]
+        for f in fns:
+            f()
+        torch.cuda.synchronize()
+        g = _timed_graph(fns, steps)
+        g.replay()
+        torch.cuda.synchronize()
+        return min(_time_replay(g) for _ in range(3)) / steps
+
+    by_grid = {grid: per_launch(grid, nb) for grid in (256, 512, 1024, 2048, (nb + 8191) // 8192)}
+    empty = per_launch(256, 16)
+    del pool, bufs
+    best = min(by_grid, key=by_grid.get)
+    return {"bytes": nb, "rotating_copies": copies, "read_us_by_grid": {str(k): round(v * 1e6, 3) for k, v in by_grid.items()},
+            "best_us": round(by_grid[best] * 1e6, 3), "best_grid": best,
+            "best_GBs": round(nb / by_grid[best] / 1e9, 1), "empty_launch_us": round(empty * 1e6, 3)}
+
+
 def check_timed_output(wl, inp, layer, X_bits, X, ws, Y_timed, last_layer, dev):
     """Checks of the timed run: (1) no bounded wait timed out (workspace
     error word); (2) the timed output equals an eager call on the layer the
@@ -556,6 +590,10 @@ def main():
         out["measured_peaks"] = peaks
         out["roofline"]["peak_measured"] = peaks["hbm_read_GBs"]
         out["roofline"]["frac_measured"] = round(achieved / peaks["hbm_read_GBs"], 4)
+        # the floor for one launch that reads as many bytes as the forward
+        floor = measure_launch_floor(dev, algo, COPIES, args.steps)
+        out["launch_floor"] = floor
+        out["roofline"]["frac_of_launch_floor"] = round(floor["best_us"] / (t * 1e6), 4)
         sweep = []
         for m in (1, 4, 16):
             Xm = _dev_bits(synth.make_x(wl.K, m, seed=11), dev)

@@ -52,6 +52,7 @@ def shared_ws():
     shapes = [(N, K, nk, rs, rs + sum(lr), max(ms)) for (N, K, nk, rs, lr, ms) in CASES]
     shapes.append((300, 4096, 2048, 16, 32, 100))  # test_forward_deterministic
     shapes.append((96, 4096, 2048, 8, 32, 16))  # test_forward_clustered_rows
+    shapes.append((4096, 1024, 512, 0, 16, 16))  # test_forward_front_loaded_rows
     need = max(srl.query_sizes(*s)["forward_ws_bytes"] for s in shapes)
     return srl.workspace(need)
 
@@ -141,6 +142,37 @@ def test_forward_clustered_rows(M, shared_ws):
     layer = upload_encoded(enc, K, 8)
     say(f"forward clustered N={N} K={K} M={M}")
     X = synth.make_x(K, M, seed=23)
+    Y = srl.linear_forward(layer, to_dev(X), ws=shared_ws)
+    torch.cuda.synchronize()
+    Yref = osl.forward(X, enc.masks, enc.values, K, enc.A_cat, enc.B_cat)
+    mr, nw = errors(to_host_bits(Y), Yref)
+    say(f"  max_rel={mr:.3e} normwise={nw:.3e}")
+    assert wait_error(shared_ws) == 0
+    assert mr <= TOL_MAX_REL and nw <= TOL_NORMWISE
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_forward_front_loaded_rows(M, shared_ws):
+    """Whole-row tiles (4096 rows, one round of workgroups) in which every
+    seventh row keeps all its values in the first half of the columns, mixed
+    with ordinary rows: the waves of the first columns read far more of
+    those rows' values than of the others."""
+    import torch
+    import sparse_rank_linear_amd as srl
+
+    N, K, n_keep = 4096, 1024, 512
+    W = ob.bits_to_f64(synth.make_w(N, K, seed=31))
+    # every seventh row: the first 512 columns outrank the rest
+    W[5::7, :512] = np.sign(W[5::7, :512]) * (np.abs(W[5::7, :512]) + 1.0)
+    rng = np.random.default_rng(32)
+    A = ob.f64_to_bits(rng.standard_normal((16, K)).astype(np.float32) * 0.01)
+    B = ob.f64_to_bits(rng.standard_normal((N, 16)).astype(np.float32) * 0.01)
+    enc = osl.encode(ob.f64_to_bits(W), n_keep, 0, [A], [B])
+    first = np.array([sum(bin(int(w)).count("1") for w in row[:8]) for row in enc.masks[5:13]])
+    assert first[0] == n_keep and first[1] < n_keep  # row 5 front-loaded, row 6 not
+    layer = upload_encoded(enc, K, 0)
+    say(f"forward front-loaded N={N} K={K} M={M}")
+    X = synth.make_x(K, M, seed=33)
     Y = srl.linear_forward(layer, to_dev(X), ws=shared_ws)
     torch.cuda.synchronize()
     Yref = osl.forward(X, enc.masks, enc.values, K, enc.A_cat, enc.B_cat)
