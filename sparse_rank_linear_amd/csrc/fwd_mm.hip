@@ -400,86 +400,91 @@ __global__ __launch_bounds__(kThreads) void fwd_mm_kernel(LargeFwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // Partial T = X * A_cat over one K range per workgroup, fp32, written to
-// tpart[split][M][r_pad] (columns >= r_cat are zero).  A workgroup owns 64
-// tokens (one 16-token MFMA tile per wave); the A_cat slice of each
-// 64-column tile is shared through LDS.  The splits are summed by the
-// consumer (the next launch), so no workgroup waits for another.
+// tpart[split][M][r_pad] (columns >= r_cat are zero).  A workgroup owns
+// 16 kTT tokens and one K range; its four waves take the range's 32-column
+// steps in turn (wave w: steps w, w + 4, ...), each wave loading its A_cat
+// operands straight from memory once for all kTT token tiles (a batch of
+// steps at a time, every load of the batch issued before the first
+// multiply), and the waves' sums are added in wave order at the end.  The
+// splits are summed by the next launch in split order, so the result does
+// not depend on scheduling.
 // ---------------------------------------------------------------------------
 constexpr int kTThreads = 256;
+constexpr int kTWaves = kTThreads / 64;
 constexpr int kMaxRTiles = 16;   // r_pad <= 256
-constexpr int kLdsRow = 36;      // words per 64-column bf16 row (+16 B pad)
+constexpr int kTBatch = 2;       // steps whose loads are issued together
 
+// kRT: rank tiles the instance holds (at least r_pad / 16); kTT: 16-token
+// tiles per workgroup.
+template <int kRT, int kTT>
 __global__ __launch_bounds__(kTThreads) void lowrank_t_kernel(LowRankTArgs a) {
-  __shared__ uint32_t al[kMaxRTiles * 16 * kLdsRow];
+  __shared__ f32x4_t red[kTWaves - 1][kRT][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, g = lane >> 4;
-  const int mb = blockIdx.x, ks = blockIdx.y;
-  const int token = mb * 64 + wave * 16 + i;
+  const int tok0 = blockIdx.x * 16 * kTT + i, ks = blockIdx.y;
   const int rt = a.r_pad / 16;
   const int k0 = ks * a.k_chunk, k1 = min(a.K, k0 + a.k_chunk);
+  const int nsteps = (k1 - k0 + 31) / 32;
 
-  f32x4_t acc[kMaxRTiles];
+  f32x4_t acc[kTT][kRT];
 #pragma unroll
-  for (int j = 0; j < kMaxRTiles; ++j) acc[j] = zero4();
-
-  // The A_cat slice and the X operands of a 64-column tile are requested
-  // two tiles ahead into a ring of three register sets (named, so the ring
-  // stays in registers): a tile's MFMAs wait for a load round trip only at
-  // the start of the range.
-  constexpr int kPer = kMaxRTiles * 16 * 8 / kTThreads;  // A_cat chunks per thread, at most
-  struct TileRegs {
-    u32x4_t a[kPer], x[2];
-  };
-  const auto load_tile = [&](int kt, TileRegs& t) __attribute__((always_inline)) {
+  for (int t = 0; t < kTT; ++t)
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int c = tid + kTThreads * u;
-      const int r = c >> 3, k = kt + 8 * (c & 7);
-      t.a[u] = (r < a.r_cat && k < k1) ? load16(a.a_cat + (size_t)r * a.K + k) : zero_u4();
+    for (int j = 0; j < kRT; ++j) acc[t][j] = zero4();
+  for (int s0 = wave; s0 < nsteps; s0 += kTWaves * kTBatch) {
+    u32x4_t xv[kTBatch][kTT], av[kTBatch][kRT];
+#pragma unroll
+    for (int b = 0; b < kTBatch; ++b) {
+      const int k = k0 + 32 * (s0 + kTWaves * b) + 8 * g;  // (k >= k1 past the last step)
+#pragma unroll
+      for (int j = 0; j < kRT; ++j) {
+        const int r = 16 * j + i;
+        av[b][j] = (j < rt && r < a.r_cat && k < k1) ? load16(a.a_cat + (size_t)r * a.K + k) : zero_u4();
+      }
+#pragma unroll
+      for (int t = 0; t < kTT; ++t) {
+        const int token = tok0 + 16 * t;
+        xv[b][t] = (token < a.M && k < k1) ? load16(a.X + (size_t)token * a.K + k) : zero_u4();
+      }
     }
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int k = kt + 32 * s + 8 * g;
-      t.x[s] = (token < a.M && k < k1) ? load16(a.X + (size_t)token * a.K + k) : zero_u4();
-    }
-  };
-  // tile kt from `cur`, after requesting tile kt + 128 into `next2`
-  const auto step = [&](int kt, const TileRegs& cur, TileRegs& next2) __attribute__((always_inline)) {
-    if (kt + 128 < k1) load_tile(kt + 128, next2);
-    __syncthreads();  // (the previous tile's reads of al are done)
-    // stage A_cat[0..r_pad)[kt .. kt+64)
+    for (int b = 0; b < kTBatch; ++b)
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int c = tid + kTThreads * u;
-      if ((c >> 3) < a.r_pad) *reinterpret_cast<u32x4_t*>(&al[(c >> 3) * kLdsRow + (c & 7) * 4]) = cur.a[u];
-    }
+      for (int j = 0; j < kRT; ++j)
+        if (j < rt)
+#pragma unroll
+          for (int t = 0; t < kTT; ++t) acc[t][j] = mfma_16x16x32(av[b][j], xv[b][t], acc[t][j]);
+  }
+  // the waves' sums, in wave order, one token tile at a time; lane holds
+  // T[token][16j + 4g + e]
+#pragma unroll
+  for (int t = 0; t < kTT; ++t) {
+    if (t > 0) __syncthreads();  // (wave 0 has read the previous tile's sums)
+    if (wave > 0)
+#pragma unroll
+      for (int j = 0; j < kRT; ++j)
+        if (j < rt) red[wave - 1][j][lane] = acc[t][j];
     __syncthreads();
+    const int token = tok0 + 16 * t;
+    if (wave == 0 && token < a.M) {
+      float* dst = a.tpart + ((size_t)ks * a.M + token) * a.r_pad;
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int j = 0; j < kMaxRTiles; ++j)
+      for (int j = 0; j < kRT; ++j)
         if (j < rt) {
-          const u32x4_t w = *reinterpret_cast<const u32x4_t*>(&al[(16 * j + i) * kLdsRow + s * 16 + g * 4]);
-          acc[j] = mfma_16x16x32(w, cur.x[s], acc[j]);
-        }
-  };
-  TileRegs t0, t1, t2;
-  if (k0 < k1) load_tile(k0, t0);
-  if (k0 + 64 < k1) load_tile(k0 + 64, t1);
-  for (int kt = k0; kt < k1; kt += 192) {
-    step(kt, t0, t2);
-    if (kt + 64 < k1) step(kt + 64, t1, t0);
-    if (kt + 128 < k1) step(kt + 128, t2, t1);
-  }
-
-  // lane holds T[token][16j + 4g + e]
-  if (token < a.M) {
-    float* dst = a.tpart + ((size_t)ks * a.M + token) * a.r_pad;
+          f32x4_t v = acc[t][j];
 #pragma unroll
-    for (int j = 0; j < kMaxRTiles; ++j)
-      if (j < rt) *reinterpret_cast<f32x4_t*>(&dst[16 * j + 4 * g]) = acc[j];
+          for (int w = 0; w < kTWaves - 1; ++w) v += red[w][j][lane];
+          *reinterpret_cast<f32x4_t*>(&dst[16 * j + 4 * g]) = v;
+        }
+    }
   }
+}
+
+template <int kRT, int kTT>
+void launch_lowrank_t_one(const LowRankTArgs& a, hipStream_t s) {
+  const dim3 grid((a.M + 16 * kTT - 1) / (16 * kTT), a.splits);
+  hipLaunchKernelGGL((lowrank_t_kernel<kRT, kTT>), grid, dim3(kTThreads), 0, s, a);
 }
 
 // Sum over `splits` partial arrays `stride` floats apart of the 8 floats at
@@ -553,8 +558,24 @@ __global__ __launch_bounds__(256) void sum_splits_kernel(const float* part, uint
 }  // namespace
 
 hipError_t launch_lowrank_t(const LowRankTArgs& a, hipStream_t s) {
-  dim3 grid((a.M + 63) / 64, a.splits);
-  hipLaunchKernelGGL(lowrank_t_kernel, grid, dim3(kTThreads), 0, s, a);
+  const int rt = a.r_pad / 16;
+  if (rt < 1 || rt > kMaxRTiles) return hipErrorInvalidValue;
+  // 64 tokens a workgroup (each A_cat operand used for four token tiles;
+  // 32 above 128 ranks, for registers) while that still gives a workgroup
+  // per CU, else 16; the smallest instance that holds rt rank tiles
+  const bool big = (int64_t)((a.M + 63) / 64) * a.splits >= 256;
+  if (rt <= 2)
+    big ? launch_lowrank_t_one<2, 4>(a, s) : launch_lowrank_t_one<2, 1>(a, s);
+  else if (rt <= 4)
+    big ? launch_lowrank_t_one<4, 4>(a, s) : launch_lowrank_t_one<4, 1>(a, s);
+  else if (rt <= 6)
+    big ? launch_lowrank_t_one<6, 4>(a, s) : launch_lowrank_t_one<6, 1>(a, s);
+  else if (rt <= 8)
+    big ? launch_lowrank_t_one<8, 4>(a, s) : launch_lowrank_t_one<8, 1>(a, s);
+  else if (rt <= 12)
+    big ? launch_lowrank_t_one<12, 2>(a, s) : launch_lowrank_t_one<12, 1>(a, s);
+  else
+    big ? launch_lowrank_t_one<16, 2>(a, s) : launch_lowrank_t_one<16, 1>(a, s);
   const int64_t mr = (int64_t)a.M * a.r_pad;  // (r_pad % 16 == 0)
   hipLaunchKernelGGL(reduce_t_kernel, dim3((unsigned)((mr + 2047) / 2048)), dim3(256), 0, s, a.tpart, a.splits, mr,
                      a.t16);

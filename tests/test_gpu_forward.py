@@ -40,6 +40,10 @@ CASES = [
     (3600, 5120, 0, 0, (), (5,)),                 # streaming, everything pruned, no adapters
     (4096, 520, 260, 0, (8,), (1, 16)),           # streaming, one-chunk tiles
     (4000, 3000, 1500, 8, (8,), (7, 16)),         # streaming, last chunk ends inside a bitmap word
+    # many-token T = X A_cat: 208 padded ranks (16- and 32-token workgroups),
+    # 128 ranks with 64-token workgroups over a ragged K
+    (64, 1024, 512, 0, (200,), (300, 4100)),
+    (64, 1000, 500, 0, (120,), (4100,)),
 ]
 
 
