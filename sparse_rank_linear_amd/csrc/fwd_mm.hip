@@ -412,11 +412,9 @@ __global__ __launch_bounds__(kThreads) void fwd_mm_kernel(LargeFwdArgs a) {
 constexpr int kTThreads = 256;
 constexpr int kTWaves = kTThreads / 64;
 constexpr int kMaxRTiles = 16;   // r_pad <= 256
-constexpr int kTBatch = 2;       // steps whose loads are issued together
-
 // kRT: rank tiles the instance holds (at least r_pad / 16); kTT: 16-token
-// tiles per workgroup.
-template <int kRT, int kTT>
+// tiles per workgroup; kTBatch: steps whose loads are issued together.
+template <int kRT, int kTT, int kTBatch>
 __global__ __launch_bounds__(kTThreads) void lowrank_t_kernel(LowRankTArgs a) {
   __shared__ f32x4_t red[kTWaves - 1][kRT][64];
   const int tid = threadIdx.x;
@@ -483,8 +481,11 @@ __global__ __launch_bounds__(kTThreads) void lowrank_t_kernel(LowRankTArgs a) {
 
 template <int kRT, int kTT>
 void launch_lowrank_t_one(const LowRankTArgs& a, hipStream_t s) {
+  // (64-token workgroups run one wave per SIMD anyway: four steps a batch,
+  // so that a split of 512 columns is one round trip)
+  constexpr int kB = kTT == 4 ? 4 : 2;
   const dim3 grid((a.M + 16 * kTT - 1) / (16 * kTT), a.splits);
-  hipLaunchKernelGGL((lowrank_t_kernel<kRT, kTT>), grid, dim3(kTThreads), 0, s, a);
+  hipLaunchKernelGGL((lowrank_t_kernel<kRT, kTT, kB>), grid, dim3(kTThreads), 0, s, a);
 }
 
 // Sum over `splits` partial arrays `stride` floats apart of the 8 floats at
