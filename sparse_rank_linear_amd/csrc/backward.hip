@@ -138,48 +138,70 @@ __global__ __launch_bounds__(256) void transpose_bf16_tiles(const uint16_t* src,
 
 // Token contraction: part[split][p][q] = sum over rows m of the split of
 // A[m][p] B[m][q] (bf16, rows of lda / ldb elements, fp32 products).  A
-// workgroup owns 64 x 64 outputs, 4 waves of 32 x 32 (2 x 2 MFMA tiles);
-// per 32 rows it loads both 32 x 64 tiles with 16-byte loads along p / q and
-// writes them to LDS transposed (k = m contiguous), which is the MFMA
-// operand layout.  Loads read up to pa / qa columns (multiples of 8; the
-// caller guarantees they exist, zero past P / Q).
-constexpr int kTnRowPad = 40;  // LDS row: 32 rows of m + 8 (fewer bank conflicts)
+// workgroup owns 64 x 64 outputs, 4 waves of 32 x 32 (2 x 2 MFMA tiles; a
+// 16-row tile past P or Q is skipped).  Per 64 rows of m it stages both
+// 64 x 64 tiles in LDS transposed (k = m contiguous, the MFMA operand
+// layout): each thread loads two consecutive rows of 8 columns with 16-byte
+// loads and stores each column's pair of values as one 32-bit word; the
+// next 64 rows' loads are requested before the current rows are multiplied.
+// Loads read up to pa / qa columns (multiples of 8; the caller guarantees
+// they exist, zero past P / Q).
+constexpr int kTnPitch = 72;  // LDS row: 64 values of m + 8 (16-row operand reads on distinct banks)
 __global__ __launch_bounds__(256) void gemm_tn_kernel(const uint16_t* A, int64_t lda, int64_t pa, const uint16_t* B,
                                                       int64_t ldb, int64_t qa, int64_t P, int64_t Q, int64_t M,
                                                       int64_t m_split, float* part) {
-  __shared__ __attribute__((aligned(16))) uint16_t at[64 * kTnRowPad];
-  __shared__ __attribute__((aligned(16))) uint16_t bt[64 * kTnRowPad];
+  __shared__ __attribute__((aligned(16))) uint16_t at[64 * kTnPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t bt[64 * kTnPitch];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, g = lane >> 4;
   const int64_t p0 = (int64_t)blockIdx.y * 64, q0 = (int64_t)blockIdx.x * 64;
   const int64_t mb = (int64_t)blockIdx.z * m_split, me = min(M, mb + m_split);
   const int wp = (wave >> 1) * 32, wq = (wave & 1) * 32;
-  // staging role: row r = tid / 8 of the 32, 8 columns at c = 8 (tid % 8)
-  const int r = tid >> 3, c = 8 * (tid & 7);
+  // staging role: rows 2 rp, 2 rp + 1 of the 64, 8 columns from c = 8 (tid % 8)
+  const int rp = tid >> 3, c = 8 * (tid & 7);
+  const bool pa_ok = p0 + c < pa, qa_ok = q0 + c < qa;
   f32x4_t acc[2][2] = {{zero4(), zero4()}, {zero4(), zero4()}};
-  for (int64_t m0 = mb; m0 < me; m0 += 32) {
-    const int64_t m = m0 + r;
-    const u32x4_t va = (m < me && p0 + c < pa) ? load16(A + m * lda + p0 + c) : zero_u4();
-    const u32x4_t vb = (m < me && q0 + c < qa) ? load16(B + m * ldb + q0 + c) : zero_u4();
+  u32x4_t va[2], vb[2];
+  const auto load_rows = [&](int64_t m0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t m = m0 + 2 * rp + h;
+      va[h] = (m < me && pa_ok) ? load16(A + m * lda + p0 + c) : zero_u4();
+      vb[h] = (m < me && qa_ok) ? load16(B + m * ldb + q0 + c) : zero_u4();
+    }
+  };
+  // 32-bit view of the tiles: column j's values for rows 2 rp, 2 rp + 1
+  uint32_t* const at32 = reinterpret_cast<uint32_t*>(at);
+  uint32_t* const bt32 = reinterpret_cast<uint32_t*>(bt);
+  const bool live_x[2] = {p0 + wp < P, p0 + wp + 16 < P};
+  const bool live_y[2] = {q0 + wq < Q, q0 + wq + 16 < Q};
+  if (mb < me) load_rows(mb);
+  for (int64_t m0 = mb; m0 < me; m0 += 64) {
     __syncthreads();  // (the previous step's operand reads are done)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      at[(c + 2 * e) * kTnRowPad + r] = (uint16_t)va[e];
-      at[(c + 2 * e + 1) * kTnRowPad + r] = (uint16_t)(va[e] >> 16);
-      bt[(c + 2 * e) * kTnRowPad + r] = (uint16_t)vb[e];
-      bt[(c + 2 * e + 1) * kTnRowPad + r] = (uint16_t)(vb[e] >> 16);
+      // columns c + 2e (low halves) and c + 2e + 1 (high halves)
+      at32[(c + 2 * e) * (kTnPitch / 2) + rp] = __builtin_amdgcn_perm(va[1][e], va[0][e], 0x05040100u);
+      at32[(c + 2 * e + 1) * (kTnPitch / 2) + rp] = __builtin_amdgcn_perm(va[1][e], va[0][e], 0x07060302u);
+      bt32[(c + 2 * e) * (kTnPitch / 2) + rp] = __builtin_amdgcn_perm(vb[1][e], vb[0][e], 0x05040100u);
+      bt32[(c + 2 * e + 1) * (kTnPitch / 2) + rp] = __builtin_amdgcn_perm(vb[1][e], vb[0][e], 0x07060302u);
     }
     __syncthreads();
-    u32x4_t a[2], b[2];
+    if (m0 + 64 < me) load_rows(m0 + 64);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      a[t] = *reinterpret_cast<const u32x4_t*>(&at[(wp + 16 * t + i) * kTnRowPad + 8 * g]);
-      b[t] = *reinterpret_cast<const u32x4_t*>(&bt[(wq + 16 * t + i) * kTnRowPad + 8 * g]);
+    for (int kh = 0; kh < 2; ++kh) {
+      u32x4_t a[2], b[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        a[t] = *reinterpret_cast<const u32x4_t*>(&at[(wp + 16 * t + i) * kTnPitch + 32 * kh + 8 * g]);
+        b[t] = *reinterpret_cast<const u32x4_t*>(&bt[(wq + 16 * t + i) * kTnPitch + 32 * kh + 8 * g]);
+      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+          if (live_x[x] && live_y[y]) acc[x][y] = mfma_16x16x32(a[x], b[y], acc[x][y]);
     }
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-      for (int y = 0; y < 2; ++y) acc[x][y] = mfma_16x16x32(a[x], b[y], acc[x][y]);
   }
   // lane holds C[p0 + wp + 16x + 4g + e][q0 + wq + 16y + i]
   float* out = part + (size_t)blockIdx.z * P * Q;
@@ -243,7 +265,7 @@ hipError_t launch_gemm_tn(const uint16_t* A, int64_t lda, int64_t pa, const uint
     hipLaunchKernelGGL(sum_parts_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, 0, n, out);
     return hipGetLastError();
   }
-  const int64_t m_split = ((M + splits - 1) / splits + 31) / 32 * 32;
+  const int64_t m_split = ((M + splits - 1) / splits + 63) / 64 * 64;
   splits = (int)((M + m_split - 1) / m_split);
   if (splits < 1) splits = 1;
   const dim3 grid((unsigned)((Q + 63) / 64), (unsigned)((P + 63) / 64), (unsigned)splits);
