@@ -118,21 +118,45 @@ __global__ __launch_bounds__(256) void transpose_scatter_kernel(const uint64_t* 
   }
 }
 
-// bf16 [R][C] -> [C][ld_dst] transpose through LDS, 64 x 64 tiles; the
-// destination row stride is ld_dst (>= R; the columns past R are zero).
-__global__ __launch_bounds__(256) void transpose_bf16_tiles(const uint16_t* src, int64_t R, int64_t C, int64_t ld_src,
-                                                            uint16_t* dst, int64_t ld_dst) {
+// bf16 [R][C] -> [C][ld_dst] transposes through LDS, 64 x 64 tiles; the
+// destination row stride is ld_dst (>= R; the columns past R are zero).  One
+// launch does two of them (blockIdx.z picks the job; blocks past a job's
+// tiles leave).  A tile whose 64 columns lie inside C and whose rows start
+// on 16 bytes is read with 16-byte loads, others element by element.
+struct TransposeJob {
+  const uint16_t* src;
+  int64_t R, C, ld_src;
+  uint16_t* dst;
+  int64_t ld_dst;
+};
+__global__ __launch_bounds__(256) void transpose_bf16_tiles(TransposeJob j0, TransposeJob j1) {
   __shared__ uint16_t tile[64][65];
+  const TransposeJob j = blockIdx.z == 0 ? j0 : j1;
   const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  if (c0 >= j.C || r0 >= (j.R > j.ld_dst ? j.R : j.ld_dst)) return;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int y = ty; y < 64; y += 4) {
-    const int64_t r = r0 + y, c = c0 + tx;
-    tile[y][tx] = (r < R && c < C) ? src[r * ld_src + c] : (uint16_t)0;
+  const bool vec = c0 + 64 <= j.C && (j.ld_src & 7) == 0 && ((uintptr_t)j.src & 15) == 0;
+  if (vec) {
+    const int ch = threadIdx.x & 7, y0 = threadIdx.x >> 3;  // 8 chunks of a row, 32 rows a pass
+    for (int y = y0; y < 64; y += 32) {
+      const int64_t r = r0 + y;
+      const u32x4_t v = r < j.R ? load16(j.src + r * j.ld_src + c0 + 8 * ch) : zero_u4();
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        tile[y][8 * ch + 2 * e] = (uint16_t)v[e];
+        tile[y][8 * ch + 2 * e + 1] = (uint16_t)(v[e] >> 16);
+      }
+    }
+  } else {
+    for (int y = ty; y < 64; y += 4) {
+      const int64_t r = r0 + y, c = c0 + tx;
+      tile[y][tx] = (r < j.R && c < j.C) ? j.src[r * j.ld_src + c] : (uint16_t)0;
+    }
   }
   __syncthreads();
   for (int y = ty; y < 64; y += 4) {
     const int64_t c = c0 + y, r = r0 + tx;
-    if (c < C && r < ld_dst) dst[c * ld_dst + r] = tile[tx][y];
+    if (c < j.C && r < j.ld_dst) j.dst[c * j.ld_dst + r] = tile[tx][y];
   }
 }
 
@@ -249,11 +273,15 @@ hipError_t launch_transpose_scatter(const uint64_t* masks, const uint16_t* value
   return hipGetLastError();
 }
 
-hipError_t launch_transpose_bf16(const uint16_t* src, int64_t R, int64_t C, int64_t ld_src, uint16_t* dst,
-                                 int64_t ld_dst, hipStream_t s) {
-  if (R == 0 || C == 0) return hipSuccess;
-  const dim3 grid((unsigned)((C + 63) / 64), (unsigned)((std::max<int64_t>(R, ld_dst) + 63) / 64));
-  hipLaunchKernelGGL(transpose_bf16_tiles, grid, dim3(256), 0, s, src, R, C, ld_src, dst, ld_dst);
+hipError_t launch_transpose_bf16_pair(const uint16_t* src0, int64_t R0, int64_t C0, int64_t ld_src0, uint16_t* dst0,
+                                      int64_t ld_dst0, const uint16_t* src1, int64_t R1, int64_t C1, int64_t ld_src1,
+                                      uint16_t* dst1, int64_t ld_dst1, hipStream_t s) {
+  const TransposeJob j0{src0, R0, C0, ld_src0, dst0, ld_dst0}, j1{src1, R1, C1, ld_src1, dst1, ld_dst1};
+  const auto tiles_x = [](const TransposeJob& j) { return (j.C + 63) / 64; };
+  const auto tiles_y = [](const TransposeJob& j) { return (std::max<int64_t>(j.R, j.ld_dst) + 63) / 64; };
+  const int64_t gx = std::max(tiles_x(j0), tiles_x(j1)), gy = std::max(tiles_y(j0), tiles_y(j1));
+  if (gx == 0 || gy == 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_bf16_tiles, dim3((unsigned)gx, (unsigned)gy, 2), dim3(256), 0, s, j0, j1);
   return hipGetLastError();
 }
 

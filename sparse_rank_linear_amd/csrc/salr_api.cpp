@@ -583,8 +583,8 @@ int salr_linear_backward(const salr_layer_t* L, const salr_layer_t* LT, const ui
   uint16_t* bt = at<uint16_t>(ws, B.bt);   // B_cat [r][N]: the transposed layer's a_cat
   uint16_t* att = at<uint16_t>(ws, B.at_); // A_cat [K][r]: the transposed layer's b_cat
   if (r > 0) {
-    if (salr::launch_transpose_bf16(L->b_cat, N, r, r, bt, N, s) != hipSuccess) return SALR_ERR_HIP;
-    if (salr::launch_transpose_bf16(L->a_cat, r, K, K, att, r, s) != hipSuccess) return SALR_ERR_HIP;
+    if (salr::launch_transpose_bf16_pair(L->b_cat, N, r, r, bt, N, L->a_cat, r, K, K, att, r, s) != hipSuccess)
+      return SALR_ERR_HIP;
   }
   if (dX) {
     salr_layer_t lt = *LT;

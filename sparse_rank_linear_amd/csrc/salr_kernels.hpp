@@ -195,8 +195,9 @@ hipError_t launch_transpose_scatter(const uint64_t* masks, const uint16_t* value
                                     const uint32_t* colpre, int64_t N, int32_t K, int32_t n_keep, int32_t n_keep_t,
                                     uint64_t* masks_t, uint16_t* values_t, hipStream_t s);
 // dst[c][r] = src[r][c] (bf16), dst rows of ld_dst >= R entries, zero past R.
-hipError_t launch_transpose_bf16(const uint16_t* src, int64_t R, int64_t C, int64_t ld_src, uint16_t* dst,
-                                 int64_t ld_dst, hipStream_t s);
+hipError_t launch_transpose_bf16_pair(const uint16_t* src0, int64_t R0, int64_t C0, int64_t ld_src0, uint16_t* dst0,
+                                      int64_t ld_dst0, const uint16_t* src1, int64_t R1, int64_t C1, int64_t ld_src1,
+                                      uint16_t* dst1, int64_t ld_dst1, hipStream_t s);
 // out[p][q] = sum over m < M of A[m][p] B[m][q] (bf16, row strides lda /
 // ldb; up to pa / qa columns readable, multiples of 8, zero past P / Q),
 // fp32, the rows cut into `splits` partials (part: splits * P * Q floats)
